@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Paged-KV decode benchmark on one MI355X.
+
+One step = the decode hot path for one batch: append each sequence's new
+K/V row through its slot (pa_reshape_and_cache), then paged split-KV decode
+over the whole context (pa_decode: split pass + log-sum-exp merge).
+
+Default workload: 12 q / 2 kv heads (Qwen2.5-1.5B attention shape), head_dim
+128, block_size 16, batch 8, every context 4096 tokens, bf16, automatic split
+count.  Inputs are synthetic N(0,1) bf16 drawn on the device from a fixed
+seed; block tables are random permutations of a shuffled pool.
+
+Method
+  * Cold HBM: steps rotate over R disjoint sets of blocks (at least
+    --rotate-gib GiB of K/V between two uses of the same block), so no call
+    finds its K/V in the 256 MB last-level cache.
+  * The K timed steps are captured once into a HIP graph and replayed
+    between two events, with torch.cuda.synchronize() on both sides, so host
+    launch overhead never starves the GPU.
+  * The dominant kernel (the split-KV pass) is timed per launch with a pair of
+    HIP events around each launch on its own stream, the queue primed by a
+    device-side sleep so the events bracket the kernel and not host gaps.
+  * value = algorithmic bytes of a step / seconds per step, in GB/s.
+    Algorithmic bytes: every K and V element of every context token once per
+    kv head, q and out once, the table entries used, the lengths, plus the
+    append's read and write of the new rows and its slot ids.
+  * roofline.achieved = algorithmic decode bytes per launch / average
+    split-kernel duration; peak = 8000 GB/s (MI355X HBM3E).
+  * cpu_baseline: the fp64 numpy oracle on host copies of the same workload,
+    one BLAS thread, repeated for about --cpu-seconds.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["paged_kv_attention_09_amd/csrc/pa_decode.hip",
+                  "paged_kv_attention_09_amd/csrc/pa_device.hpp"]
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="c2b8",
+                   choices=["c2b8", "c2b1", "c3", "c4", "c5d"])
+    p.add_argument("--splits", type=int, default=0, help="0 = automatic")
+    p.add_argument("--rotate-gib", type=float, default=2.0)
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--others", default="c2b1,c3,c4,c5d",
+                   help="comma list of extra workloads measured into 'workloads' ('' = none)")
+    p.add_argument("--kernel-loop", type=int, default=0,
+                   help="profiling mode: launch only the split kernel this many times and exit")
+    p.add_argument("--copy-calibration", type=int, default=0,
+                   help="profiling mode: run a plain device copy of this many MiB, 20 times")
+    return p.parse_args(argv)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+
+
+class DecodeWorkload:
+    """Device-resident inputs of one decode workload with R block rotations."""
+
+    def __init__(self, spec, rotate_gib: float, splits: int, seed: int = 1234):
+        import numpy as np
+        import torch
+
+        import paged_kv_attention_09_amd as pa
+        import workloads as W
+
+        self.spec = spec
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        self.lens_np = W.draw_context_lens(spec)
+        bs, Hkv, D, B, Hq = spec.block_size, spec.num_kv_heads, spec.head_dim, spec.num_seqs, \
+            spec.num_q_heads
+        nblk = [(int(L) + bs - 1) // bs for L in self.lens_np]
+        per_rot = sum(nblk)
+        kv_bytes = int(self.lens_np.sum()) * Hkv * D * 2 * 2
+        self.R = max(1, math.ceil(rotate_gib * 2**30 / kv_bytes))
+        NB = max(spec.num_blocks, self.R * per_rot + 1)
+        self.NB = NB
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        shape = (NB, bs, Hkv, D)
+        self.k_cache = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        self.v_cache = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        step = max(1, (256 << 20) // (bs * Hkv * D * 2))
+        for i in range(0, NB, step):
+            j = min(NB, i + step)
+            self.k_cache[i:j].normal_(generator=g)
+            self.v_cache[i:j].normal_(generator=g)
+        perm = torch.randperm(NB, generator=g, device=dev).cpu().numpy()
+        W_ = spec.max_blocks_per_seq
+        tables, slots = [], []
+        for r in range(self.R):
+            ids = perm[r * per_rot:(r + 1) * per_rot]
+            t = np.full((B, W_), int(perm[-1]), np.int32)
+            off = 0
+            for b, n in enumerate(nblk):
+                t[b, :n] = ids[off:off + n]
+                off += n
+            L = self.lens_np.astype(np.int64)
+            last = t[np.arange(B), (L - 1) // bs].astype(np.int64) * bs + (L - 1) % bs
+            tables.append(torch.from_numpy(t).to(dev))
+            slots.append(torch.from_numpy(last).to(dev))
+        self.tables, self.slots = tables, slots
+        self.lens = torch.from_numpy(self.lens_np).to(dev)
+        self.q = torch.randn((B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+        self.new_k = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+        self.new_v = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+        self.out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        self.scale = float(spec.scale_f32)
+        self.S = splits if splits > 0 else pa.auto_splits(B, Hkv, W_, bs, dev)
+        ws = pa.decode_workspace_size(B, Hq, D, self.S)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.pa = pa
+        self.decode_bytes = W.algorithmic_decode_bytes(self.lens_np, Hq, Hkv, D, bs)
+        self.append_bytes = B * Hkv * D * 2 * 2 * 2 + B * 8
+        self.decode_flop = 4 * D * Hq * int(self.lens_np.sum())
+
+    def step(self, r: int):
+        pa = self.pa
+        pa.reshape_and_cache(self.new_k, self.new_v, self.slots[r], self.k_cache, self.v_cache)
+        pa.decode(self.q, self.k_cache, self.v_cache, self.tables[r], self.lens, self.scale,
+                  self.S, self.out, workspace=self.ws)
+
+    def kernel(self, r: int):
+        """The dominant kernel alone: the split pass (or the whole decode when
+        there is a single piece, which is then one kernel)."""
+        pa = self.pa
+        if self.S > 1:
+            pa.decode_partials(self.q, self.k_cache, self.v_cache, self.tables[r], self.lens,
+                               self.scale, self.S, self.ws)
+        else:
+            pa.decode(self.q, self.k_cache, self.v_cache, self.tables[r], self.lens, self.scale,
+                      1, self.out, workspace=self.ws)
+
+
+def sleep_cycles_for(ms: float) -> int:
+    """Calibrate torch.cuda._sleep (device spin) to roughly `ms` milliseconds."""
+    import torch
+    n = 1_000_000
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    torch.cuda._sleep(n)
+    e.record()
+    torch.cuda.synchronize()
+    per = max(s.elapsed_time(e), 1e-3) / n
+    return int(ms / per)
+
+
+def time_kernel_events(fn, n: int, rotations: int):
+    """Per-launch HIP event pairs around `fn(i)`, queue primed by a device sleep."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    cyc = sleep_cycles_for(max(20.0, 0.1 * n))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda._sleep(cyc)
+    for i in range(n):
+        evs[i][0].record()
+        fn(i % rotations)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    d = sorted(s.elapsed_time(e) for s, e in evs)
+    return sum(d) / n, d[len(d) // 2]
+
+
+def time_steps_graph(wl, steps: int, warmup: int):
+    """Warm up eagerly, capture `steps` steps in one graph, replay it between events."""
+    import torch
+    for i in range(warmup):
+        wl.step(i % wl.R)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            wl.step(i % wl.R)
+    torch.cuda.synchronize()
+    g.replay()          # first replay uploads the graph
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return s.elapsed_time(e) / steps, wall
+
+
+def load_traffic(workload: str):
+    path = os.path.join(PROFILES, f"decode_split_{workload}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(spec, seconds: float):
+    """The oracle, as it stands, on host copies of the workload, one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import workloads as W
+
+    inp = W.make_decode_inputs(spec)
+    ct = inp.pool.compact_tables(inp.block_tables, inp.poison_block)
+    per_call = W.algorithmic_decode_bytes(inp.context_lens, spec.num_q_heads, spec.num_kv_heads,
+                                          spec.head_dim, spec.block_size)
+    n, t = 0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            oracle.decode(inp.q, inp.pool.k, inp.pool.v, ct, inp.context_lens, inp.scale)
+            n += 1
+            t = time.perf_counter() - t0
+            if t >= seconds:
+                break
+    return {"value": round(per_call * n / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle decode of the full {spec.name} call "
+                      f"({spec.num_seqs} seqs, {int(np.sum(inp.context_lens))} tokens), "
+                      f"{n} calls in {t:.1f} s, 1 BLAS thread",
+            "us_per_call": round(t / n * 1e6, 1)}
+
+
+def measure(name, args, steps, warmup, with_kernel=True):
+    import workloads as W
+    spec = W.CONFIGS[name]
+    wl = DecodeWorkload(spec, args.rotate_gib, args.splits)
+    ms_step, wall = time_steps_graph(wl, steps, warmup)
+    bytes_step = wl.decode_bytes + wl.append_bytes
+    rec = {"workload": name, "ms_per_step": ms_step, "wall_s": wall,
+           "gbps": bytes_step / (ms_step * 1e-3) / 1e9,
+           "us_per_call": ms_step * 1e3, "splits": wl.S, "rotations": wl.R,
+           "decode_bytes": wl.decode_bytes, "append_bytes": wl.append_bytes,
+           "context_tokens": int(wl.lens_np.sum())}
+    if with_kernel:
+        avg, med = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
+        rec["kernel_avg_us"] = avg * 1e3
+        rec["kernel_median_us"] = med * 1e3
+        rec["kernel_gbps"] = wl.decode_bytes / (avg * 1e-3) / 1e9
+    return wl, rec
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not a measured configuration.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(20):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n, "launches": 20}))
+        return
+    if args.kernel_loop:
+        wl = DecodeWorkload(W.CONFIGS[args.workload], args.rotate_gib, args.splits)
+        for i in range(args.kernel_loop):
+            wl.kernel(i % wl.R)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": args.workload, "kernel_launches": args.kernel_loop,
+                          "splits": wl.S, "decode_bytes_per_launch": wl.decode_bytes}))
+        return
+
+    print(f"[bench] {args.workload}: building inputs", file=sys.stderr, flush=True)
+    wl, main_rec = measure(args.workload, args, args.steps, args.warmup)
+    print(f"[bench] {args.workload}: {main_rec['us_per_call']:.2f} us/step, "
+          f"{main_rec['gbps']:.1f} GB/s; kernel {main_rec['kernel_avg_us']:.2f} us",
+          file=sys.stderr, flush=True)
+    others = {}
+    for name in [x for x in args.others.split(",") if x and x != args.workload]:
+        del wl
+        torch.cuda.empty_cache()
+        wl, rec = measure(name, args, min(args.steps, 100), min(args.warmup, 10))
+        others[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rec.items()
+                        if k not in ("wall_s",)}
+        print(f"[bench] {name}: {rec['us_per_call']:.2f} us/step, {rec['gbps']:.1f} GB/s; "
+              f"kernel {rec['kernel_avg_us']:.2f} us ({rec['kernel_gbps']:.0f} GB/s)",
+              file=sys.stderr, flush=True)
+
+    spec = W.CONFIGS[args.workload]
+    achieved = main_rec["kernel_gbps"]
+    traffic = load_traffic(args.workload)
+    line = {
+        "metric": "paged-decode achieved HBM GB/s (% of peak) and us/call at ctx 4096",
+        "value": round(main_rec["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_rec["ms_per_step"], 6),
+        "us_per_call": round(main_rec["us_per_call"], 3),
+        "pct_of_hbm_peak": round(100 * main_rec["gbps"] / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) bf16, seeded; random block tables; cold-HBM rotation",
+        "config": {"workload": spec.name, "num_seqs": spec.num_seqs,
+                   "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
+                   "head_dim": spec.head_dim, "block_size": spec.block_size,
+                   "context_tokens": main_rec["context_tokens"], "num_splits": main_rec["splits"],
+                   "rotations": main_rec["rotations"], "step": "append + split-KV decode + merge",
+                   "timing": "HIP graph of the timed steps between HIP events"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode_split_kernel", "kernel_avg_us": round(main_rec["kernel_avg_us"], 3),
+                     "algorithmic_bytes_per_launch": main_rec["decode_bytes"]},
+        "workloads": others,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

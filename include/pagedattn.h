@@ -1,0 +1,195 @@
+/*
+ * pagedattn.h - C ABI of libpagedattn.so: paged-KV attention for AMD MI355X
+ * (gfx950).
+ *
+ * The calls implement the attention step of an LLM decode loop over a paged
+ * KV cache, as the mini-infer pages describe it:
+ *   - a fixed pool of physical KV blocks with a per-request
+ *     virtual-to-physical block table (mini-infer docs,
+ *     prajwal7-2002.github.io/mini-infer, "Systems Architecture" figure);
+ *   - new K/V rows written straight to their physical slot, and one query
+ *     token per sequence attending through the block table ("Batched Paged
+ *     Decode", same page, "Core Capabilities at a Glance" table);
+ *   - split-KV / flash-decoding partitioning of long contexts (zingnex.cn
+ *     mini-infer thread, feature list item 7 "Flash Decoding"; MiniInfer
+ *     README, "Attention Backend" table);
+ *   - bounded prompt chunks attending causally to the cached prefix
+ *     ("Prompt Ingestion", mini-infer docs, "Core Capabilities at a Glance").
+ *
+ * Conventions for every call
+ *   - Tensors are caller-owned device memory, row-major and contiguous, in
+ *     the layouts given per argument.  "bf16" means IEEE bfloat16 bit
+ *     patterns (uint16 storage).
+ *   - KV pool layout: k_cache, v_cache are [num_blocks, block_size,
+ *     num_kv_heads, head_dim] bf16.  Slot s (s = block * block_size + offset)
+ *     is row s of the pool viewed as [num_blocks * block_size, kv_heads *
+ *     head_dim].
+ *   - Grouped-query attention: q head h reads kv head h / (num_q_heads /
+ *     num_kv_heads) (consecutive groups).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All device work is enqueued on it; no call synchronises, allocates or
+ *     frees memory, or reads device memory on the host.
+ *   - Supported shapes: head_dim 64 or 128; block_size 16 or 256;
+ *     num_q_heads a multiple of num_kv_heads with a group of 1..8.
+ *   - Errors are reported only through the returned status; on any status
+ *     other than PA_OK from argument checking, nothing was enqueued.
+ *     PA_ERR_HIP means a launch failed (hipGetLastError).  Faults inside a
+ *     kernel surface asynchronously at the caller's next synchronisation.
+ *   - Device-resident preconditions are NOT checked (checking would need a
+ *     host sync): block ids in [0, num_blocks); context_lens[b] <=
+ *     max_blocks_per_seq * block_size; valid slots unique within one call.
+ *     Violating them is undefined behaviour.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  PA_ERR_SHAPE = -2,       /* sizes inconsistent or out of range              */
+  PA_ERR_UNSUPPORTED = -3, /* head_dim / block_size / group not supported     */
+  PA_ERR_SPLITS = -4,      /* num_splits outside [0, PA_MAX_SPLITS]           */
+  PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required      */
+  PA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed      */
+};
+
+#define PA_MAX_SPLITS 256
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *pa_status_string(int status);
+
+/*
+ * Slot-mapped KV append.  For each token i < num_tokens with
+ * s = slot_mapping[i] >= 0, copies k[i] (num_kv_heads * head_dim bf16) to
+ * row s of k_cache and v[i] to row s of v_cache, bit for bit.  Negative slots
+ * are padding and write nothing.  Source: "direct physical tensor gather with
+ * zero-overhead slot mapping", mini-infer docs, "Core Capabilities at a
+ * Glance" table, row "Batched Paged Decode (v0.2.1)".
+ *   k, v          bf16 [num_tokens, num_kv_heads, head_dim]   (read)
+ *   slot_mapping  int64 [num_tokens]                            (read)
+ *   k_cache, v_cache  bf16 pools (written in place)
+ * num_tokens may be 0 (nothing is enqueued).  Slots must be < num_blocks *
+ * block_size (not checked; device-resident).
+ */
+int pa_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mapping,
+                         void *k_cache, void *v_cache, int64_t num_tokens, int64_t num_blocks,
+                         int block_size, int num_kv_heads, int head_dim, void *stream);
+
+/*
+ * Paged decode: one query token per sequence attends to the first
+ * context_lens[b] tokens of its sequence, fetched through block_tables:
+ *   out[b, h] = softmax_t(scale * q[b, h] . K_b[t, g]) V_b[t, g],  g = kv head of h,
+ * with K_b[t] = k_cache[block_tables[b, t / block_size], t % block_size].
+ * context_lens counts every cached token, including one appended this step.
+ * A sequence with context length 0 gets a zero output.
+ *
+ * Split-KV: each sequence's token range is cut into contiguous pieces of
+ * split_len tokens, split_len = round_up(ceil(max_blocks_per_seq *
+ * block_size / S), 64), S = num_splits (0 = choose automatically, see
+ * pa_decode_auto_splits).  Each piece is reduced independently to a partial
+ * (normalised output, log-sum-exp) and a second kernel merges the pieces
+ * with weights exp(lse_s - max lse).  With one piece per sequence the merge
+ * is skipped and the first kernel writes `out` directly.
+ *   q             bf16 [num_seqs, num_q_heads, head_dim]
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens  int32 [num_seqs]
+ *   out           bf16 [num_seqs, num_q_heads, head_dim] (written, RNE from fp32)
+ *   workspace     device scratch of at least
+ *                 pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, S)
+ *                 bytes for the S actually used (may be NULL when that is 0).
+ * Arithmetic: fp32 scores and accumulators from bf16 inputs; softmax weights
+ * are rounded to bf16 before the weighted sum of V.
+ */
+int pa_decode(const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, const int32_t *context_lens, float scale,
+              int num_splits, void *out, int num_seqs, int num_q_heads, int num_kv_heads,
+              int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The two passes of pa_decode as separate calls, for callers that merge
+ * pieces themselves (for example pieces of one sequence computed on
+ * different devices) or time the passes apart.  Arguments mean what they mean
+ * for pa_decode; num_splits = 0 chooses automatically, and the resolved
+ * number of pieces must be at least 2 (otherwise PA_ERR_SPLITS: use
+ * pa_decode, which then runs a single kernel).
+ *
+ * pa_decode_partials writes, for every sequence b, q head h and non-empty
+ * piece s (s < ceil(context_lens[b] / split_len)), into the workspace:
+ *   o_part[b, h, s, :]  fp32 [num_seqs, num_q_heads, S, head_dim] at byte 0,
+ *                       the piece's softmax-normalised output;
+ *   lse[b, h, s]        fp32 [num_seqs, num_q_heads, S] at byte
+ *                       round_up(num_seqs * num_q_heads * S * head_dim * 4, 256),
+ *                       log2 of the piece's sum of exp2(scale * log2(e) * q.k),
+ *                       i.e. the base-2 log-sum-exp of the scaled scores.
+ * Empty pieces are not written.  pa_decode_merge reads those partials for the
+ * non-empty pieces and writes out[b, h] = sum_s 2^(lse_s - M) o_s /
+ * sum_s 2^(lse_s - M), M = max_s lse_s, as bf16 (zeros when context_lens[b]
+ * is 0).  Both need the same num_splits, block_size and max_blocks_per_seq so
+ * that they resolve the same split_len.
+ */
+int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens, float scale,
+                       int num_splits, int num_seqs, int num_q_heads, int num_kv_heads,
+                       int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+int pa_decode_merge(const void *workspace, size_t workspace_bytes, const int32_t *context_lens,
+                    void *out, int num_splits, int num_seqs, int num_q_heads, int num_kv_heads,
+                    int head_dim, int block_size, int max_blocks_per_seq, void *stream);
+
+/* Workspace bytes pa_decode needs for a given split count (0 when
+ * num_splits <= 1).  Returns 0 for invalid arguments. */
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int num_splits);
+
+/* Split count that pa_decode uses for num_splits = 0 on a device with
+ * num_cus compute units.  Pure host arithmetic on the shapes (context
+ * lengths are device-resident and are not read): it aims for enough
+ * (sequence, kv head, piece) work units to fill the device.  Returns a value
+ * in [1, PA_MAX_SPLITS], or a negative status for invalid arguments. */
+int pa_decode_plan_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
+                          int block_size, int num_cus);
+
+/* pa_decode_plan_splits with the compute-unit count of HIP device `device`
+ * (queried once per device and cached). */
+int pa_decode_auto_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
+                          int block_size, int device);
+
+/*
+ * Chunked prefill over the paged cache: sequence b contributes the
+ * n_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b] query rows
+ * q[cu_seqlens_q[b] .. cu_seqlens_q[b + 1]), the last n_b tokens of a
+ * sequence whose context_lens[b] tokens (cached prefix plus this chunk) are
+ * all in the pool already (append the chunk's K/V first).  Query i sits at
+ * position p = context_lens[b] - n_b + i and attends causally to keys
+ * 0 .. p.  Source: "Bounded 512-token chunks interleaving prompt ingestion
+ * with active decodes", mini-infer docs, "Core Capabilities at a Glance"
+ * table, row "Prompt Ingestion (v0.2.1)".
+ *   q            bf16 [total_q, num_q_heads, head_dim], total_q = cu_seqlens_q[num_seqs]
+ *   cu_seqlens_q int32 [num_seqs + 1], non-decreasing, from 0
+ *   out          bf16 [total_q, num_q_heads, head_dim]
+ *   max_q_len    an upper bound of every n_b (sizes the launch grid)
+ * The QK^T and PV products run on the bf16 matrix cores (MFMA) with fp32
+ * accumulation; softmax weights are rounded to bf16 for the PV product.
+ */
+int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
+               const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+               float scale, void *out, int num_seqs, int max_q_len, int num_q_heads,
+               int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+               int max_blocks_per_seq, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

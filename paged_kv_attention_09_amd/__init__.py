@@ -1,0 +1,259 @@
+"""Python binding of libpagedattn.so (paged-KV attention for MI355X / gfx950).
+
+Argument marshalling only: shapes, dtypes and devices of torch tensors are
+checked, raw device pointers and the current HIP stream are handed to the C
+ABI declared in include/pagedattn.h, and every step of the computation runs
+in the library's HIP kernels.  There is no fallback: if the library is not
+built, or no GPU is present, the calls raise.
+
+Calls (argument order as in the C ABI):
+  reshape_and_cache(k, v, slot_mapping, k_cache, v_cache, stream=None)
+  decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
+         stream=None, workspace=None)
+  prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, out,
+          max_q_len, stream=None)
+  decode_workspace_size(num_seqs, num_q_heads, head_dim, num_splits)
+  plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus)
+  auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, device=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libpagedattn.so")
+
+PA_OK = 0
+PA_MAX_SPLITS = 256
+
+# Every symbol include/pagedattn.h declares, with its ctypes signature.
+_VP, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+SIGNATURES = {
+    "pa_version": (_I, []),
+    "pa_status_string": (ctypes.c_char_p, [_I]),
+    "pa_reshape_and_cache": (_I, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I, _I, _I, _VP]),
+    "pa_decode": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _I, _VP, _I, _I, _I, _I, _I, _I64, _I, _VP,
+                       _SZ, _VP]),
+    "pa_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "pa_decode_plan_splits": (_I, [_I, _I, _I, _I, _I]),
+    "pa_decode_auto_splits": (_I, [_I, _I, _I, _I, _I]),
+    "pa_decode_partials": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _I, _I, _I, _I, _I, _I, _I64, _I, _VP,
+                                _SZ, _VP]),
+    "pa_decode_merge": (_I, [_VP, _SZ, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP]),
+    "pa_prefill": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _F, _VP, _I, _I, _I, _I, _I, _I, _I64, _I,
+                        _VP]),
+}
+
+_lib = None
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().pa_status_string(status).decode()
+        super().__init__(f"{fn} failed with status {status} ({msg})")
+        self.status = status
+
+
+def lib():
+    """Load libpagedattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_attention_09_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PA_OK:
+        raise PagedAttnError(fn, status)
+
+
+def _stream_ptr(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _pool_dims(k_cache, v_cache):
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, k_cache.device)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    return tuple(int(x) for x in k_cache.shape)     # NB, bs, Hkv, D
+
+
+def reshape_and_cache(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Write k[i], v[i] ([T, Hkv, D] bf16) to pool row slot_mapping[i] (int64 [T];
+    negative = skip)."""
+    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _need(k, "k", torch.bfloat16, 3, dev)
+    _need(v, "v", torch.bfloat16, 3, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    T = int(k.shape[0])
+    if tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D):
+        raise ValueError(f"k/v must be [{T}, {Hkv}, {D}]")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping length differs from the token count")
+    _check("pa_reshape_and_cache", lib().pa_reshape_and_cache(
+        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), T, NB, bs, Hkv, D, _stream_ptr(stream, dev)))
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
+    return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, num_splits))
+
+
+def plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus) -> int:
+    r = int(lib().pa_decode_plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
+                                        num_cus))
+    _check("pa_decode_plan_splits", min(r, 0))
+    return r
+
+
+def auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, device=None) -> int:
+    if device is None:
+        device = torch.cuda.current_device()
+    elif isinstance(device, torch.device):
+        device = device.index if device.index is not None else torch.cuda.current_device()
+    r = int(lib().pa_decode_auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
+                                        int(device)))
+    _check("pa_decode_auto_splits", min(r, 0))
+    return r
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_splits: int, out,
+           stream=None, workspace: Optional[torch.Tensor] = None):
+    """out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over the first
+    context_lens[b] tokens of sequence b, read through block_tables.
+    num_splits = 0 picks the split count automatically.  The split workspace
+    comes from torch's caching allocator unless `workspace` (uint8, on the
+    device) is given."""
+    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _need(q, "q", torch.bfloat16, 3, dev)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, Dq = (int(x) for x in q.shape)
+    if Dq != D or tuple(out.shape) != (B, Hq, D):
+        raise ValueError(f"q/out must be [{B}, {Hq}, {D}]")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables/context_lens batch differs from q")
+    W = int(block_tables.shape[1])
+    if num_splits == 0 and B > 0:
+        num_splits = auto_splits(B, Hkv, W, bs, dev)
+    need = decode_workspace_size(B, Hq, D, num_splits) if B > 0 else 0
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace.device != dev or workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace needs {need} bytes on {dev}")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check("pa_decode", lib().pa_decode(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), float(scale), int(num_splits), out.data_ptr(), B, Hq, Hkv, D,
+        bs, NB, W, ws_ptr, ws_bytes, _stream_ptr(stream, dev)))
+    return out
+
+
+def _decode_dims(q, k_cache, v_cache, block_tables, context_lens):
+    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _need(q, "q", torch.bfloat16, 3, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, Dq = (int(x) for x in q.shape)
+    if Dq != D:
+        raise ValueError(f"q head_dim {Dq} differs from the pool's {D}")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables/context_lens batch differs from q")
+    return NB, bs, Hkv, D, B, Hq, int(block_tables.shape[1]), dev
+
+
+def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                    num_splits: int, workspace: torch.Tensor, stream=None) -> int:
+    """Split pass only: per-piece normalised outputs and base-2 log-sum-exps
+    into `workspace` (layout in include/pagedattn.h).  Needs at least two
+    pieces.  Returns the resolved num_splits."""
+    NB, bs, Hkv, D, B, Hq, W, dev = _decode_dims(q, k_cache, v_cache, block_tables, context_lens)
+    if num_splits == 0:
+        num_splits = auto_splits(B, Hkv, W, bs, dev)
+    _check("pa_decode_partials", lib().pa_decode_partials(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), float(scale), int(num_splits), B, Hq, Hkv, D, bs, NB, W,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream_ptr(stream, dev)))
+    return num_splits
+
+
+def decode_merge(workspace: torch.Tensor, context_lens, out, num_splits: int, num_kv_heads: int,
+                 block_size: int, max_blocks_per_seq: int, stream=None):
+    """Merge pass only: combine the partials in `workspace` into bf16 `out`."""
+    dev = out.device
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, D = (int(x) for x in out.shape)
+    _check("pa_decode_merge", lib().pa_decode_merge(
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        context_lens.data_ptr(), out.data_ptr(), int(num_splits), B, Hq, int(num_kv_heads), D,
+        int(block_size), int(max_blocks_per_seq), _stream_ptr(stream, dev)))
+    return out
+
+
+def prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+            max_q_len: int, stream=None):
+    """Causal attention of packed chunk queries q [Tq, Hq, D] (sequence b owns
+    rows cu_seqlens_q[b]..cu_seqlens_q[b+1]) over each sequence's cached
+    context_lens[b] tokens, chunk included; query i of an n-row chunk sits at
+    position context_lens[b] - n + i."""
+    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _need(q, "q", torch.bfloat16, 3, dev)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    Tq, Hq, Dq = (int(x) for x in q.shape)
+    B = int(context_lens.shape[0])
+    if Dq != D or tuple(out.shape) != (Tq, Hq, D):
+        raise ValueError(f"q/out must be [{Tq}, {Hq}, {D}]")
+    if cu_seqlens_q.shape[0] != B + 1 or block_tables.shape[0] != B:
+        raise ValueError("cu_seqlens_q must have num_seqs + 1 entries")
+    W = int(block_tables.shape[1])
+    _check("pa_prefill", lib().pa_prefill(
+        q.data_ptr(), cu_seqlens_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), out.data_ptr(), B,
+        int(max_q_len), Hq, Hkv, D, bs, NB, W, _stream_ptr(stream, dev)))
+    return out
+
+
+__all__ = ["reshape_and_cache", "decode", "decode_partials", "decode_merge", "prefill", "decode_workspace_size", "plan_splits",
+           "auto_splits", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError", "PA_MAX_SPLITS"]

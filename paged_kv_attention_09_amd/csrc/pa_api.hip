@@ -1,0 +1,299 @@
+// C ABI of libpagedattn.so: argument checking, split planning and dispatch.
+// The operations are documented in include/pagedattn.h.  Nothing here
+// allocates, synchronises or reads device memory; all work goes on the
+// caller's stream, in the order the calls are made.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+
+#include "pa_kernels.hpp"
+#include "pagedattn.h"
+
+namespace {
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+bool supported_block_size(int bs) { return bs == 16 || bs == 256; }
+int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+int check_heads(int num_q_heads, int num_kv_heads, int head_dim) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int g = num_q_heads / num_kv_heads;
+  if (g < 1 || g > 8) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int check_pool(int64_t num_blocks, int block_size, int max_blocks_per_seq) {
+  if (!supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  // token indices are kept in 32-bit registers on the device
+  if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 30) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+// Tokens per piece for S pieces over a table of `max_tokens` tokens.
+int split_len_for(int64_t max_tokens, int num_splits) {
+  int64_t c = (max_tokens + num_splits - 1) / num_splits;
+  c = (c + 63) / 64 * 64;
+  if (c < 64) c = 64;
+  return (int)c;
+}
+
+int num_pieces(int64_t max_tokens, int split_len) {
+  return (int)((max_tokens + split_len - 1) / split_len);
+}
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_cu_once[kMaxDevices];
+int g_cu_count[kMaxDevices];
+
+int cu_count(int device) {
+  if (device < 0 || device >= kMaxDevices) return -1;
+  std::call_once(g_cu_once[device], [device] {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+      v = -1;
+    g_cu_count[device] = v;
+  });
+  return g_cu_count[device];
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return 100; }
+
+const char *pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: sizes inconsistent or out of range";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: head_dim must be 64 or 128, block_size 16 or 256, group 1..8";
+    case PA_ERR_SPLITS: return "PA_ERR_SPLITS: num_splits outside [0, PA_MAX_SPLITS]";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: a HIP call or kernel launch failed";
+    default: return "unknown pagedattn status";
+  }
+}
+
+int pa_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
+                         void *v_cache, int64_t num_tokens, int64_t num_blocks, int block_size,
+                         int num_kv_heads, int head_dim, void *stream) {
+  if (!k_cache || !v_cache) return PA_ERR_NULL;
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping) return PA_ERR_NULL;
+  pa::AppendArgs a;
+  a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
+  a.slot_mapping = slot_mapping;
+  a.k_cache = (uint16_t *)k_cache;
+  a.v_cache = (uint16_t *)v_cache;
+  a.num_tokens = num_tokens;
+  a.row_elems = num_kv_heads * head_dim;
+  return pa::launch_append(a, head_dim, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int num_splits) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  if (num_splits <= 1 || num_splits > PA_MAX_SPLITS) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads * num_splits;
+  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
+  return o_bytes + (rows * sizeof(float) + 255) / 256 * 256;
+}
+
+int pa_decode_plan_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq, int block_size,
+                          int num_cus) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_cus <= 0) return PA_ERR_SHAPE;
+  const int st = check_pool(1, block_size, max_blocks_per_seq);
+  if (st != PA_OK) return st;
+  const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  // Aim for about two resident workgroups per compute unit.
+  const int64_t target = 2 * (int64_t)num_cus;
+  int64_t s = 1;
+  if (units < target) s = (target + units - 1) / units;
+  if (s > PA_MAX_SPLITS) s = PA_MAX_SPLITS;
+  const int c = split_len_for(max_tokens, (int)s);
+  int n = num_pieces(max_tokens, c);
+  if (n < 1) n = 1;
+  if (n > PA_MAX_SPLITS) n = PA_MAX_SPLITS;
+  return n;
+}
+
+int pa_decode_auto_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq, int block_size,
+                          int device) {
+  const int cus = cu_count(device);
+  if (cus <= 0) return PA_ERR_HIP;
+  return pa_decode_plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, cus);
+}
+
+namespace {
+
+// Shared argument resolution of the decode entry points.  Fills `a` except the
+// output pointers; returns a status.
+int resolve_decode(const void *q, const void *k_cache, const void *v_cache,
+                   const int32_t *block_tables, const int32_t *context_lens, float scale,
+                   int num_splits, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                   int block_size, int64_t num_blocks, int max_blocks_per_seq, pa::DecodeArgs *a) {
+  if (num_seqs < 0) return PA_ERR_SHAPE;
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (st != PA_OK) return st;
+  st = check_pool(num_blocks, block_size, max_blocks_per_seq);
+  if (st != PA_OK) return st;
+  if (num_splits < 0 || num_splits > PA_MAX_SPLITS) return PA_ERR_SPLITS;
+  if (!(std::isfinite(scale))) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (num_splits == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+    num_splits = pa_decode_auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, dev);
+    if (num_splits < 0) return num_splits;
+  }
+  const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
+  const int split_len = split_len_for(max_tokens, num_splits);
+  a->q = (const uint16_t *)q;
+  a->k_cache = (const uint16_t *)k_cache;
+  a->v_cache = (const uint16_t *)v_cache;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->out = nullptr;
+  a->o_part = nullptr;
+  a->lse_part = nullptr;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  a->num_q_heads = num_q_heads;
+  a->num_kv_heads = num_kv_heads;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->bs_shift = log2_exact(block_size);
+  a->split_len = split_len;
+  a->num_splits = num_pieces(max_tokens, split_len);
+  return PA_OK;
+}
+
+int attach_workspace(pa::DecodeArgs *a, int num_seqs, int head_dim, const void *workspace,
+                     size_t workspace_bytes) {
+  const size_t need = pa_decode_workspace_size(num_seqs, a->num_q_heads, head_dim, a->num_splits);
+  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  const size_t rows = (size_t)num_seqs * a->num_q_heads * a->num_splits;
+  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
+  a->o_part = (float *)workspace;
+  a->lse_part = (float *)((char *)workspace + o_bytes);
+  return PA_OK;
+}
+
+}  // namespace
+
+int pa_decode(const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, const int32_t *context_lens, float scale,
+              int num_splits, void *out, int num_seqs, int num_q_heads, int num_kv_heads,
+              int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+              void *workspace, size_t workspace_bytes, void *stream) {
+  pa::DecodeArgs a;
+  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!out) return PA_ERR_NULL;
+  a.out = (uint16_t *)out;
+  if (a.num_splits > 1) {
+    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const int group = num_q_heads / num_kv_heads;
+  if (pa::launch_decode_split(a, head_dim, group, num_seqs, s) != hipSuccess) return PA_ERR_HIP;
+  if (a.num_splits > 1 && pa::launch_decode_combine(a, head_dim, num_seqs, s) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
+int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens, float scale,
+                       int num_splits, int num_seqs, int num_q_heads, int num_kv_heads,
+                       int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  pa::DecodeArgs a;
+  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (a.num_splits < 2) return PA_ERR_SPLITS;
+  st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  const int group = num_q_heads / num_kv_heads;
+  return pa::launch_decode_split(a, head_dim, group, num_seqs, (hipStream_t)stream) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int pa_decode_merge(const void *workspace, size_t workspace_bytes, const int32_t *context_lens,
+                    void *out, int num_splits, int num_seqs, int num_q_heads, int num_kv_heads,
+                    int head_dim, int block_size, int max_blocks_per_seq, void *stream) {
+  pa::DecodeArgs a;
+  // q and the pools are not used by the merge; pass placeholders through the
+  // shared resolution so both passes agree on split_len and the piece count.
+  const void *ph = (const void *)1;
+  int st = resolve_decode(ph, ph, ph, (const int32_t *)ph, context_lens, 1.f, num_splits,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, 1,
+                          max_blocks_per_seq, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!out) return PA_ERR_NULL;
+  if (a.num_splits < 2) return PA_ERR_SPLITS;
+  st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  a.q = nullptr;
+  a.k_cache = a.v_cache = nullptr;
+  a.block_tables = nullptr;
+  a.out = (uint16_t *)out;
+  return pa::launch_decode_combine(a, head_dim, num_seqs, (hipStream_t)stream) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
+               const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+               float scale, void *out, int num_seqs, int max_q_len, int num_q_heads,
+               int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+               int max_blocks_per_seq, void *stream) {
+  if (num_seqs < 0 || max_q_len < 0) return PA_ERR_SHAPE;
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (st != PA_OK) return st;
+  st = check_pool(num_blocks, block_size, max_blocks_per_seq);
+  if (st != PA_OK) return st;
+  if (!(std::isfinite(scale))) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || max_q_len == 0) return PA_OK;
+  if (!q || !cu_seqlens_q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return PA_ERR_NULL;
+  pa::PrefillArgs a;
+  a.q = (const uint16_t *)q;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.k_cache = (const uint16_t *)k_cache;
+  a.v_cache = (const uint16_t *)v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = (uint16_t *)out;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.bs_shift = log2_exact(block_size);
+  a.max_q_len = max_q_len;
+  const hipError_t e = pa::launch_prefill(a, head_dim, num_q_heads / num_kv_heads,
+                                          (hipStream_t)stream);
+  if (e == hipErrorInvalidValue) return PA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

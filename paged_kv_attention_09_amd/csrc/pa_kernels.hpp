@@ -1,0 +1,54 @@
+// Kernel argument blocks and host-side launchers shared by the C ABI
+// (pa_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct AppendArgs {
+  const uint16_t *k, *v;
+  const int64_t *slot_mapping;
+  uint16_t *k_cache, *v_cache;
+  int64_t num_tokens;
+  int row_elems;  // num_kv_heads * head_dim
+};
+
+struct DecodeArgs {
+  const uint16_t *q;          // [B, Hq, D]
+  const uint16_t *k_cache;    // [NB, bs, Hkv, D]
+  const uint16_t *v_cache;
+  const int32_t *block_tables;  // [B, W]
+  const int32_t *context_lens;  // [B]
+  uint16_t *out;              // [B, Hq, D]        (num_splits == 1)
+  float *o_part;              // [B, Hq, S, D]     (num_splits > 1)
+  float *lse_part;            // [B, Hq, S], base-2 log-sum-exp of scaled scores
+  float scale_log2;           // scale * log2(e)
+  int num_q_heads, num_kv_heads, max_blocks_per_seq;
+  int bs_shift;               // log2(block_size)
+  int split_len;              // tokens per split, multiple of 64
+  int num_splits;
+};
+
+struct PrefillArgs {
+  const uint16_t *q;          // [Tq, Hq, D]
+  const int32_t *cu_seqlens_q;  // [B + 1]
+  const uint16_t *k_cache, *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  uint16_t *out;              // [Tq, Hq, D]
+  float scale_log2;
+  int num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, bs_shift;
+  int max_q_len;
+};
+
+hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t stream);
+// Returns hipErrorInvalidValue for an unsupported (head_dim, group).
+hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, int group, int num_seqs,
+                               hipStream_t stream);
+hipError_t launch_decode_combine(const DecodeArgs &a, int head_dim, int num_seqs,
+                                 hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, int head_dim, int group, hipStream_t stream);
+
+}  // namespace pa

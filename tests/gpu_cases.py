@@ -1,0 +1,97 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the
+library through its binding, and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+
+DEV = "cuda:0"
+ATOL = 1e-2
+RTOL = 1e-2
+
+
+def bf16_tensor(bits: np.ndarray, device=DEV) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return oracle.bf16_bits_to_f64(to_bits(t))
+
+
+def device_pool(pool: W.CompactPool, device=DEV):
+    """Full [num_blocks, ...] pools on the device: NaN everywhere except the
+    referenced blocks."""
+    shape = (pool.num_blocks,) + pool.k.shape[1:]
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16)
+    k = torch.full(shape, nan, dtype=torch.bfloat16, device=device)
+    v = torch.full(shape, nan, dtype=torch.bfloat16, device=device)
+    ids = torch.from_numpy(pool.ids).to(device)
+    k.index_copy_(0, ids, bf16_tensor(pool.k, device))
+    v.index_copy_(0, ids, bf16_tensor(pool.v, device))
+    return k, v
+
+
+class DecodeCase:
+    """Device tensors for one decode call plus the oracle's answer."""
+
+    def __init__(self, inp: W.DecodeInputs, device=DEV, with_oracle=True):
+        self.inp = inp
+        s = inp.spec
+        self.k_cache, self.v_cache = device_pool(inp.pool, device)
+        self.q = bf16_tensor(inp.q, device)
+        self.tables = torch.from_numpy(inp.block_tables).to(device)
+        self.lens = torch.from_numpy(inp.context_lens).to(device)
+        self.out = torch.empty((s.num_seqs, s.num_q_heads, s.head_dim), dtype=torch.bfloat16,
+                               device=device)
+        self.scale = float(inp.scale)
+        if inp.new_k is not None:
+            self.new_k = bf16_tensor(inp.new_k, device)
+            self.new_v = bf16_tensor(inp.new_v, device)
+            self.slots = torch.from_numpy(inp.slot_mapping).to(device)
+        self.ref = self.oracle() if with_oracle else None
+
+    def oracle_pools(self):
+        """Compact pools (after the append, if any) and tables into them."""
+        p = self.inp.pool
+        kc, vc = p.k, p.v
+        ct = p.compact_tables(self.inp.block_tables, self.inp.poison_block)
+        if self.inp.new_k is not None:
+            lut = {int(x): i for i, x in enumerate(p.ids)}
+            bs = self.inp.spec.block_size
+            slots = np.array([lut[int(s) // bs] * bs + int(s) % bs for s in self.inp.slot_mapping],
+                             np.int64)
+            kc, vc = oracle.append(self.inp.new_k, self.inp.new_v, slots, kc, vc)
+        return kc, vc, ct
+
+    def oracle(self):
+        kc, vc, ct = self.oracle_pools()
+        return oracle.decode(self.inp.q, kc, vc, ct, self.inp.context_lens, self.inp.scale)
+
+    def run(self, num_splits=0, append=True, stream=None):
+        import paged_kv_attention_09_amd as pa
+        if append and self.inp.new_k is not None:
+            pa.reshape_and_cache(self.new_k, self.new_v, self.slots, self.k_cache, self.v_cache,
+                                 stream=stream)
+        pa.decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, self.scale,
+                  num_splits, self.out, stream=stream)
+        return self.out
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, atol=ATOL, rtol=RTOL, what=""):
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance; worst at {i}: "
+                             f"got {got[i]!r} ref {ref[i]!r}; max abs err {err.max():.3e}")
+    return float(err.max()), float(np.sqrt((err ** 2).mean()))

@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status codes
+before touching the device.  Only argument-checking paths are called here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_attention_09_amd as pa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "pagedattn.h")
+OK, NULL, SHAPE, UNSUP, SPLITS, WS, HIP = 0, -1, -2, -3, -4, -5, -6
+P = ctypes.c_void_p(16)     # a non-NULL pointer that is never dereferenced
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) == 10, names
+    L = pa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(pa.SIGNATURES) == names
+
+
+def test_status_strings():
+    L = pa.lib()
+    for code in (OK, NULL, SHAPE, UNSUP, SPLITS, WS, HIP):
+        assert L.pa_status_string(code).decode().startswith("PA_")
+    assert L.pa_version() >= 100
+
+
+def _decode(**kw):
+    a = dict(q=P, k=P, v=P, tables=P, lens=P, scale=0.1, S=1, out=P, B=2, Hq=12, Hkv=2, D=128,
+             bs=16, NB=100, W=8, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return pa.lib().pa_decode(a["q"], a["k"], a["v"], a["tables"], a["lens"], a["scale"], a["S"],
+                              a["out"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["W"],
+                              a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), UNSUP), (dict(D=256), UNSUP), (dict(bs=32), UNSUP), (dict(bs=8), UNSUP),
+    (dict(Hq=12, Hkv=5), SHAPE), (dict(Hq=18, Hkv=2), UNSUP), (dict(Hkv=0), SHAPE),
+    (dict(S=-1), SPLITS), (dict(S=257), SPLITS), (dict(NB=0), SHAPE), (dict(W=0), SHAPE),
+    (dict(B=-1), SHAPE), (dict(q=None), NULL), (dict(tables=None), NULL), (dict(out=None), NULL),
+    (dict(S=4), WS), (dict(S=4, ws=P, wsb=100), WS), (dict(scale=float("nan")), SHAPE),
+    (dict(B=0), OK), (dict(B=0, q=None), OK),
+])
+def test_decode_argument_checks(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_partials_and_merge_argument_checks():
+    L = pa.lib()
+    part = [P, P, P, P, P, 0.1, 1, 2, 12, 2, 128, 16, 100, 8, P, 1 << 20, None]
+    assert L.pa_decode_partials(*part) == SPLITS          # one piece: use pa_decode
+    part[6] = 4
+    bad = list(part); bad[15] = 10
+    assert L.pa_decode_partials(*bad) == WS
+    bad = list(part); bad[10] = 80
+    assert L.pa_decode_partials(*bad) == UNSUP
+    merge = [P, 1 << 20, P, P, 1, 2, 12, 2, 128, 16, 8, None]
+    assert L.pa_decode_merge(*merge) == SPLITS
+    merge[4] = 4
+    bad = list(merge); bad[1] = 16
+    assert L.pa_decode_merge(*bad) == WS
+    bad = list(merge); bad[3] = None
+    assert L.pa_decode_merge(*bad) == NULL
+
+
+def test_append_argument_checks():
+    f = pa.lib().pa_reshape_and_cache
+    assert f(P, P, P, None, P, 1, 10, 16, 1, 64, None) == NULL
+    assert f(P, P, P, P, P, -1, 10, 16, 1, 64, None) == SHAPE
+    assert f(P, P, P, P, P, 1, 10, 32, 1, 64, None) == UNSUP
+    assert f(P, P, P, P, P, 1, 10, 16, 1, 80, None) == UNSUP
+    assert f(None, None, None, P, P, 0, 10, 16, 1, 64, None) == OK
+    assert f(None, P, P, P, P, 3, 10, 16, 1, 64, None) == NULL
+
+
+def test_prefill_argument_checks():
+    f = pa.lib().pa_prefill
+    args = [P, P, P, P, P, P, 0.1, P, 1, 512, 28, 4, 128, 256, 100, 16, None]
+    bad = list(args); bad[12] = 100
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[10] = 30
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[1] = None
+    assert f(*bad) == NULL
+    ok0 = list(args); ok0[9] = 0
+    assert f(*ok0) == OK
+
+
+def test_workspace_size():
+    ws = pa.lib().pa_decode_workspace_size
+    assert ws(8, 12, 128, 1) == 0 and ws(8, 12, 128, 0) == 0
+    rows = 8 * 12 * 32
+    want = (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    assert ws(8, 12, 128, 32) == want
+    assert ws(0, 12, 128, 4) == 0 and ws(8, 12, 128, 300) == 0
+
+
+def test_plan_splits():
+    plan = pa.lib().pa_decode_plan_splits
+    # many (sequence, kv head) units already fill the device: one piece each
+    assert plan(256, 8, 5, 256, 256) == 1
+    # few units: enough pieces for ~2 workgroups per compute unit, 64-token multiples
+    s = plan(8, 2, 256, 16, 256)
+    assert 16 <= s <= 64
+    assert plan(1, 2, 256, 16, 256) == 64        # pieces cannot go below 64 tokens
+    for args in [(4, 1, 16, 16, 256), (8, 4, 16, 256, 256), (64, 4, 16, 256, 256)]:
+        s = plan(*args)
+        assert 1 <= s <= 256
+        max_tokens = args[2] * args[3]
+        c = -(-max_tokens // s)
+        assert s == -(-max_tokens // ((c + 63) // 64 * 64))
+    assert plan(0, 2, 256, 16, 256) == SHAPE and plan(1, 2, 256, 16, 0) == SHAPE
+    assert plan(1, 2, 256, 32, 256) == UNSUP

@@ -1,0 +1,241 @@
+"""GPU parity of the split-KV paged decode against the fp64 oracle, plus the
+invariants that the loose absolute tolerance alone would not catch.
+
+Tolerance (stated for attention outputs): |gpu - oracle| <= 1e-2 + 1e-2 |oracle|
+elementwise, gpu output widened from bf16.  Tighter gates are used where the
+exact answer is known (ctx = 1, constant V, uniform-weight histogram, GQA
+constants) or where two GPU runs must agree bit for bit (physical block
+relabelling, block size 16 vs 256, repeated runs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_cases import DEV, DecodeCase, assert_close, bf16_tensor, to_bits, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case, S):
+    out = case.run(num_splits=S)
+    torch.cuda.synchronize()
+    return to_f64(out)
+
+
+@pytest.mark.parametrize("S", [1, 4, 0])
+def test_tiny_decode(S):
+    """4 sequences of lengths {1, 17, 100, 255}, group 2, head_dim 64, bs 16."""
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c1"]))
+    assert_close(_run(case, S), case.ref, what=f"c1 S={S}")
+
+
+@pytest.mark.parametrize("name", ["c2b1", "c2b8"])
+def test_ctx4096_decode(name):
+    """12 q / 2 kv heads, head_dim 128, bs 16, every context 4096, auto splits
+    (the launch configuration the benchmark times)."""
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS[name]))
+    maxe, rms = assert_close(_run(case, 0), case.ref, what=name)
+    print(f"{name}: max abs err {maxe:.3e} rms {rms:.3e}")
+
+
+def test_qwen7b_append_then_decode():
+    """28 q / 4 kv (group 7), bs 256, random lengths; the 8 new tokens are
+    appended through slot_mapping first."""
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c3"]))
+    assert_close(_run(case, 0), case.ref, what="c3")
+
+
+@pytest.mark.slow
+def test_large_batch_decode():
+    """16 q / 8 kv heads, bs 256, 256 sequences of 256..1280 tokens in an
+    18 GB pool (17166 blocks); all outputs against the oracle."""
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c4"]))
+    assert_close(_run(case, 0), case.ref, what="c4")
+
+
+def test_mixed_batch_decode_part():
+    """The 64 decode sequences of the mixed batch (lengths 512..4096, group 7)."""
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c5d"]))
+    assert_close(_run(case, 0), case.ref, what="c5 decode")
+
+
+@pytest.mark.parametrize("name", ["c3", "c2b8"])
+def test_split_sweep(name):
+    """Any split count reaches the oracle, and split counts agree closely."""
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS[name]))
+    outs = {}
+    for S in (1, 2, 3, 4, 7, 8, 16, 32, 64, 256):
+        outs[S] = _run(case, S)
+        assert_close(outs[S], case.ref, what=f"{name} S={S}")
+    base = outs[1]
+    for S, o in outs.items():
+        # each differs from the exact value by bf16 output rounding plus the
+        # bf16 rounding of the softmax weights, which depends on the split
+        assert (np.abs(o - base) <= 2 ** -7 * np.abs(base) + 1e-3).all(), S
+
+
+@pytest.mark.parametrize("D,G,bs", [(64, 1, 16), (64, 3, 256), (64, 8, 16), (128, 1, 256),
+                                    (128, 2, 16), (128, 5, 16), (128, 8, 256)])
+def test_shape_matrix(D, G, bs):
+    """Every supported head_dim and group size, both block sizes, ragged lengths."""
+    spec = W.DecodeSpec(f"m{D}_{G}_{bs}", 5, 2 * G, 2, D, bs, 200, 4096 // bs,
+                        context_lens=(1, 15, 16, 17, 700 if bs == 16 else 2049), seed=D + G + bs)
+    case = DecodeCase(W.make_decode_inputs(spec))
+    for S in (1, 5, 0):
+        assert_close(_run(case, S), case.ref, what=f"D{D} G{G} bs{bs} S{S}")
+
+
+def test_empty_sequences_give_zeros():
+    spec = W.CONFIGS["c1"].with_(context_lens=(0, 17, 0, 3))
+    case = DecodeCase(W.make_decode_inputs(spec))
+    for S in (1, 4):
+        out = _run(case, S)
+        assert (out[0] == 0).all() and (out[2] == 0).all()
+        assert_close(out, case.ref, what=f"empty S={S}")
+
+
+def test_ctx1_returns_v_exactly():
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c1"]))
+    b = int(np.nonzero(case.inp.context_lens == 1)[0][0])
+    blk = case.inp.block_tables[b, 0]
+    i = list(case.inp.pool.ids).index(blk)
+    v0 = case.inp.pool.v[i, 0, 0].astype(np.uint16)
+    for S in (1, 4):
+        case.run(num_splits=S)
+        torch.cuda.synchronize()
+        bits = to_bits(case.out)
+        assert (bits[b, 0] == v0).all() and (bits[b, 1] == v0).all(), S
+
+
+def _set_values(case, which, fn):
+    """Overwrite referenced pool rows on the device with fn(shape) bf16 bits."""
+    pool = case.inp.pool
+    arr = fn(pool.k.shape)
+    if which == "k":
+        pool.k = np.where(pool.k == W.BF16_NAN, pool.k, arr).astype(np.uint16)
+    else:
+        pool.v = np.where(pool.v == W.BF16_NAN, pool.v, arr).astype(np.uint16)
+    ids = torch.from_numpy(pool.ids).to(DEV)
+    dst = case.k_cache if which == "k" else case.v_cache
+    dst.index_copy_(0, ids, bf16_tensor(pool.k if which == "k" else pool.v))
+
+
+def test_constant_v():
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c3"]), with_oracle=False)
+    case.inp.new_v[:] = W.f32_to_bf16_bits(np.float32(0.75))
+    case.new_v = bf16_tensor(case.inp.new_v)
+    _set_values(case, "v", lambda s: np.full(s, W.f32_to_bf16_bits(np.float32(0.75)), np.uint16))
+    for S in (1, 0):
+        assert (_run(case, S) == 0.75).all(), S
+
+
+def test_gqa_head_mapping():
+    spec = W.CONFIGS["c5d"]
+    case = DecodeCase(W.make_decode_inputs(spec), with_oracle=False)
+    consts = [0.5, -1.25, 2.0, 3.5]
+
+    def fill(shape):
+        a = np.empty(shape, np.uint16)
+        for g, c in enumerate(consts):
+            a[:, :, g, :] = W.f32_to_bf16_bits(np.float32(c))
+        return a
+    _set_values(case, "v", fill)
+    for g, c in enumerate(consts):
+        case.inp.new_v[:, g, :] = W.f32_to_bf16_bits(np.float32(c))
+    case.new_v = bf16_tensor(case.inp.new_v)
+    out = _run(case, 0)
+    G = spec.group
+    for h in range(spec.num_q_heads):
+        assert (out[:, h] == consts[h // G]).all(), h
+
+
+@pytest.mark.parametrize("name,S", [("c2b8", 0), ("c2b8", 1), ("c1", 4), ("c3", 0)])
+def test_uniform_weight_histogram(name, S):
+    """K = 0 makes every weight 1/L; V[t, d] = [d == t mod D] then gives
+    out[h, d] = #{t < L : t mod D = d} / L.  A dropped, repeated or misplaced
+    token shifts some bin by far more than the 2^-8 relative gate."""
+    spec = W.CONFIGS[name]
+    inp = W.make_decode_inputs(spec)
+    inp.new_k = None  # no append: the whole context comes from the pool
+    pool = inp.pool
+    D, bs = spec.head_dim, spec.block_size
+    lut = {int(p): i for i, p in enumerate(pool.ids)}
+    for b, L in enumerate(inp.context_lens):
+        for t in range(int(L)):
+            i = lut[int(inp.block_tables[b, t // bs])]
+            pool.k[i, t % bs, :, :] = 0
+            pool.v[i, t % bs, :, :] = 0
+            pool.v[i, t % bs, :, t % D] = W.BF16_ONE
+    case = DecodeCase(inp, with_oracle=False)
+    out = _run(case, S)
+    for b, L in enumerate(inp.context_lens):
+        L = int(L)
+        want = np.array([len(range(d, L, D)) / L for d in range(D)])
+        err = np.abs(out[b] - want[None, :]).max()
+        assert err <= 2 ** -8 * want.max(), (b, err)
+
+
+def test_permutation_bit_identical():
+    """Relabelling physical blocks changes no output bit: the reduction order
+    follows logical token order only."""
+    inp = W.make_decode_inputs(W.CONFIGS["c2b8"])
+    case = DecodeCase(inp, with_oracle=False)
+    base = to_bits(case.run(num_splits=0).clone())
+    NB = inp.pool.num_blocks
+    pi = np.random.default_rng(7).permutation(NB)
+    k2 = torch.empty_like(case.k_cache)
+    v2 = torch.empty_like(case.v_cache)
+    pit = torch.from_numpy(pi).to(DEV)
+    k2[pit] = case.k_cache
+    v2[pit] = case.v_cache
+    case.k_cache, case.v_cache = k2, v2
+    case.tables = torch.from_numpy(pi[inp.block_tables].astype(np.int32)).to(DEV)
+    out = to_bits(case.run(num_splits=0))
+    assert np.array_equal(base, out)
+
+
+def test_block_size_16_vs_256_bit_identical():
+    """The same logical cache paged with 16-token and 256-token blocks."""
+    spec16 = W.DecodeSpec("bs16", 6, 28, 4, 128, 16, 2000, 256, len_range=(100, 4096), seed=91)
+    inp = W.make_decode_inputs(spec16)
+    case16 = DecodeCase(inp, with_oracle=False)
+    o16 = to_bits(case16.run(num_splits=0).clone())
+    # repack: logical rows of each sequence into fresh 256-token blocks
+    lut = {int(p): i for i, p in enumerate(inp.pool.ids)}
+    nbl = [(int(L) + 255) // 256 for L in inp.context_lens]
+    NB = sum(nbl) + 3
+    perm = np.random.default_rng(5).permutation(NB)
+    k = np.full((NB, 256, 4, 128), W.BF16_NAN, np.uint16)
+    v = k.copy()
+    tables = np.full((6, 16), perm[-1], np.int32)
+    off = 0
+    for b, L in enumerate(inp.context_lens):
+        for j in range(nbl[b]):
+            tables[b, j] = perm[off]
+            off += 1
+        for t in range(int(L)):
+            i = lut[int(inp.block_tables[b, t // 16])]
+            k[tables[b, t // 256], t % 256] = inp.pool.k[i, t % 16]
+            v[tables[b, t // 256], t % 256] = inp.pool.v[i, t % 16]
+    case16.k_cache, case16.v_cache = bf16_tensor(k), bf16_tensor(v)
+    case16.tables = torch.from_numpy(tables).to(DEV)
+    o256 = to_bits(case16.run(num_splits=0))
+    assert np.array_equal(o16, o256)
+
+
+def test_repeat_runs_bit_identical():
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c5d"]), with_oracle=False)
+    a = to_bits(case.run(num_splits=0).clone())
+    for _ in range(3):
+        assert np.array_equal(a, to_bits(case.run(num_splits=0)))
+
+
+def test_nonzero_stream_and_no_host_sync():
+    """Work is ordered on the caller's stream."""
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c3"]))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        case.run(num_splits=0, stream=s)
+    s.synchronize()
+    assert_close(to_f64(case.out), case.ref, what="side stream")
