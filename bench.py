@@ -2,8 +2,11 @@
 """Paged-KV decode benchmark on one MI355X.
 
 One step = the decode hot path for one batch: append each sequence's new
-K/V row through its slot (pa_reshape_and_cache), then paged split-KV decode
-over the whole context (pa_decode: split pass + log-sum-exp merge).
+K/V row at its last token's slot and run the paged split-KV decode over the
+whole context (pa_append_decode: the append fused into the split pass, then
+the log-sum-exp merge).  The same step as separate calls
+(pa_reshape_and_cache, then pa_decode) is timed too and reported as
+config.unfused_us_per_step.
 
 Default workload: 12 q / 2 kv heads (Qwen2.5-1.5B attention shape), head_dim
 128, block_size 16, batch 8, every context 4096 tokens, bf16, automatic split
@@ -17,9 +20,9 @@ Method
   * The K timed steps are captured once into a HIP graph and replayed
     between two events, with torch.cuda.synchronize() on both sides, so host
     launch overhead never starves the GPU.
-  * The dominant kernel (the split-KV pass) is timed per launch with a pair of
-    HIP events around each launch on its own stream, the queue primed by a
-    device-side sleep so the events bracket the kernel and not host gaps.
+  * The dominant kernel (the split-KV pass) is timed with HIP events around
+    back-to-back launches on the current stream, the queue primed by a
+    device-side sleep so the events bracket GPU work and not host gaps.
   * value = algorithmic bytes of a step / seconds per step, in GB/s.
     Algorithmic bytes: every K and V element of every context token once per
     kv head, q and out once, the table entries used, the lengths, plus the
@@ -66,6 +69,8 @@ def parse_args(argv=None):
                    help="comma list of extra workloads measured into 'workloads' ('' = none)")
     p.add_argument("--kernel-loop", type=int, default=0,
                    help="profiling mode: launch only the split kernel this many times and exit")
+    p.add_argument("--sweep-splits", default="",
+                   help="tuning mode: comma list of split counts; prints us/step per workload")
     p.add_argument("--copy-calibration", type=int, default=0,
                    help="profiling mode: run a plain device copy of this many MiB, 20 times")
     return p.parse_args(argv)
@@ -137,13 +142,27 @@ class DecodeWorkload:
         self.scale = float(spec.scale_f32)
         self.S = splits if splits > 0 else pa.auto_splits(B, Hkv, W_, bs, dev)
         ws = pa.decode_workspace_size(B, Hq, D, self.S)
-        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         self.pa = pa
         self.decode_bytes = W.algorithmic_decode_bytes(self.lens_np, Hq, Hkv, D, bs)
         self.append_bytes = B * Hkv * D * 2 * 2 * 2 + B * 8
         self.decode_flop = 4 * D * Hq * int(self.lens_np.sum())
 
+    def set_splits(self, S: int):
+        import torch
+        self.S = S
+        ws = self.pa.decode_workspace_size(self.spec.num_seqs, self.spec.num_q_heads,
+                                           self.spec.head_dim, S)
+        self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=self.dev)
+
     def step(self, r: int):
+        """Append of each sequence's new row fused with the decode."""
+        self.pa.append_decode(self.q, self.new_k, self.new_v, self.k_cache, self.v_cache,
+                              self.tables[r], self.lens, self.scale, self.S, self.out,
+                              workspace=self.ws)
+
+    def step_unfused(self, r: int):
+        """The same step as separate calls: slot-mapped append, then decode."""
         pa = self.pa
         pa.reshape_and_cache(self.new_k, self.new_v, self.slots[r], self.k_cache, self.v_cache)
         pa.decode(self.q, self.k_cache, self.v_cache, self.tables[r], self.lens, self.scale,
@@ -176,33 +195,35 @@ def sleep_cycles_for(ms: float) -> int:
 
 
 def time_kernel_events(fn, n: int, rotations: int):
-    """Per-launch HIP event pairs around `fn(i)`, queue primed by a device sleep."""
+    """HIP events around n back-to-back launches of `fn(i)` on the current
+    stream, the queue primed by a device-side sleep so that the launches run
+    back to back on the GPU and host enqueue time is not measured.  Returns
+    the average milliseconds per launch."""
     import torch
     fn(0)
     torch.cuda.synchronize()
     cyc = sleep_cycles_for(max(20.0, 0.1 * n))
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(cyc)
+    s.record()
     for i in range(n):
-        evs[i][0].record()
         fn(i % rotations)
-        evs[i][1].record()
+    e.record()
     torch.cuda.synchronize()
-    d = sorted(s.elapsed_time(e) for s, e in evs)
-    return sum(d) / n, d[len(d) // 2]
+    return s.elapsed_time(e) / n
 
 
-def time_steps_graph(wl, steps: int, warmup: int):
+def time_steps_graph(wl, steps: int, warmup: int, fused: bool = True):
     """Warm up eagerly, capture `steps` steps in one graph, replay it between events."""
     import torch
+    step = wl.step if fused else wl.step_unfused
     for i in range(warmup):
-        wl.step(i % wl.R)
+        step(i % wl.R)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(steps):
-            wl.step(i % wl.R)
+            step(i % wl.R)
     torch.cuda.synchronize()
     g.replay()          # first replay uploads the graph
     torch.cuda.synchronize()
@@ -268,10 +289,11 @@ def measure(name, args, steps, warmup, with_kernel=True):
            "us_per_call": ms_step * 1e3, "splits": wl.S, "rotations": wl.R,
            "decode_bytes": wl.decode_bytes, "append_bytes": wl.append_bytes,
            "context_tokens": int(wl.lens_np.sum())}
+    ms_unfused, _ = time_steps_graph(wl, steps, 2, fused=False)
+    rec["unfused_us_per_step"] = ms_unfused * 1e3
     if with_kernel:
-        avg, med = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
+        avg = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
         rec["kernel_avg_us"] = avg * 1e3
-        rec["kernel_median_us"] = med * 1e3
         rec["kernel_gbps"] = wl.decode_bytes / (avg * 1e-3) / 1e9
     return wl, rec
 
@@ -302,6 +324,22 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"workload": args.workload, "kernel_launches": args.kernel_loop,
                           "splits": wl.S, "decode_bytes_per_launch": wl.decode_bytes}))
+        return
+
+    if args.sweep_splits:
+        res = {}
+        for name in [args.workload] + [x for x in args.others.split(",") if x]:
+            wl = DecodeWorkload(W.CONFIGS[name], args.rotate_gib, args.splits)
+            auto = wl.S
+            res[name] = {"auto": auto}
+            for S in [int(x) for x in args.sweep_splits.split(",")]:
+                wl.set_splits(S)
+                ms, _ = time_steps_graph(wl, min(args.steps, 100), 3)
+                res[name][S] = round(ms * 1e3, 2)
+                print(f"[sweep] {name} S={S}: {ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+            del wl
+            torch.cuda.empty_cache()
+        print(json.dumps(res))
         return
 
     print(f"[bench] {args.workload}: building inputs", file=sys.stderr, flush=True)
@@ -342,8 +380,10 @@ def main(argv=None):
                    "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
                    "head_dim": spec.head_dim, "block_size": spec.block_size,
                    "context_tokens": main_rec["context_tokens"], "num_splits": main_rec["splits"],
-                   "rotations": main_rec["rotations"], "step": "append + split-KV decode + merge",
-                   "timing": "HIP graph of the timed steps between HIP events"},
+                   "rotations": main_rec["rotations"], "step": "append fused into split-KV decode, then merge",
+                   "unfused_us_per_step": round(main_rec["unfused_us_per_step"], 3),
+                   "timing": "HIP graph of the timed steps between HIP events; kernel: HIP "
+                             "events around back-to-back launches behind a primed queue"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

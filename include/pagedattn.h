@@ -107,6 +107,7 @@ int pa_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mappi
  *   workspace     device scratch of at least
  *                 pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, S)
  *                 bytes for the S actually used (may be NULL when that is 0).
+ *                 Calls that run concurrently must not share a workspace.
  * Arithmetic: fp32 scores and accumulators from bf16 inputs; softmax weights
  * are rounded to bf16 before the weighted sum of V.
  */
@@ -115,6 +116,24 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
               int num_splits, void *out, int num_seqs, int num_q_heads, int num_kv_heads,
               int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step with the append fused in: for every sequence b with
+ * context_lens[b] > 0, first writes new_k[b], new_v[b] (bf16 [num_seqs,
+ * num_kv_heads, head_dim]) to the cache row of token context_lens[b] - 1 (the
+ * slot block_tables[b, (L - 1) / block_size] * block_size + (L - 1) %
+ * block_size), then computes exactly what pa_decode computes.  Equivalent to
+ * pa_reshape_and_cache with those slots followed by pa_decode, in one kernel
+ * launch fewer: the workgroup that reads a sequence's last token writes it
+ * first.  k_cache and v_cache are written; the other arguments are as for
+ * pa_decode.
+ */
+int pa_append_decode(const void *q, const void *new_k, const void *new_v, void *k_cache,
+                     void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                     float scale, int num_splits, void *out, int num_seqs, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                     int max_blocks_per_seq, void *workspace, size_t workspace_bytes,
+                     void *stream);
 
 /*
  * The two passes of pa_decode as separate calls, for callers that merge

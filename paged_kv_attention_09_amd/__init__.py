@@ -10,6 +10,9 @@ Calls (argument order as in the C ABI):
   reshape_and_cache(k, v, slot_mapping, k_cache, v_cache, stream=None)
   decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
          stream=None, workspace=None)
+  append_decode(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, scale,
+                num_splits, out, stream=None, workspace=None)
+  decode_partials(...), decode_merge(...): the two passes of decode
   prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, out,
           max_q_len, stream=None)
   decode_workspace_size(num_seqs, num_q_heads, head_dim, num_splits)
@@ -38,6 +41,8 @@ SIGNATURES = {
     "pa_reshape_and_cache": (_I, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I, _I, _I, _VP]),
     "pa_decode": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _I, _VP, _I, _I, _I, _I, _I, _I64, _I, _VP,
                        _SZ, _VP]),
+    "pa_append_decode": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F, _I, _VP, _I, _I, _I, _I, _I,
+                              _I64, _I, _VP, _SZ, _VP]),
     "pa_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "pa_decode_plan_splits": (_I, [_I, _I, _I, _I, _I]),
     "pa_decode_auto_splits": (_I, [_I, _I, _I, _I, _I]),
@@ -153,8 +158,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_sp
     """out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over the first
     context_lens[b] tokens of sequence b, read through block_tables.
     num_splits = 0 picks the split count automatically.  The split workspace
-    comes from torch's caching allocator unless `workspace` (uint8, on the
-    device) is given."""
+    comes zero-filled from torch's caching allocator unless `workspace` (uint8,
+    on the device, zero-filled before its first use) is given."""
     NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
     dev = k_cache.device
     _need(q, "q", torch.bfloat16, 3, dev)
@@ -169,19 +174,46 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_sp
     W = int(block_tables.shape[1])
     if num_splits == 0 and B > 0:
         num_splits = auto_splits(B, Hkv, W, bs, dev)
-    need = decode_workspace_size(B, Hq, D, num_splits) if B > 0 else 0
-    ws_ptr, ws_bytes = None, 0
-    if need:
-        if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-        if workspace.device != dev or workspace.numel() * workspace.element_size() < need:
-            raise ValueError(f"workspace needs {need} bytes on {dev}")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace)
     _check("pa_decode", lib().pa_decode(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), float(scale), int(num_splits), out.data_ptr(), B, Hq, Hkv, D,
         bs, NB, W, ws_ptr, ws_bytes, _stream_ptr(stream, dev)))
     return out
+
+
+def append_decode(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, scale: float,
+                  num_splits: int, out, stream=None, workspace: Optional[torch.Tensor] = None):
+    """One decode step with the append fused in: new_k[b], new_v[b] ([B, Hkv, D])
+    are written to the cache row of token context_lens[b] - 1 of sequence b,
+    then out = decode(...) over all context_lens[b] tokens."""
+    NB, bs, Hkv, D, B, Hq, W, dev = _decode_dims(q, k_cache, v_cache, block_tables, context_lens)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(new_k, "new_k", torch.bfloat16, 3, dev)
+    _need(new_v, "new_v", torch.bfloat16, 3, dev)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError(f"out must be [{B}, {Hq}, {D}]")
+    if tuple(new_k.shape) != (B, Hkv, D) or tuple(new_v.shape) != (B, Hkv, D):
+        raise ValueError(f"new_k/new_v must be [{B}, {Hkv}, {D}]")
+    if num_splits == 0 and B > 0:
+        num_splits = auto_splits(B, Hkv, W, bs, dev)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace)
+    _check("pa_append_decode", lib().pa_append_decode(
+        q.data_ptr(), new_k.data_ptr(), new_v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), int(num_splits),
+        out.data_ptr(), B, Hq, Hkv, D, bs, NB, W, ws_ptr, ws_bytes, _stream_ptr(stream, dev)))
+    return out
+
+
+def _workspace(B, Hq, D, num_splits, dev, workspace):
+    need = decode_workspace_size(B, Hq, D, num_splits) if B > 0 else 0
+    if not need:
+        return None, 0, workspace
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes on {dev}")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
 
 
 def _decode_dims(q, k_cache, v_cache, block_tables, context_lens):
@@ -255,5 +287,5 @@ def prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale
     return out
 
 
-__all__ = ["reshape_and_cache", "decode", "decode_partials", "decode_merge", "prefill", "decode_workspace_size", "plan_splits",
+__all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "decode_merge", "prefill", "decode_workspace_size", "plan_splits",
            "auto_splits", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError", "PA_MAX_SPLITS"]

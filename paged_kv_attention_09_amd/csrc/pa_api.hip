@@ -168,6 +168,8 @@ int resolve_decode(const void *q, const void *k_cache, const void *v_cache,
   a->v_cache = (const uint16_t *)v_cache;
   a->block_tables = block_tables;
   a->context_lens = context_lens;
+  a->new_k = nullptr;
+  a->new_v = nullptr;
   a->out = nullptr;
   a->o_part = nullptr;
   a->lse_part = nullptr;
@@ -192,6 +194,14 @@ int attach_workspace(pa::DecodeArgs *a, int num_seqs, int head_dim, const void *
   return PA_OK;
 }
 
+int launch_split_and_merge(const pa::DecodeArgs &a, int head_dim, int group, int num_seqs,
+                           hipStream_t s) {
+  if (pa::launch_decode_split(a, head_dim, group, num_seqs, s) != hipSuccess) return PA_ERR_HIP;
+  if (a.num_splits > 1 && pa::launch_decode_combine(a, head_dim, num_seqs, s) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
 }  // namespace
 
 int pa_decode(const void *q, const void *k_cache, const void *v_cache,
@@ -210,12 +220,31 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
     st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
     if (st != PA_OK) return st;
   }
-  hipStream_t s = (hipStream_t)stream;
-  const int group = num_q_heads / num_kv_heads;
-  if (pa::launch_decode_split(a, head_dim, group, num_seqs, s) != hipSuccess) return PA_ERR_HIP;
-  if (a.num_splits > 1 && pa::launch_decode_combine(a, head_dim, num_seqs, s) != hipSuccess)
-    return PA_ERR_HIP;
-  return PA_OK;
+  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
+                                (hipStream_t)stream);
+}
+
+int pa_append_decode(const void *q, const void *new_k, const void *new_v, void *k_cache,
+                     void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                     float scale, int num_splits, void *out, int num_seqs, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                     int max_blocks_per_seq, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+  pa::DecodeArgs a;
+  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!out || !new_k || !new_v) return PA_ERR_NULL;
+  a.out = (uint16_t *)out;
+  a.new_k = (const uint16_t *)new_k;
+  a.new_v = (const uint16_t *)new_v;
+  if (a.num_splits > 1) {
+    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+  }
+  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
+                                (hipStream_t)stream);
 }
 
 int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,

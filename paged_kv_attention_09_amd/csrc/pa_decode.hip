@@ -42,7 +42,8 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kChunk = 16;  // tokens per wave step
+constexpr int kChunk = 16;     // tokens per wave step
+constexpr float kSlack = 8.f;  // log2 headroom before the running max moves
 
 template <int D>
 __device__ __forceinline__ int row_swizzle(int r) {
@@ -76,17 +77,34 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // Grid: x = (sequence, kv head), y = piece.  Workgroups dispatch in id
+  // order and round-robin over the 8 XCDs, so every sequence's first piece
+  // (never empty) goes out first and pieces of one index spread over all
+  // XCDs instead of piling one piece index onto one XCD.
+  const int g = blockIdx.x % a.num_kv_heads, b = blockIdx.x / a.num_kv_heads;
+  const int split = blockIdx.y;
   const int Hq = a.num_q_heads;
-  const int L = as_const(a.context_lens)[b];
   const int t0 = split * a.split_len;
   const size_t head0 = (size_t)b * Hq + (size_t)g * G;  // first q head of the group
+  const int bs_shift = a.bs_shift;
+  const int bs_mask = (1 << bs_shift) - 1;
+  const int Wm1 = a.max_blocks_per_seq - 1;
+  const auto *table = as_const(a.block_tables + (size_t)b * a.max_blocks_per_seq);
+
+  // The length and the block ids of this wave's first chunks are independent
+  // scalar loads, so they are in flight together (table entries past the
+  // sequence end are read but never used).
+  const int L = as_const(a.context_lens)[b];
+  int blk_first[NSTAGE];
+#pragma unroll
+  for (int s = 0; s < NSTAGE; ++s)
+    blk_first[s] = table[min((t0 + (wave + kWaves * s) * kChunk) >> bs_shift, Wm1)];
 
   if (t0 >= L) {
-    // Nothing to read.  Writing the output directly (one piece), this
-    // workgroup owns the rows and writes zeros (empty sequence); writing
-    // partials, the merge never reads an empty piece.
-    if (a.o_part == nullptr) {
+    // Nothing to read.  Only an empty sequence (L = 0) reaches this with
+    // split 0; writing the output directly (one piece) this workgroup owns
+    // the rows and writes zeros.  The merge never reads an empty piece.
+    if (split == 0 && a.o_part == nullptr) {
       for (int i = threadIdx.x; i < G * D; i += 256) a.out[head0 * D + i] = 0;
     }
     return;
@@ -101,12 +119,27 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   const uint32_t my_off = lds_offset(my);
   const uint32_t q_off = lds_offset(qlds);
 
-  const int bs_shift = a.bs_shift;
-  const int bs_mask = (1 << bs_shift) - 1;
   const uint32_t RS = (uint32_t)a.num_kv_heads * ROWB;  // bytes between token rows
   const char *kbase = (const char *)a.k_cache + (size_t)g * ROWB;
   const char *vbase = (const char *)a.v_cache + (size_t)g * ROWB;
-  const auto *table = as_const(a.block_tables + (size_t)b * a.max_blocks_per_seq);
+
+  // Fused append: the wave that owns the sequence's last token writes the new
+  // K/V row of this kv head to that token's slot, and waits for the stores to
+  // complete before it issues any load of the chunk holding the row.  Only
+  // this wave reads that row in this launch.
+  if (a.new_k != nullptr && t1 == L && wave == (nck - 1) % kWaves) {
+    const int tl = L - 1;
+    const size_t row = ((size_t)(uint32_t)table[tl >> bs_shift] << bs_shift) + (tl & bs_mask);
+    const size_t src = ((size_t)b * a.num_kv_heads + g) * ROWB;
+    if (lane < 2 * NPOS) {
+      const int c = lane % NPOS;
+      const bool is_v = lane >= NPOS;
+      const char *from = (const char *)(is_v ? a.new_v : a.new_k) + src + c * 16;
+      char *to = (char *)(is_v ? vbase : kbase) + row * RS + c * 16;
+      *(uint4 *)to = *(const uint4 *)from;
+    }
+    wait_vmcnt<0>();
+  }
 
   // Per-lane DMA geometry: instruction j moves rows j*(1024/ROWB) + lane/NPOS.
   uint32_t dma_voff[NDMA], dma_pos[NDMA];
@@ -121,9 +154,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     dma_voff[j] = (uint32_t)r * RS + (uint32_t)c * 16;
   }
 
-  auto issue_chunk = [&](int ci, int stage) {
+  auto issue_chunk = [&](int ci, int stage, int blk) {
     const int tc = t0 + ci * kChunk;
-    const int blk = table[tc >> bs_shift];
     const size_t row0 = ((size_t)(uint32_t)blk << bs_shift) + (size_t)(tc & bs_mask);
     const char *kb = kbase + row0 * RS;
     const char *vb = vbase + row0 * RS;
@@ -162,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < NSTAGE; ++s)
-      if (s < n_my) issue_chunk(wave + kWaves * s, s);
+      if (s < n_my) issue_chunk(wave + kWaves * s, s, blk_first[s]);
 
     const int r = lane >> 2, u = lane & 3;
     const int swr = row_swizzle<D>(r);
@@ -202,25 +234,40 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
           s[h] = dot2(qreg[h][k].w, kv.w, s[h]);
         }
       }
+      // ---- online softmax, exp2 domain, lazily rescaled ----
+      // The running max m only moves when some score of the chunk exceeds it
+      // by more than kSlack (one wave ballot decides); otherwise the weights
+      // exp2(x - m) <= 2^kSlack stay well inside fp32/bf16 range and no
+      // cross-lane max or rescale is needed.  The result is the same up to
+      // rounding: numerator and denominator share the factor 2^-m.
       const bool valid = tc + r < t1;
-      float alpha[G];
+      float x[G];
+      bool grow = false;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float x = valid ? quad_sum(s[h]) * a.scale_log2 : -INFINITY;
-        const float m_new = fmaxf(m[h], max_over_quads(x));
-        alpha[h] = exp2_fast(m[h] - m_new);
-        m[h] = m_new;
-        const uint32_t pk = pack_bf16(exp2_fast(x - m_new), 0.f);
-        l_lane[h] = l_lane[h] * alpha[h] + bf16_lo(pk);
-        if (u == 0) *(uint16_t *)(plds + h * (kChunk * 2) + r * 2) = (uint16_t)pk;
+        x[h] = valid ? quad_sum(s[h]) * a.scale_log2 : -INFINITY;
+        grow |= x[h] > m[h] + kSlack;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float m_new = fmaxf(m[h], max_over_quads(x[h]));
+          const float alpha = exp2_fast(m[h] - m_new);
+          m[h] = m_new;
+          l_lane[h] *= alpha;
+          acc[h][0] *= alpha;
+          acc[h][1] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t pk = pack_bf16(exp2_fast(x[h] - m[h]), 0.f);
+        l_lane[h] += bf16_lo(pk);
+        // the 4 lanes of a token hold the same weight and all store it
+        *(u16_alias *)(plds + h * (kChunk * 2) + r * 2) = (uint16_t)pk;
       }
 
       // ---- P.V: lanes own head_dim columns, tokens in pairs ----
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        acc[h][0] *= alpha[h];
-        acc[h][1] *= alpha[h];
-      }
       const char *vst = st + CHB;
 #pragma unroll
       for (int jj = 0; jj < PAIRS; ++jj) {
@@ -231,13 +278,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
         const uint32_t lo = lo_pair(va, vb), hi = hi_pair(va, vb);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const uint32_t pp = *(const uint32_t *)(plds + h * (kChunk * 2) + j * 4);
+          const uint32_t pp = *(const u32_alias *)(plds + h * (kChunk * 2) + j * 4);
           acc[h][0] = dot2(pp, lo, acc[h][0]);
           acc[h][1] = dot2(pp, hi, acc[h][1]);
         }
       }
 
-      if (i + NSTAGE < n_my) issue_chunk(ci + kWaves * NSTAGE, i % NSTAGE);
+      if (i + NSTAGE < n_my) {
+        const int cn = ci + kWaves * NSTAGE;
+        issue_chunk(cn, i % NSTAGE, table[(t0 + cn * kChunk) >> bs_shift]);
+      }
     }
   }
 
@@ -271,6 +321,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
+  const bool direct = a.o_part == nullptr;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D;
     float mw[kWaves];
@@ -290,58 +341,107 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
         num += e * mw_base[2 * G + idx];
       }
     }
-    const float o = den > 0.f ? num / den : 0.f;
-    if (a.o_part == nullptr) {
+    // den is 0 only when no wave saw a token (empty sequence); a NaN read from
+    // the cache propagates to the output.
+    const float o = den != 0.f ? num / den : 0.f;
+    if (direct) {
       a.out[head0 * D + idx] = (uint16_t)pack_bf16(o, 0.f);
     } else {
       const size_t row = (head0 + h) * a.num_splits + split;
       a.o_part[row * D + (idx % D)] = o;
-      if (idx % D == 0) a.lse_part[row] = den > 0.f ? M + log2_fast(den) : -INFINITY;
+      if (idx % D == 0) a.lse_part[row] = den != 0.f ? M + log2_fast(den) : -INFINITY;
     }
   }
 }
 
-// Merge the pieces of one (sequence, q head): one wave per output row.
+// Merge the pieces of one (sequence, q head) row; one 256-thread workgroup
+// per row.  Thread t reads lse of piece t; the workgroup max and the weights
+// 2^(lse_s - M) go through LDS.  For the weighted sum, thread t owns float4
+// column group t % (D/4) and pieces s = t / (D/4) (mod 256 / (D/4)); all of
+// its piece loads are issued before the weights are known, so the row costs
+// one memory round trip rather than one per piece.
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int NV = D / 4;        // float4 column groups per row
+  constexpr int SG = 256 / NV;     // piece groups
+  constexpr int BATCH = 8;         // piece loads in flight per thread
+  __shared__ float w_lds[256];
+  __shared__ float red_max[4], red_sum[4];
+  __shared__ float4 red[SG][NV];
   const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int L = as_const(a.context_lens)[b];
   const int S = a.num_splits;
   const size_t row = (size_t)b * a.num_q_heads + h;
-  constexpr int PER = D / 64;  // columns per lane
-  uint16_t *out = a.out + row * D + lane * PER;
+  uint16_t *out = a.out + row * D;
   if (L <= 0) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) out[e] = 0;
+    if (tid < D) out[tid] = 0;
     return;
   }
   const int ns = min(S, (L + a.split_len - 1) / a.split_len);
-  const auto *lse = as_const(a.lse_part + row * S);
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, lse[s]);
-  M = wave_max(M);
-  float den = 0.f;
-  float acc[PER];
+  const int v = tid % NV, sg = tid / NV;
+  const float4 *op = (const float4 *)(a.o_part + row * (size_t)S * D) + v;
+
+  float4 ov[BATCH];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  const float *op = a.o_part + row * (size_t)S * D + lane * PER;
-  for (int s = 0; s < ns; ++s) {
-    const float w = exp2_fast(lse[s] - M);
-    den += w;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * op[(size_t)s * D + e];
+  for (int k = 0; k < BATCH; ++k) {
+    const int s = sg + k * SG;
+    ov[k] = s < ns ? op[(size_t)s * NV] : float4{0.f, 0.f, 0.f, 0.f};
   }
-  const float inv = 1.f / den;
+  const float lse = tid < ns ? a.lse_part[row * S + tid] : -INFINITY;
+  float M = wave_max(lse);
+  if (lane == 0) red_max[wv] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
+  const float w = tid < ns ? exp2_fast(lse - M) : 0.f;
+  w_lds[tid] = w;
+  float ws = w;
+  ws += dpp<0xB1>(ws);
+  ws += dpp<0x4E>(ws);
+  ws = sum_over_quads(ws);
+  if (lane == 0) red_sum[wv] = ws;
+  __syncthreads();
+  const float den = (red_sum[0] + red_sum[1]) + (red_sum[2] + red_sum[3]);
+
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int e = 0; e < PER; ++e) out[e] = (uint16_t)pack_bf16(acc[e] * inv, 0.f);
+  for (int k = 0; k < BATCH; ++k) {
+    const float wk = w_lds[min(sg + k * SG, 255)];
+    acc.x += wk * ov[k].x; acc.y += wk * ov[k].y; acc.z += wk * ov[k].z; acc.w += wk * ov[k].w;
+  }
+  for (int s0 = BATCH * SG; s0 < ns; s0 += BATCH * SG) {
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int s = s0 + sg + k * SG;
+      ov[k] = s < ns ? op[(size_t)s * NV] : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const float wk = w_lds[min(s0 + sg + k * SG, 255)];
+      acc.x += wk * ov[k].x; acc.y += wk * ov[k].y; acc.z += wk * ov[k].z; acc.w += wk * ov[k].w;
+    }
+  }
+  red[sg][v] = acc;
+  __syncthreads();
+  if (tid < NV) {
+    float4 t = red[0][tid];
+#pragma unroll
+    for (int k = 1; k < SG; ++k) {
+      t.x += red[k][tid].x; t.y += red[k][tid].y; t.z += red[k][tid].z; t.w += red[k][tid].w;
+    }
+    const float inv = 1.f / den;
+    uint2 pk;
+    pk.x = pack_bf16(t.x * inv, t.y * inv);
+    pk.y = pack_bf16(t.z * inv, t.w * inv);
+    *(uint2 *)(out + 4 * tid) = pk;
+  }
 }
 
 constexpr int kStages = 2;
 
 template <int D, int G>
 hipError_t launch_split_dg(const DecodeArgs &a, int num_seqs, hipStream_t stream) {
-  dim3 grid(a.num_splits, a.num_kv_heads, num_seqs);
+  dim3 grid(num_seqs * a.num_kv_heads, a.num_splits);
   hipLaunchKernelGGL((decode_split_kernel<D, G, kStages>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -374,9 +474,9 @@ hipError_t launch_decode_combine(const DecodeArgs &a, int head_dim, int num_seqs
                                  hipStream_t stream) {
   dim3 grid(a.num_q_heads, num_seqs);
   if (head_dim == 128)
-    hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(256), 0, stream, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(256), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

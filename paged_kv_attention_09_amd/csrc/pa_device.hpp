@@ -10,6 +10,12 @@ namespace pa {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// LDS scratch is written and read back at different widths (bf16 weights
+// stored singly, read in pairs); these types keep type-based alias analysis
+// from reordering such accesses.
+typedef uint16_t __attribute__((may_alias)) u16_alias;
+typedef uint32_t __attribute__((may_alias)) u32_alias;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -84,6 +90,13 @@ __device__ __forceinline__ float sum_over_quads(float x) {
   float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
   float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
   return (r0 + r1) + (r2 + r3);
+}
+
+// Sum of x over the 64 lanes of the wave, returned in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  return sum_over_quads(x);
 }
 
 // Sum of the 4 lanes of each quad, in every lane of the quad.

@@ -21,6 +21,8 @@ struct DecodeArgs {
   const uint16_t *v_cache;
   const int32_t *block_tables;  // [B, W]
   const int32_t *context_lens;  // [B]
+  const uint16_t *new_k;      // [B, Hkv, D] rows appended at token L_b - 1, or null
+  const uint16_t *new_v;
   uint16_t *out;              // [B, Hq, D]        (num_splits == 1)
   float *o_part;              // [B, Hq, S, D]     (num_splits > 1)
   float *lse_part;            // [B, Hq, S], base-2 log-sum-exp of scaled scores

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n

@@ -239,3 +239,107 @@ def test_nonzero_stream_and_no_host_sync():
         case.run(num_splits=0, stream=s)
     s.synchronize()
     assert_close(to_f64(case.out), case.ref, what="side stream")
+
+
+@pytest.mark.parametrize("name,S", [("c3", 0), ("c3", 1), ("c5d", 0), ("c2b8", 7), ("empty", 4)])
+def test_fused_append_decode(name, S):
+    """append_decode == reshape_and_cache at each sequence's last token followed
+    by decode: pools bit-exact against the oracle append, output within
+    tolerance of the oracle decode."""
+    import oracle
+    import paged_kv_attention_09_amd as pa
+    if name == "empty":
+        spec = W.CONFIGS["c1"].with_(context_lens=(0, 17, 0, 3), append=True)
+    else:
+        spec = W.CONFIGS[name].with_(append=True)
+    inp = W.make_decode_inputs(spec)
+    case = DecodeCase(inp)
+    B, Hkv, D = spec.num_seqs, spec.num_kv_heads, spec.head_dim
+    sel = np.nonzero(inp.context_lens > 0)[0]
+    nk = np.zeros((B, Hkv, D), np.uint16)
+    nv = np.zeros((B, Hkv, D), np.uint16)
+    nk[sel], nv[sel] = inp.new_k, inp.new_v
+    before_k, before_v = to_bits(case.k_cache), to_bits(case.v_cache)
+    pa.append_decode(case.q, bf16_tensor(nk), bf16_tensor(nv), case.k_cache, case.v_cache,
+                     case.tables, case.lens, case.scale, S, case.out)
+    torch.cuda.synchronize()
+    want_k, want_v = oracle.append(inp.new_k, inp.new_v, inp.slot_mapping, before_k, before_v)
+    assert np.array_equal(to_bits(case.k_cache), want_k)
+    assert np.array_equal(to_bits(case.v_cache), want_v)
+    assert_close(to_f64(case.out), case.ref, what=f"fused {name} S={S}")
+
+
+def test_workspace_reused_across_calls():
+    """One workspace shared by consecutive calls on different inputs: each
+    result matches its own oracle (no stale partials)."""
+    import paged_kv_attention_09_amd as pa
+    cases = [DecodeCase(W.make_decode_inputs(W.CONFIGS["c2b8"].with_(seed=s))) for s in (11, 12)]
+    ws = torch.zeros(pa.decode_workspace_size(8, 12, 128, 32), dtype=torch.uint8, device=DEV)
+    for c in cases + cases[::-1]:
+        pa.decode(c.q, c.k_cache, c.v_cache, c.tables, c.lens, c.scale, 32, c.out, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(to_f64(c.out), c.ref, what="reuse")
+
+
+def test_partials_then_merge_matches_decode():
+    """The two passes as separate calls reach the oracle and agree with the
+    single-launch decode up to rounding (the merges sum in different orders,
+    and the single launch writes one-piece sequences without a merge)."""
+    import paged_kv_attention_09_amd as pa
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c3"]))
+    one = _run(case, 0)
+    s = case.inp.spec
+    S = pa.auto_splits(s.num_seqs, s.num_kv_heads, s.max_blocks_per_seq, s.block_size)
+    ws = torch.zeros(pa.decode_workspace_size(s.num_seqs, s.num_q_heads, s.head_dim, S),
+                     dtype=torch.uint8, device=DEV)
+    out2 = torch.empty_like(case.out)
+    pa.decode_partials(case.q, case.k_cache, case.v_cache, case.tables, case.lens, case.scale, S, ws)
+    pa.decode_merge(ws, case.lens, out2, S, s.num_kv_heads, s.block_size, s.max_blocks_per_seq)
+    torch.cuda.synchronize()
+    two = to_f64(out2)
+    assert_close(two, case.ref, what="partials+merge")
+    assert (np.abs(two - one) <= 2 ** -7 * np.abs(one) + 1e-4).all()
+
+
+def test_graph_replays_match_eager():
+    """A captured graph of append + decode calls gives, on every replay, the
+    result of eager execution (with eager work and syncs between replays)."""
+    import paged_kv_attention_09_amd as pa
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c3"].with_(append=False)))
+    s = case.inp.spec
+    S = 16
+    n = pa.decode_workspace_size(s.num_seqs, s.num_q_heads, s.head_dim, S)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    pa.decode(case.q, case.k_cache, case.v_cache, case.tables, case.lens, case.scale, S, case.out,
+              workspace=ws)
+    torch.cuda.synchronize()
+    eager = to_bits(case.out.clone())
+    assert_close(to_f64(case.out), case.ref, what="eager")
+    g = torch.cuda.CUDAGraph()
+    out2 = torch.empty_like(case.out)
+    with torch.cuda.graph(g):
+        pa.decode(case.q, case.k_cache, case.v_cache, case.tables, case.lens, case.scale, S, out2,
+                  workspace=ws)
+    for i in range(4):
+        out2.fill_(0)
+        ws.fill_(0x7F)            # stale partials must not leak into a replay
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(out2), eager), i
+
+
+@pytest.mark.parametrize("S", [1, 0])
+def test_nan_in_a_read_token_propagates(S):
+    """Poison must not be read - but a NaN that IS part of the context must
+    reach the output of the heads reading it, not be masked to a number."""
+    spec = W.CONFIGS["c2b8"].with_(append=False)
+    inp = W.make_decode_inputs(spec)
+    b, t = 3, 1234
+    i = list(inp.pool.ids).index(int(inp.block_tables[b, t // 16]))
+    inp.pool.v[i, t % 16, 1, 5] = W.BF16_NAN      # kv head 1, column 5
+    case = DecodeCase(inp, with_oracle=False)
+    out = _run(case, S)
+    G = spec.group
+    assert np.isnan(out[b, G:, 5]).all()          # q heads of kv head 1
+    assert np.isfinite(out[b, :G]).all() and np.isfinite(np.delete(out, b, axis=0)).all()
