@@ -197,15 +197,35 @@ int pa_decode_auto_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq
  *   q            bf16 [total_q, num_q_heads, head_dim], total_q = cu_seqlens_q[num_seqs]
  *   cu_seqlens_q int32 [num_seqs + 1], non-decreasing, from 0
  *   out          bf16 [total_q, num_q_heads, head_dim]
- *   max_q_len    an upper bound of every n_b (sizes the launch grid)
+ *   max_q_len    an upper bound of every n_b (sizes the launch grid); every
+ *                n_b must also be <= context_lens[b] (not checked)
+ *   num_splits   pieces of the key range (0 = choose automatically, see
+ *                pa_prefill_plan_splits); with more than one piece a second
+ *                kernel merges them by log-sum-exp, as in pa_decode
+ *   workspace    at least pa_prefill_workspace_size(num_seqs, max_q_len,
+ *                num_q_heads, head_dim, S) bytes for the S actually used
+ *                (may be NULL when that is 0)
  * The QK^T and PV products run on the bf16 matrix cores (MFMA) with fp32
  * accumulation; softmax weights are rounded to bf16 for the PV product.
  */
 int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
                const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
-               float scale, void *out, int num_seqs, int max_q_len, int num_q_heads,
-               int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
-               int max_blocks_per_seq, void *stream);
+               float scale, int num_splits, void *out, int num_seqs, int max_q_len,
+               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+               int64_t num_blocks, int max_blocks_per_seq, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* Workspace bytes pa_prefill needs for a given split count (0 when
+ * num_splits <= 1).  Returns 0 for invalid arguments. */
+size_t pa_prefill_workspace_size(int num_seqs, int max_q_len, int num_q_heads, int head_dim,
+                                 int num_splits);
+
+/* Split count pa_prefill uses for num_splits = 0 on a device with num_cus
+ * compute units: the key range is cut until the (32 query positions, kv
+ * head, piece) work units number about one per compute unit.  Returns a value
+ * in [1, PA_MAX_SPLITS] or a negative status. */
+int pa_prefill_plan_splits(int num_seqs, int max_q_len, int num_kv_heads, int max_blocks_per_seq,
+                           int block_size, int num_cus);
 
 #ifdef __cplusplus
 }

@@ -14,7 +14,7 @@ Calls (argument order as in the C ABI):
                 num_splits, out, stream=None, workspace=None)
   decode_partials(...), decode_merge(...): the two passes of decode
   prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, out,
-          max_q_len, stream=None)
+          max_q_len, num_splits=0, stream=None, workspace=None)
   decode_workspace_size(num_seqs, num_q_heads, head_dim, num_splits)
   plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus)
   auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, device=None)
@@ -49,8 +49,10 @@ SIGNATURES = {
     "pa_decode_partials": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _I, _I, _I, _I, _I, _I, _I64, _I, _VP,
                                 _SZ, _VP]),
     "pa_decode_merge": (_I, [_VP, _SZ, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP]),
-    "pa_prefill": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _F, _VP, _I, _I, _I, _I, _I, _I, _I64, _I,
-                        _VP]),
+    "pa_prefill": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _F, _I, _VP, _I, _I, _I, _I, _I, _I, _I64,
+                        _I, _VP, _SZ, _VP]),
+    "pa_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+    "pa_prefill_plan_splits": (_I, [_I, _I, _I, _I, _I, _I]),
 }
 
 _lib = None
@@ -261,11 +263,13 @@ def decode_merge(workspace: torch.Tensor, context_lens, out, num_splits: int, nu
 
 
 def prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
-            max_q_len: int, stream=None):
+            max_q_len: int, num_splits: int = 0, stream=None,
+            workspace: Optional[torch.Tensor] = None):
     """Causal attention of packed chunk queries q [Tq, Hq, D] (sequence b owns
     rows cu_seqlens_q[b]..cu_seqlens_q[b+1]) over each sequence's cached
     context_lens[b] tokens, chunk included; query i of an n-row chunk sits at
-    position context_lens[b] - n + i."""
+    position context_lens[b] - n + i.  num_splits = 0 picks the key split
+    automatically."""
     NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
     dev = k_cache.device
     _need(q, "q", torch.bfloat16, 3, dev)
@@ -280,12 +284,43 @@ def prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale
     if cu_seqlens_q.shape[0] != B + 1 or block_tables.shape[0] != B:
         raise ValueError("cu_seqlens_q must have num_seqs + 1 entries")
     W = int(block_tables.shape[1])
+    if num_splits == 0 and B > 0 and max_q_len > 0:
+        num_splits = prefill_auto_splits(B, int(max_q_len), Hkv, W, bs, dev)
+    need = (int(lib().pa_prefill_workspace_size(B, int(max_q_len), Hq, D, int(num_splits)))
+            if B > 0 and max_q_len > 0 else 0)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace needs {need} bytes")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check("pa_prefill", lib().pa_prefill(
         q.data_ptr(), cu_seqlens_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), out.data_ptr(), B,
-        int(max_q_len), Hq, Hkv, D, bs, NB, W, _stream_ptr(stream, dev)))
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), int(num_splits),
+        out.data_ptr(), B, int(max_q_len), Hq, Hkv, D, bs, NB, W, ws_ptr, ws_bytes,
+        _stream_ptr(stream, dev)))
     return out
 
 
-__all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "decode_merge", "prefill", "decode_workspace_size", "plan_splits",
+def prefill_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim, num_splits) -> int:
+    return int(lib().pa_prefill_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim,
+                                               num_splits))
+
+
+def prefill_auto_splits(num_seqs, max_q_len, num_kv_heads, max_blocks_per_seq, block_size,
+                        device=None) -> int:
+    if device is None:
+        device = torch.cuda.current_device()
+    elif isinstance(device, torch.device):
+        device = device.index if device.index is not None else torch.cuda.current_device()
+    cus = torch.cuda.get_device_properties(int(device)).multi_processor_count
+    r = int(lib().pa_prefill_plan_splits(num_seqs, max_q_len, num_kv_heads, max_blocks_per_seq,
+                                         block_size, cus))
+    _check("pa_prefill_plan_splits", min(r, 0))
+    return r
+
+
+__all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "decode_merge", "prefill",
+           "prefill_workspace_size", "prefill_auto_splits", "decode_workspace_size", "plan_splits",
            "auto_splits", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError", "PA_MAX_SPLITS"]

@@ -290,20 +290,57 @@ int pa_decode_merge(const void *workspace, size_t workspace_bytes, const int32_t
              : PA_ERR_HIP;
 }
 
+size_t pa_prefill_workspace_size(int num_seqs, int max_q_len, int num_q_heads, int head_dim,
+                                 int num_splits) {
+  if (num_seqs <= 0 || max_q_len <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  if (num_splits <= 1 || num_splits > PA_MAX_SPLITS) return 0;
+  const size_t rows = (size_t)num_seqs * max_q_len * num_q_heads * num_splits;
+  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
+  return o_bytes + (rows * sizeof(float) + 255) / 256 * 256;
+}
+
+int pa_prefill_plan_splits(int num_seqs, int max_q_len, int num_kv_heads, int max_blocks_per_seq,
+                           int block_size, int num_cus) {
+  if (num_seqs <= 0 || max_q_len <= 0 || num_kv_heads <= 0 || num_cus <= 0) return PA_ERR_SHAPE;
+  const int st = check_pool(1, block_size, max_blocks_per_seq);
+  if (st != PA_OK) return st;
+  const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
+  // One workgroup per 32 query positions and kv head; split the key range
+  // until there is about one workgroup per compute unit.
+  const int64_t units = (int64_t)num_seqs * num_kv_heads * ((max_q_len + 31) / 32);
+  int64_t s = 1;
+  if (units < num_cus) s = (num_cus + units - 1) / units;
+  if (s > PA_MAX_SPLITS) s = PA_MAX_SPLITS;
+  int n = num_pieces(max_tokens, split_len_for(max_tokens, (int)s));
+  return n < 1 ? 1 : (n > PA_MAX_SPLITS ? PA_MAX_SPLITS : n);
+}
+
 int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
                const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
-               float scale, void *out, int num_seqs, int max_q_len, int num_q_heads,
-               int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
-               int max_blocks_per_seq, void *stream) {
+               float scale, int num_splits, void *out, int num_seqs, int max_q_len,
+               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+               int64_t num_blocks, int max_blocks_per_seq, void *workspace,
+               size_t workspace_bytes, void *stream) {
   if (num_seqs < 0 || max_q_len < 0) return PA_ERR_SHAPE;
   int st = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (st != PA_OK) return st;
   st = check_pool(num_blocks, block_size, max_blocks_per_seq);
   if (st != PA_OK) return st;
+  if (num_splits < 0 || num_splits > PA_MAX_SPLITS) return PA_ERR_SPLITS;
   if (!(std::isfinite(scale))) return PA_ERR_SHAPE;
   if (num_seqs == 0 || max_q_len == 0) return PA_OK;
   if (!q || !cu_seqlens_q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return PA_ERR_NULL;
+  if (num_splits == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+    const int cus = cu_count(dev);
+    if (cus <= 0) return PA_ERR_HIP;
+    num_splits = pa_prefill_plan_splits(num_seqs, max_q_len, num_kv_heads, max_blocks_per_seq,
+                                        block_size, cus);
+    if (num_splits < 0) return num_splits;
+  }
+  const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
   pa::PrefillArgs a;
   a.q = (const uint16_t *)q;
   a.cu_seqlens_q = cu_seqlens_q;
@@ -312,6 +349,8 @@ int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = (uint16_t *)out;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -319,10 +358,24 @@ int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.bs_shift = log2_exact(block_size);
   a.max_q_len = max_q_len;
-  const hipError_t e = pa::launch_prefill(a, head_dim, num_q_heads / num_kv_heads,
-                                          (hipStream_t)stream);
+  a.split_len = split_len_for(max_tokens, num_splits);
+  a.num_splits = num_pieces(max_tokens, a.split_len);
+  if (a.num_splits > 1) {
+    const size_t need = pa_prefill_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim,
+                                                  a.num_splits);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    const size_t rows = (size_t)num_seqs * max_q_len * num_q_heads * a.num_splits;
+    a.o_part = (float *)workspace;
+    a.lse_part = (float *)((char *)workspace + (rows * head_dim * sizeof(float) + 255) / 256 * 256);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = pa::launch_prefill(a, head_dim, num_q_heads / num_kv_heads, s);
   if (e == hipErrorInvalidValue) return PA_ERR_UNSUPPORTED;
-  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (a.num_splits > 1 &&
+      pa::launch_prefill_merge(a, head_dim, num_seqs * max_q_len, s) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
 }
 
 }  // extern "C"

@@ -128,6 +128,13 @@ __device__ __forceinline__ uint32_t lds_offset(T *p) {
 // first (lgkmcnt(0)) so a buffer is never overwritten under a pending read.
 // M0 is saved and restored around the use.
 __device__ __forceinline__ void dma16(uint32_t lds, const void *base, uint32_t voff) {
+  // Both are wave-uniform by contract; readfirstlane puts them in SGPRs even
+  // where the compiler cannot prove uniformity.
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  const uint64_t b64 = (uint64_t)(uintptr_t)base;
+  base = (const void *)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32))
+                                    << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64));
   uint32_t saved;
   asm volatile(
       "s_waitcnt lgkmcnt(0)\n\t"

@@ -40,9 +40,13 @@ struct PrefillArgs {
   const int32_t *block_tables;
   const int32_t *context_lens;
   uint16_t *out;              // [Tq, Hq, D]
+  float *o_part;              // [Tq, Hq, S, D] when the key range is split, else null
+  float *lse_part;            // [Tq, Hq, S]
   float scale_log2;
   int num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, bs_shift;
   int max_q_len;
+  int split_len;              // keys per piece, multiple of 64
+  int num_splits;
 };
 
 hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t stream);
@@ -52,5 +56,7 @@ hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, int group, int
 hipError_t launch_decode_combine(const DecodeArgs &a, int head_dim, int num_seqs,
                                  hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, int head_dim, int group, hipStream_t stream);
+hipError_t launch_prefill_merge(const PrefillArgs &a, int head_dim, int total_q_bound,
+                                hipStream_t stream);
 
 }  // namespace pa

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -87,15 +87,30 @@ def test_append_argument_checks():
 
 def test_prefill_argument_checks():
     f = pa.lib().pa_prefill
-    args = [P, P, P, P, P, P, 0.1, P, 1, 512, 28, 4, 128, 256, 100, 16, None]
-    bad = list(args); bad[12] = 100
+    args = [P, P, P, P, P, P, 0.1, 1, P, 1, 512, 28, 4, 128, 256, 100, 16, None, 0, None]
+    bad = list(args); bad[13] = 100
     assert f(*bad) == UNSUP
-    bad = list(args); bad[10] = 30
+    bad = list(args); bad[11] = 30
     assert f(*bad) == SHAPE
     bad = list(args); bad[1] = None
     assert f(*bad) == NULL
-    ok0 = list(args); ok0[9] = 0
+    bad = list(args); bad[7] = 4                 # split without a workspace
+    assert f(*bad) == WS
+    bad = list(args); bad[7] = 300
+    assert f(*bad) == SPLITS
+    ok0 = list(args); ok0[10] = 0
     assert f(*ok0) == OK
+
+
+def test_prefill_planning():
+    L = pa.lib()
+    # one 512-token chunk, 4 kv heads: 64 units -> split the 4096 keys in 4
+    assert L.pa_prefill_plan_splits(1, 512, 4, 16, 256, 256) == 4
+    assert L.pa_prefill_plan_splits(8, 512, 8, 16, 256, 256) == 1
+    rows = 1 * 512 * 28 * 4
+    want = (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    assert L.pa_prefill_workspace_size(1, 512, 28, 128, 4) == want
+    assert L.pa_prefill_workspace_size(1, 512, 28, 128, 1) == 0
 
 
 def test_workspace_size():
