@@ -65,12 +65,18 @@ def parse_args(argv=None):
     p.add_argument("--rotate-gib", type=float, default=2.0)
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--others", default="c2b1,c3,c4,c5d",
+    p.add_argument("--others", default="c2b1,c3,c4,c5d,c5p,c5mix",
                    help="comma list of extra workloads measured into 'workloads' ('' = none)")
     p.add_argument("--kernel-loop", type=int, default=0,
                    help="profiling mode: launch only the split kernel this many times and exit")
     p.add_argument("--sweep-splits", default="",
                    help="tuning mode: comma list of split counts; prints us/step per workload")
+    p.add_argument("--ingest-trace", nargs=3, metavar=("DIR", "NAME", "COMMAND"),
+                   help="write profiles/NAME.md from a rocprofv3 --stats output directory")
+    p.add_argument("--ingest-counters", nargs=7,
+                   metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR",
+                            "COPY_MIB", "KERNEL_CMD", "COPY_CMD"),
+                   help="write profiles/decode_split_<workload>_hbm_counters.{json,md}")
     p.add_argument("--copy-calibration", type=int, default=0,
                    help="profiling mode: run a plain device copy of this many MiB, 20 times")
     return p.parse_args(argv)
@@ -180,6 +186,164 @@ class DecodeWorkload:
                       1, self.out, workspace=self.ws)
 
 
+class PrefillWorkload:
+    """A prompt chunk (causal, over its cached prefix) and, optionally, the
+    decode sequences that share the step with it, in one pool with R block
+    rotations.  step() is the mixed-batch step: slot-mapped append of the
+    chunk's K/V, the chunked prefill on MFMA, then the fused append + decode
+    of the decode sequences."""
+
+    def __init__(self, pspec, dspec, rotate_gib: float, seed: int = 4321):
+        import numpy as np
+        import torch
+
+        import paged_kv_attention_09_amd as pa
+        import workloads as W
+
+        self.pa = pa
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        bs, Hkv, D, Hq = pspec.block_size, pspec.num_kv_heads, pspec.head_dim, pspec.num_q_heads
+        assert dspec is None or (dspec.block_size, dspec.num_kv_heads, dspec.head_dim,
+                                 dspec.num_q_heads) == (bs, Hkv, D, Hq)
+        self.plens = np.asarray(pspec.total_lens, np.int32)
+        self.chunks = np.asarray(pspec.chunk_lens, np.int32)
+        self.dlens = W.draw_context_lens(dspec) if dspec is not None else np.zeros(0, np.int32)
+        P, B = len(self.plens), len(self.dlens)
+        pblk = [-(-int(L) // bs) for L in self.plens]
+        dblk = [-(-int(L) // bs) for L in self.dlens]
+        per_rot = sum(pblk) + sum(dblk)
+        kv_bytes = (int(self.plens.sum()) + int(self.dlens.sum())) * Hkv * D * 2 * 2
+        self.R = max(1, math.ceil(rotate_gib * 2**30 / kv_bytes))
+        NB = max(pspec.num_blocks, self.R * per_rot + 1)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        shape = (NB, bs, Hkv, D)
+        self.k_cache = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        self.v_cache = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        step = max(1, (256 << 20) // (bs * Hkv * D * 2))
+        for i in range(0, NB, step):
+            j = min(NB, i + step)
+            self.k_cache[i:j].normal_(generator=g)
+            self.v_cache[i:j].normal_(generator=g)
+        perm = torch.randperm(NB, generator=g, device=dev).cpu().numpy()
+        Wp, Wd = pspec.max_blocks_per_seq, (dspec.max_blocks_per_seq if dspec else 1)
+        self.ptables, self.dtables, self.cslots = [], [], []
+        for r in range(self.R):
+            ids = perm[r * per_rot:(r + 1) * per_rot]
+            tp = np.full((P, Wp), int(perm[-1]), np.int32)
+            td = np.full((max(B, 1), Wd), int(perm[-1]), np.int32)
+            off = 0
+            for b, nblk in enumerate(pblk):
+                tp[b, :nblk] = ids[off:off + nblk]
+                off += nblk
+            for b, nblk in enumerate(dblk):
+                td[b, :nblk] = ids[off:off + nblk]
+                off += nblk
+            slots = []
+            for b in range(P):
+                for t in range(int(self.plens[b] - self.chunks[b]), int(self.plens[b])):
+                    slots.append(int(tp[b, t // bs]) * bs + t % bs)
+            self.ptables.append(torch.from_numpy(tp).to(dev))
+            self.dtables.append(torch.from_numpy(td).to(dev))
+            self.cslots.append(torch.from_numpy(np.asarray(slots, np.int64)).to(dev))
+        Tq = int(self.chunks.sum())
+        self.Tq = Tq
+        cu = np.zeros(P + 1, np.int32)
+        cu[1:] = np.cumsum(self.chunks)
+        self.cu = torch.from_numpy(cu).to(dev)
+        self.plens_t = torch.from_numpy(self.plens).to(dev)
+        self.max_q = int(self.chunks.max())
+        self.q = torch.randn((Tq, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+        self.ck = torch.randn((Tq, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+        self.cv = torch.randn((Tq, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+        self.out = torch.empty_like(self.q)
+        self.scale = float(pspec.scale_f32)
+        self.S = pa.prefill_auto_splits(P, self.max_q, Hkv, Wp, bs, dev)
+        self.ws = torch.zeros(max(pa.prefill_workspace_size(P, self.max_q, Hq, D, self.S), 256),
+                              dtype=torch.uint8, device=dev)
+        pos = np.concatenate([np.arange(int(L - n), int(L)) for L, n in zip(self.plens, self.chunks)])
+        self.flop = 4 * D * Hq * int((pos + 1).sum())
+        self.append_bytes = Tq * Hkv * D * 2 * 2 * 2 + Tq * 8
+        self.prefill_bytes = (int(self.plens.sum()) * Hkv * D * 2 * 2 + 2 * Tq * Hq * D * 2)
+        if B:
+            self.dlens_t = torch.from_numpy(self.dlens).to(dev)
+            self.dq = torch.randn((B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+            self.dk = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+            self.dv = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+            self.dout = torch.empty_like(self.dq)
+            self.dS = pa.auto_splits(B, Hkv, Wd, bs, dev)
+            self.dws = torch.zeros(max(pa.decode_workspace_size(B, Hq, D, self.dS), 256),
+                                   dtype=torch.uint8, device=dev)
+            self.decode_bytes = W.algorithmic_decode_bytes(self.dlens, Hq, Hkv, D, bs) + \
+                B * Hkv * D * 2 * 2 * 2
+        self.B = B
+        # the chunk's K/V must be in the pool before any prefill-only timing
+        for r in range(self.R):
+            self.append_chunk(r)
+        torch.cuda.synchronize()
+
+    def append_chunk(self, r):
+        self.pa.reshape_and_cache(self.ck, self.cv, self.cslots[r], self.k_cache, self.v_cache)
+
+    def prefill(self, r):
+        self.pa.prefill(self.q, self.cu, self.k_cache, self.v_cache, self.ptables[r],
+                        self.plens_t, self.scale, self.out, self.max_q, num_splits=self.S,
+                        workspace=self.ws)
+
+    def decode(self, r):
+        self.pa.append_decode(self.dq, self.dk, self.dv, self.k_cache, self.v_cache,
+                              self.dtables[r], self.dlens_t, self.scale, self.dS, self.dout,
+                              workspace=self.dws)
+
+    def step(self, r):
+        self.append_chunk(r)
+        self.prefill(r)
+        if self.B:
+            self.decode(r)
+
+
+def time_graph(fn, R: int, steps: int, warmup: int) -> float:
+    """Average milliseconds of fn(i % R) over `steps` calls captured in one
+    HIP graph (after `warmup` eager calls)."""
+    import torch
+    for i in range(warmup):
+        fn(i % R)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i % R)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def measure_prefill(args, steps, warmup, with_decode: bool):
+    import workloads as W
+    wl = PrefillWorkload(W.PREFILL_CONFIGS["c5p"], W.CONFIGS["c5d"] if with_decode else None,
+                         args.rotate_gib)
+    ms_pf = time_graph(wl.prefill, wl.R, steps, warmup)
+    rec = {"prefill_us": ms_pf * 1e3, "prefill_tflops": wl.flop / (ms_pf * 1e-3) / 1e12,
+           "prefill_splits": wl.S, "prefill_gflop": wl.flop / 1e9, "query_rows": wl.Tq,
+           "rotations": wl.R}
+    if with_decode:
+        ms_step = time_graph(wl.step, wl.R, steps, warmup)
+        ms_dec = time_graph(wl.decode, wl.R, steps, warmup)
+        ms_app = time_graph(wl.append_chunk, wl.R, steps, warmup)
+        rec.update({"us_per_step": ms_step * 1e3, "decode_us": ms_dec * 1e3,
+                    "decode_gbps": wl.decode_bytes / (ms_dec * 1e-3) / 1e9,
+                    "append_us": ms_app * 1e3, "decode_splits": wl.dS,
+                    "step": "append 512-token chunk, MFMA prefill, fused append + decode of 64"})
+    return wl, rec
+
+
 def sleep_cycles_for(ms: float) -> int:
     """Calibrate torch.cuda._sleep (device spin) to roughly `ms` milliseconds."""
     import torch
@@ -236,6 +400,103 @@ def time_steps_graph(wl, steps: int, warmup: int, fused: bool = True):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return s.elapsed_time(e) / steps, wall
+
+
+def _short_kernel(name: str) -> str:
+    for k in ("decode_split_kernel", "decode_combine_kernel", "append_kernel", "prefill_kernel",
+              "prefill_merge_kernel", "spin_kernel"):
+        if k in name:
+            tmpl = name[name.find(k):]
+            return tmpl[:tmpl.find("(")] if "(" in tmpl else tmpl
+    return name[:60]
+
+
+def _read_csv(directory: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return rows
+
+
+def ingest_trace(directory: str, out_name: str, command: str):
+    """rocprofv3 --stats CSV -> a short markdown summary under profiles/."""
+    rows = _read_csv(directory, "kernel_stats.csv")
+    lines = [f"# Kernel durations: {out_name}", "", "Command (run from /tmp with TMPDIR=/tmp):", "",
+             "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        k = _short_kernel(r["Name"])
+        if not k.startswith(("decode", "append", "prefill")):
+            continue
+        lines.append(f"| `{k}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    path = os.path.join(PROFILES, out_name + ".md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
+def ingest_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib: int,
+                    workload: str, command_kernel: str, command_copy: str):
+    """FETCH_SIZE / WRITE_SIZE per dispatch of the split kernel, scaled by what
+    the same counters read for a plain device copy of known size."""
+    import statistics
+
+    def med(rows, counter, pick):
+        v = [float(r["Counter_Value"]) for r in rows
+             if r["Counter_Name"] == counter and pick(r["Kernel_Name"])]
+        if not v:
+            raise SystemExit(f"no {counter} rows")
+        return statistics.median(v)
+
+    is_split = lambda n: "decode_split_kernel" in n                            # noqa: E731
+    fetch = med(_read_csv(fetch_dir, "counter_collection.csv"), "FETCH_SIZE", is_split)
+    write = med(_read_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE", is_split)
+    copy_rows_f = _read_csv(copy_fetch_dir, "counter_collection.csv")
+    copy_rows_w = _read_csv(copy_write_dir, "counter_collection.csv")
+    big = lambda rows, c: max(float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == c)  # noqa: E731
+    copy_bytes = copy_mib << 20
+    f_fetch = copy_bytes / (big(copy_rows_f, "FETCH_SIZE") * 1024)
+    f_write = copy_bytes / (big(copy_rows_w, "WRITE_SIZE") * 1024)
+    import workloads as W
+    spec = W.CONFIGS[workload]
+    alg = W.algorithmic_decode_bytes(W.draw_context_lens(spec), spec.num_q_heads,
+                                     spec.num_kv_heads, spec.head_dim, spec.block_size)
+    hbm = fetch * 1024 * f_fetch + write * 1024 * f_write
+    rec = {"kernel": "decode_split_kernel", "workload": spec.name,
+           "fetch_size_kib_per_dispatch": fetch, "write_size_kib_per_dispatch": write,
+           "copy_calibration_bytes": copy_bytes, "fetch_scale": round(f_fetch, 4),
+           "write_scale": round(f_write, 4), "hbm_bytes_per_launch": int(hbm),
+           "algorithmic_bytes_per_launch": alg, "ratio_to_algorithmic": round(hbm / alg, 4),
+           "kernel_source_sha256_16": kernel_source_hash(),
+           "commands": [command_kernel.replace("PMC", "FETCH_SIZE"),
+                        command_kernel.replace("PMC", "WRITE_SIZE"),
+                        command_copy.replace("PMC", "FETCH_SIZE"),
+                        command_copy.replace("PMC", "WRITE_SIZE")]}
+    base = os.path.join(PROFILES, f"decode_split_{workload}_hbm_counters")
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+    with open(base + ".md", "w") as f:
+        f.write(f"# HBM traffic of decode_split_kernel, {spec.name}\n\n"
+                f"Counters per dispatch (median over the launches), each pass its own run:\n\n"
+                + "".join(f"    {c}\n" for c in rec["commands"]) +
+                f"\n| quantity | value |\n|---|---|\n"
+                f"| FETCH_SIZE (KiB/dispatch, raw) | {fetch:.1f} |\n"
+                f"| WRITE_SIZE (KiB/dispatch, raw) | {write:.1f} |\n"
+                f"| plain copy of {copy_mib} MiB: bytes / (FETCH_SIZE x 1024) | {f_fetch:.3f} |\n"
+                f"| plain copy of {copy_mib} MiB: bytes / (WRITE_SIZE x 1024) | {f_write:.3f} |\n"
+                f"| HBM bytes per launch (scaled) | {int(hbm)} |\n"
+                f"| algorithmic bytes per launch | {alg} |\n"
+                f"| ratio | {hbm / alg:.3f} |\n"
+                f"| kernel sources sha256[:16] | {rec['kernel_source_sha256_16']} |\n")
+    print(base + ".json")
 
 
 def load_traffic(workload: str):
@@ -305,6 +566,13 @@ def main(argv=None):
               "sharding of this path is a design note, not a measured configuration.",
               file=sys.stderr)
         sys.exit(2)
+    if args.ingest_trace:
+        ingest_trace(*args.ingest_trace)
+        return
+    if args.ingest_counters:
+        a = args.ingest_counters
+        ingest_counters(a[0], a[1], a[2], a[3], int(a[4]), args.workload, a[5], a[6])
+        return
     import torch
     import workloads as W
 
@@ -351,12 +619,20 @@ def main(argv=None):
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         del wl
         torch.cuda.empty_cache()
-        wl, rec = measure(name, args, min(args.steps, 100), min(args.warmup, 10))
+        if name in ("c5p", "c5mix"):
+            wl, rec = measure_prefill(args, min(args.steps, 50), min(args.warmup, 5),
+                                      with_decode=(name == "c5mix"))
+            msg = f"prefill {rec['prefill_us']:.2f} us ({rec['prefill_tflops']:.0f} TFLOP/s)"
+            if name == "c5mix":
+                msg += (f"; mixed step {rec['us_per_step']:.2f} us (append {rec['append_us']:.2f}, "
+                        f"decode {rec['decode_us']:.2f})")
+        else:
+            wl, rec = measure(name, args, min(args.steps, 100), min(args.warmup, 10))
+            msg = (f"{rec['us_per_call']:.2f} us/step, {rec['gbps']:.1f} GB/s; "
+                   f"kernel {rec['kernel_avg_us']:.2f} us ({rec['kernel_gbps']:.0f} GB/s)")
         others[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rec.items()
                         if k not in ("wall_s",)}
-        print(f"[bench] {name}: {rec['us_per_call']:.2f} us/step, {rec['gbps']:.1f} GB/s; "
-              f"kernel {rec['kernel_avg_us']:.2f} us ({rec['kernel_gbps']:.0f} GB/s)",
-              file=sys.stderr, flush=True)
+        print(f"[bench] {name}: {msg}", file=sys.stderr, flush=True)
 
     spec = W.CONFIGS[args.workload]
     achieved = main_rec["kernel_gbps"]
