@@ -597,6 +597,20 @@ def main(argv=None):
     if args.sweep_splits:
         res = {}
         for name in [args.workload] + [x for x in args.others.split(",") if x]:
+            if name == "c5p":
+                wl = PrefillWorkload(W.PREFILL_CONFIGS["c5p"], None, args.rotate_gib)
+                res[name] = {"auto": wl.S}
+                for S in [int(x) for x in args.sweep_splits.split(",")]:
+                    wl.S = S
+                    n = wl.pa.prefill_workspace_size(1, wl.max_q, wl.q.shape[1], wl.q.shape[2], S)
+                    wl.ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=wl.dev)
+                    ms = time_graph(wl.prefill, wl.R, min(args.steps, 50), 3)
+                    res[name][S] = round(ms * 1e3, 2)
+                    print(f"[sweep] {name} S={S}: {ms * 1e3:.2f} us ({wl.flop / ms / 1e9:.0f} "
+                          f"TFLOP/s)", file=sys.stderr, flush=True)
+                del wl
+                torch.cuda.empty_cache()
+                continue
             wl = DecodeWorkload(W.CONFIGS[name], args.rotate_gib, args.splits)
             auto = wl.S
             res[name] = {"auto": auto}

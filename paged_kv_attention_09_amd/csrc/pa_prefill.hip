@@ -11,8 +11,8 @@
 //    tile staged in LDS serves all G heads.  Long key ranges are cut into
 //    pieces handled by separate workgroups (the same split-KV scheme as
 //    decode) and merged by log-sum-exp afterwards.
-//  * Key tiles of 64 rows stream into LDS by global_load_lds_dwordx4,
-//    double buffered.  K rows are stored with their 16-byte chunks XOR
+//  * Key tiles of 64 rows stream into LDS by global_load_lds_dwordx4, three
+//    stages deep (two tiles in flight while one is computed).  K rows are stored with their 16-byte chunks XOR
 //    swizzled by row, V rows with their 32-byte column pairs swizzled, so the
 //    reads below hit distinct banks.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K fragments (keys x head_dim)
@@ -28,7 +28,9 @@
 //  * Online softmax in the exp2 domain with a lazily moved running max (one
 //    ballot per tile; exact max and rescale only when a score exceeds the
 //    max by 2^8).  Masks (causal diagonal, piece end) are applied only on
-//    tiles that cross them.
+//    tiles that cross them; elsewhere the scale folds into one fma per
+//    weight.  The row sums of P come from the matrix core too (a block of
+//    ones times P^T), not from per-element adds.
 #include "pa_device.hpp"
 #include "pa_kernels.hpp"
 
@@ -47,6 +49,14 @@ constexpr float kSlackP = 8.f;
 __device__ __forceinline__ f32x4 mfma16(const uint4 &a, const uint4 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// v_max3_f32 without the input canonicalisation the compiler adds for fmaxf
+// in IEEE mode (inputs here are matrix-core results, never signalling NaNs).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 __device__ __forceinline__ uint2 read_tr(const char *p) {
@@ -82,7 +92,14 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   using Lay = PrefillLayout<D>;
   constexpr int ROWB = Lay::ROWB, TILEB = Lay::TILEB, NDMA = Lay::NDMA, KS = Lay::KSTEPS;
   constexpr int DB = Lay::DBLK, RPD = Lay::ROWS_PER_DMA, NCH = Lay::NCH;
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILEB];  // [buffer][K, V]
+  // Three tile buffers: two tiles in flight while one is computed.  The DMAs
+  // of a tile are issued by NI waves (a power of two), NPW instructions each,
+  // so every issuing wave waits on a fixed count.
+  constexpr int NST = 3;
+  constexpr int NI = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
+  constexpr int NPW = 2 * NDMA / NI;
+  static_assert(NPW <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[NST][2][TILEB];  // [stage][K, V]
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // q head within the group
@@ -120,90 +137,179 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // Tile DMA: the 2 * NDMA instructions of a tile are spread over the waves.
-  auto issue_tile = [&](int kt0, int buf) {
-    for (int j = w; j < 2 * NDMA; j += G) {
+  // Block ids of the four 16-key groups of the tile starting at kt0 (one
+  // block for block_size 256), clamped into the table.  Loaded one tile ahead
+  // of their use so the scalar-load latency hides behind a tile of compute.
+  const int Wm1 = a.max_blocks_per_seq - 1;
+  auto tile_blocks = [&](int kt0, int (&blk)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) blk[q] = table[min((kt0 + 16 * q) >> bs_shift, Wm1)];
+  };
+
+  // Tile DMA: the 2 * NDMA instructions of a tile are issued by NI waves,
+  // NPW each.  Instruction jj of a tensor fills tile rows jj*RPD .. +RPD,
+  // all inside the tile's 16-row group (jj*RPD) / 16, whose start row sits at
+  // a scalar base; the per-lane part of the address is fixed for the launch.
+  // Rows past the piece end re-read a valid row of the tile, so masked keys
+  // only ever see finite data.
+  uint32_t dma_voff[NPW];
+#pragma unroll
+  for (int jw = 0; jw < NPW; ++jw) {
+    const int j = w + jw * NI;
+    const bool is_v = j >= NDMA;
+    const int jj = is_v ? j - NDMA : j;
+    const int row_in = jj * RPD + lane / NCH;
+    const int p = lane % NCH;
+    const int c = is_v ? v_pos<D>(p, row_in) : k_pos<D>(p, row_in);
+    dma_voff[jw] = (uint32_t)(row_in & 15) * RS + (uint32_t)c * 16;
+  }
+  auto issue_tile = [&](int kt0, int buf, const int (&blk)[4]) {
+    if (w >= NI) return;
+    const char *gk[4], *gv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int kg = kt0 + 16 * q;
+      const size_t row0 = ((size_t)(uint32_t)blk[q] << bs_shift) + (size_t)(kg & bs_mask);
+      gk[q] = kbase + row0 * RS;
+      gv[q] = vbase + row0 * RS;
+    }
+    const bool edge_tile = kt0 + kKeys > kend;
+#pragma unroll
+    for (int jw = 0; jw < NPW; ++jw) {
+      const int j = w + jw * NI;
       const bool is_v = j >= NDMA;
       const int jj = is_v ? j - NDMA : j;
-      const int rfirst = kt0 + jj * RPD;                 // first key of this instruction
-      const int row_in = jj * RPD + lane / NCH;          // tile row this lane fills
-      const int p = lane % NCH;                          // stored 16-byte position
-      const int c = is_v ? v_pos<D>(p, row_in) : k_pos<D>(p, row_in);
-      int key = kt0 + row_in, kfirst = rfirst;
-      if (rfirst >= kend) kfirst = kt0;                  // whole instruction past the end:
-      if (key >= kend) key = kfirst;                     // re-read a valid row (finite data)
-      const size_t row0 = ((size_t)(uint32_t)table[kfirst >> bs_shift] << bs_shift) +
-                          (size_t)(kfirst & bs_mask);
-      const uint32_t voff = (uint32_t)(key - kfirst) * RS + (uint32_t)c * 16;
-      const char *base = (is_v ? vbase : kbase) + row0 * RS;
+      const int grp = (jj * RPD) >> 4;
+      const char *base = is_v ? gv[grp] : gk[grp];
+      uint32_t voff = dma_voff[jw];
+      if (edge_tile) {
+        const int row_in = jj * RPD + lane / NCH;
+        if (kt0 + jj * RPD >= kend) {
+          base = is_v ? gv[0] : gk[0];               // whole instruction past the end:
+          voff = voff - (uint32_t)(row_in & 15) * RS; // re-read tile row 0
+        } else if (kt0 + row_in >= kend) {
+          voff = voff - (uint32_t)(row_in & 15) * RS + (uint32_t)((jj * RPD) & 15) * RS;
+        }
+      }
       dma16(lds_offset(&smem[buf][is_v][jj * 1024]), base, voff);
     }
   };
 
   const int ntiles = (kend - kbeg + kKeys - 1) / kKeys;
-  issue_tile(kbeg, 0);
+  int blk_a[4], blk_b[4];
+  tile_blocks(kbeg, blk_a);
+  issue_tile(kbeg, 0, blk_a);
+  if (ntiles > 1) {
+    tile_blocks(kbeg + kKeys, blk_b);
+    issue_tile(kbeg + kKeys, 1, blk_b);
+  }
+  if (ntiles > 2) tile_blocks(kbeg + 2 * kKeys, blk_a);   // for tile 2
 
   float m[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
   f32x4 o[DB][2];
+  f32x4 ol[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};  // row sums (all 4 equal)
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db][0] = o[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint4 kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
+
+  // Per-lane LDS offsets, fixed for the launch.  K fragment (key block mb,
+  // step ks): row 16 mb + c16, chunk 4 ks + q4, stored at chunk ^ (row & 15)
+  // = chunk ^ c16; the key block adds 16 rows.  V^T fragment (head_dim block
+  // db, key step kk): source row 4 q4 + c16 / 4 (+ 32 kk, + 16 for the upper
+  // half), columns 16 db + 4 (c16 % 4) in the 32-byte pair db ^ (row & 7).
+  int k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = c16 * ROWB + k_pos<D>(ks * 4 + q4, c16) * 16;
+  const int tr_row = 4 * q4 + (c16 >> 2);
+  int v_off[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    v_off[db] = tr_row * ROWB + v_pos<D>(2 * db + ((c16 & 3) >> 1), tr_row) * 16 + (c16 & 1) * 8;
 
   for (int it = 0; it < ntiles; ++it) {
-    wait_vmcnt<0>();
+    // this wave's DMAs of tile it are done when at most those of tile it+1
+    // are outstanding; the barrier then publishes everyone's tile it and
+    // retires all reads of the stage tile it+2 is about to overwrite.
+    if (it + 1 < ntiles)
+      wait_vmcnt<NPW>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
     const int kt0 = kbeg + it * kKeys;
-    if (it + 1 < ntiles) issue_tile(kt0 + kKeys, (it + 1) & 1);
-    const char *Kt = smem[it & 1][0];
-    const char *Vt = smem[it & 1][1];
+    if (it + 2 < ntiles) {
+      issue_tile(kt0 + 2 * kKeys, (it + 2) % NST, blk_a);
+      if (it + 3 < ntiles) tile_blocks(kt0 + 3 * kKeys, blk_a);   // consumed next iteration
+    }
+    const char *Kt = smem[it % NST][0];
+    const char *Vt = smem[it % NST][1];
 
-    // ---- S^T = K Q^T: 4 key blocks x 2 row blocks ----
+    // ---- S^T = K Q^T: 4 key blocks x 2 row blocks, 8 independent chains ----
     f32x4 s[4][2];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      s[mb][0] = s[mb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r = mb * 16 + c16;
+      const uint4 kf = *(const uint4 *)(Kt + k_off[0] + mb * 16 * ROWB);
+      s[mb][0] = mfma16(kf, qf[0][0], zero4);
+      s[mb][1] = mfma16(kf, qf[1][0], zero4);
+    }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kf = *(const uint4 *)(Kt + r * ROWB + k_pos<D>(ks * 4 + q4, r) * 16);
+    for (int ks = 1; ks < KS; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const uint4 kf = *(const uint4 *)(Kt + k_off[ks] + mb * 16 * ROWB);
         s[mb][0] = mfma16(kf, qf[0][ks], s[mb][0]);
         s[mb][1] = mfma16(kf, qf[1][ks], s[mb][1]);
       }
     }
 
-    // ---- scale, masks, lazily rescaled online softmax ----
-    // lane holds S^T[key = kt0 + 16 mb + 4 q4 + e][row = 16 nb + c16]
+    // ---- online softmax, exp2 domain, lazily moved max ----
+    // lane holds S^T[key = kt0 + 16 mb + 4 q4 + e][row = 16 nb + c16].
+    // Interior tiles (no mask) with a positive scale keep the raw scores and
+    // fold the scale into one fma per weight; edge tiles (causal diagonal or
+    // piece end) scale and mask explicitly.
     const bool edge = (kt0 + kKeys > kend) || (kt0 + kKeys - 1 > pos0);
-    bool grow = false;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int prow = pos0 + nb * 16 + c16;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = s[mb][nb][e] * a.scale_log2;
-          if (edge) {
-            const int key = kt0 + mb * 16 + q4 * 4 + e;
-            x = (key < kend && key <= prow) ? x : -INFINITY;
-          }
-          s[mb][nb][e] = x;
-          grow |= x > m[nb] + kSlackP;
-        }
-    }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const bool plain = !edge && a.scale_log2 > 0.f;
+    float mxs[2];
+    if (plain) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        float mx = m[nb];
+        float t = max3(s[0][nb][0], s[0][nb][1], s[0][nb][2]);
+        t = max3(t, s[0][nb][3], s[1][nb][0]);
+        t = max3(t, s[1][nb][1], s[1][nb][2]);
+        t = max3(t, s[1][nb][3], s[2][nb][0]);
+        t = max3(t, s[2][nb][1], s[2][nb][2]);
+        t = max3(t, s[2][nb][3], s[3][nb][0]);
+        t = max3(t, s[3][nb][1], s[3][nb][2]);
+        t = max3(t, s[3][nb][3], t);
+        mxs[nb] = t * a.scale_log2;
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int prow = pos0 + nb * 16 + c16;
+        float t = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[mb][nb][e]);
+          for (int e = 0; e < 4; ++e) {
+            const int key = kt0 + mb * 16 + q4 * 4 + e;
+            const float x = (key < kend && key <= prow) ? s[mb][nb][e] * a.scale_log2 : -INFINITY;
+            s[mb][nb][e] = x;
+            t = fmaxf(t, x);
+          }
+        mxs[nb] = t;
+      }
+    }
+    const bool grow = (mxs[0] > m[0] + kSlackP) || (mxs[1] > m[1] + kSlackP);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float mx = fmaxf(m[nb], mxs[nb]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float alpha = mx == -INFINITY ? 1.f : exp2_fast(m[nb] - mx);
         m[nb] = mx;
-        lsum[nb] *= alpha;
+        ol[nb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db][nb] *= alpha;
       }
@@ -214,49 +320,41 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const float mm = m[nb] == -INFINITY ? 0.f : m[nb];
+      const float c = plain ? a.scale_log2 : 1.f;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         uint32_t pk[4];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const f32x4 sv = s[2 * kk + half][nb];
-          pk[2 * half] = pack_bf16(exp2_fast(sv[0] - mm), exp2_fast(sv[1] - mm));
-          pk[2 * half + 1] = pack_bf16(exp2_fast(sv[2] - mm), exp2_fast(sv[3] - mm));
+          pk[2 * half] = pack_bf16(exp2_fast(fmaf(sv[0], c, -mm)), exp2_fast(fmaf(sv[1], c, -mm)));
+          pk[2 * half + 1] = pack_bf16(exp2_fast(fmaf(sv[2], c, -mm)), exp2_fast(fmaf(sv[3], c, -mm)));
         }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) lsum[nb] += bf16_lo(pk[t]) + bf16_hi(pk[t]);
         pf[nb][kk] = uint4{pk[0], pk[1], pk[2], pk[3]};
       }
     }
 
-    // ---- O^T += V^T P^T: head_dim blocks x 2 row blocks x 2 key steps ----
-    // V^T fragment lane (q4, c16): V[16 kb + 4 q4 + j][16 db + c16], j = 0..3,
-    // for kb = 2 kk and 2 kk + 1, via transposing reads: source lane s of the
-    // 16-lane group addresses row 4 q4 + s / 4, columns 16 db + 4 (s % 4).
-    const int tr_row = 4 * q4 + (c16 >> 2);
-    const int tr_col_chunk_lo = (c16 & 3) >> 1;   // which 16-byte half of the 32-byte pair
-    const int tr_byte = (c16 & 1) * 8;
+    // ---- O^T += V^T P^T, and the row sums l += ones P^T on the same unit ----
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int r0 = 32 * kk + tr_row, r1 = r0 + 16;
-        const int c = 2 * db + tr_col_chunk_lo;
-        const uint2 lo = read_tr(Vt + r0 * ROWB + v_pos<D>(c, r0) * 16 + tr_byte);
-        const uint2 hi = read_tr(Vt + r1 * ROWB + v_pos<D>(c, r1) * 16 + tr_byte);
+      for (int db = 0; db < DB; ++db) {
+        const char *vp = Vt + v_off[db] + kk * 32 * ROWB;
+        const uint2 lo = read_tr(vp);
+        const uint2 hi = read_tr(vp + 16 * ROWB);
         const uint4 vf = uint4{lo.x, lo.y, hi.x, hi.y};
         o[db][0] = mfma16(vf, pf[0][kk], o[db][0]);
         o[db][1] = mfma16(vf, pf[1][kk], o[db][1]);
       }
+      ol[0] = mfma16(kOnes, pf[0][kk], ol[0]);
+      ol[1] = mfma16(kOnes, pf[1][kk], ol[1]);
     }
   }
 
   // ---- normalise and write: lane holds O^T[d = 16 db + 4 q4 + e][row = 16 nb + c16] ----
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    float l = lsum[nb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = ol[nb][0];
     const int i = i0 + nb * 16 + c16;
     if (i >= n) continue;
     const size_t row = (size_t)(q0 + i) * Hq + h;
@@ -282,13 +380,21 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-// Merge the key pieces of one (query row, q head): row t of sequence b sits
+// Merge the key pieces of (query row, q head) rows: row t of sequence b sits
 // at position p = L_b - n_b + (t - cu[b]) and has floor(p / split_len) + 1
-// non-empty pieces.  One 64-lane wave per output row.
+// non-empty pieces.  One wave per row, four rows per workgroup; a row's
+// weights 2^(lse_s - M) go through LDS and all its piece loads are in flight
+// together.
 template <int D>
-__global__ __launch_bounds__(64) void prefill_merge_kernel(PrefillArgs a) {
-  const int h = blockIdx.x, t = blockIdx.y;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int rows_bound) {
+  constexpr int PER = D / 64;      // columns per lane
+  constexpr int BATCH = 8;
+  __shared__ float w_l[4][256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = blockIdx.x * 4 + wv;
+  if (r >= rows_bound) return;
+  const int Hq = a.num_q_heads;
+  const int t = r / Hq;
   const auto *cu = as_const(a.cu_seqlens_q);
   if (t >= cu[a.num_seqs]) return;   // the grid covers num_seqs * max_q_len rows
   int b = 0;
@@ -297,26 +403,55 @@ __global__ __launch_bounds__(64) void prefill_merge_kernel(PrefillArgs a) {
   const int p = as_const(a.context_lens)[b] - n + (t - cu[b]);
   const int S = a.num_splits;
   const int ns = min(S, p / a.split_len + 1);
-  const size_t row = (size_t)t * a.num_q_heads + h;
-  const float *lse = a.lse_part + row * S;
-  constexpr int PER = D / 64;
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, lse[s]);
-  M = wave_max(M);
-  float den = 0.f, acc[PER];
+  const float *lse = a.lse_part + (size_t)r * S;
+  const float *op = a.o_part + (size_t)r * S * D + lane * PER;
+
+  float ov[BATCH][PER];
+#pragma unroll
+  for (int k = 0; k < BATCH; ++k)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) ov[k][e] = k < ns ? op[(size_t)k * D + e] : 0.f;
+  float x[4], mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int s = lane + 64 * k;
+    x[k] = s < ns ? lse[s] : -INFINITY;
+    mx = fmaxf(mx, x[k]);
+  }
+  const float M = wave_max(mx);
+  float den = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int s = lane + 64 * k;
+    const float wgt = s < ns ? exp2_fast(x[k] - M) : 0.f;
+    w_l[wv][s] = wgt;
+    den += wgt;
+  }
+  den = wave_sum(den);
+  float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  const float *op = a.o_part + row * (size_t)S * D + lane * PER;
-  for (int s = 0; s < ns; ++s) {
-    const float wgt = exp2_fast(lse[s] - M);
-    den += wgt;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += wgt * op[(size_t)s * D + e];
+  for (int k = 0; k < BATCH; ++k)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += w_l[wv][k] * ov[k][e];
+  for (int s0 = BATCH; s0 < ns; s0 += BATCH) {
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) ov[k][e] = s0 + k < ns ? op[(size_t)(s0 + k) * D + e] : 0.f;
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += w_l[wv][min(s0 + k, 255)] * ov[k][e];
   }
   const float inv = 1.f / den;
-  uint16_t *out = a.out + row * D + lane * PER;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) out[e] = (uint16_t)pack_bf16(acc[e] * inv, 0.f);
+  uint16_t *out = a.out + (size_t)r * D + lane * PER;
+  if constexpr (PER == 2) {
+    *(uint32_t *)out = pack_bf16(acc[0] * inv, acc[1] * inv);
+  } else {
+    out[0] = (uint16_t)pack_bf16(acc[0] * inv, 0.f);
+  }
 }
 
 template <int D, int G>
@@ -351,11 +486,12 @@ hipError_t launch_prefill(const PrefillArgs &a, int head_dim, int group, hipStre
 
 hipError_t launch_prefill_merge(const PrefillArgs &a, int head_dim, int total_q,
                                 hipStream_t stream) {
-  dim3 grid(a.num_q_heads, total_q);
+  const int rows = total_q * a.num_q_heads;
+  dim3 grid((rows + 3) / 4);
   if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, dim3(256), 0, stream, a, rows);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_merge_kernel<64>, grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(prefill_merge_kernel<64>, grid, dim3(256), 0, stream, a, rows);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
