@@ -16,20 +16,23 @@
 //  * K and V rows of a chunk (16 x head_dim bf16 each) stream HBM -> LDS with
 //    global_load_lds_dwordx4 (16 bytes per lane, no VGPRs held in flight),
 //    NSTAGE chunks deep per wave.  The 16-byte positions of each row are
-//    XOR-swizzled by row so both read patterns below are bank-conflict free.
-//  * Scores: 4 lanes per token, each lane dots a quarter of the row against
-//    the G query rows of the group with v_dot2c_f32_bf16 (q kept in VGPRs as
-//    bf16 pairs), then a 2-step DPP quad sum.  This reads K once for all G
-//    heads sharing the kv head.
-//  * Online softmax per head in the exp2 domain: the chunk max over the 16
-//    tokens (DPP row rotations + 4 readlanes) updates the running max m; the
-//    weights exp2(x - m) are rounded to bf16 and parked in LDS.
-//  * P.V: every lane owns 2 of the head_dim columns (1 for head_dim 64,
-//    with two token halves) and walks the chunk's tokens in pairs: two bf16
-//    V values of adjacent tokens are paired with a byte permute and one
-//    v_dot2c per head accumulates both tokens into fp32.
-//  * The 4 waves' (m, l, acc) are merged through LDS; the workgroup writes
-//    either the final bf16 row (one piece) or an fp32 partial plus its
+//    XOR-swizzled by a rotation of the row index, so both LDS read patterns
+//    below touch every bank once.
+//  * The G q heads that share the kv head are the 16 columns of one matrix
+//    tile (columns G..15 are zero).  Scores S^T = K Q^T come from
+//    v_mfma_f32_16x16x32_bf16 (K rows from LDS, Q^T held in registers), which
+//    leaves lane l with head l % 16 and tokens 4 (l / 16) + i of the chunk.
+//  * Online softmax per head in the exp2 domain with a lazily moved running
+//    max: the max moves (exact cross-lane max and rescale) only when a score
+//    exceeds it by more than kSlack; a wave ballot decides.  The weights are
+//    rounded to bf16 in place, and in place they are exactly the B operand
+//    of the second product.
+//  * O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, with V^T fragments taken
+//    from the row-major V chunk by ds_read_b64_tr_b16.  Per-head statistics
+//    and the output column of a head live in the same lanes, so a rescale
+//    is lane-local.
+//  * The 4 waves' (m, l, O) are merged through LDS; the workgroup writes
+//    either the final bf16 rows (one piece) or fp32 partials plus their
 //    base-2 log-sum-exp for the combine kernel.
 //  * Tokens past the piece end are masked to -inf before the max; their DMA
 //    lanes re-read the chunk's first row, so every load stays inside blocks
@@ -45,9 +48,17 @@ constexpr int kWaves = 4;
 constexpr int kChunk = 16;     // tokens per wave step
 constexpr float kSlack = 8.f;  // log2 headroom before the running max moves
 
+// LDS position of 16-byte chunk c of row r is c ^ row_swizzle(r): a rotation
+// of the row index over the position bits (for head_dim 64 two rows share a
+// 256-byte bank line, so the row pair index is rotated).
 template <int D>
 __device__ __forceinline__ int row_swizzle(int r) {
-  return (r * 4) & (D / 8 - 1);
+  if constexpr (D == 128) {
+    return ((r << 1) | (r >> 3)) & 15;
+  } else {
+    const int s = r >> 1;
+    return ((s << 1) | (s >> 2)) & 7;
+  }
 }
 
 template <int D, int G, int NSTAGE>
@@ -59,20 +70,21 @@ struct DecodeLayout {
   static constexpr int STB = 2 * CHB;                // one stage: K chunk then V chunk
   static constexpr int QB = ((G * ROWB + 1023) / 1024) * 1024;
   static constexpr int NQDMA = QB / 1024;
-  static constexpr int PB = ((G * kChunk * 2 + 15) / 16) * 16;  // bf16 weights of a chunk
-  static constexpr int WAVE_LDS = NSTAGE * STB + QB + PB;
-  static constexpr int KPL = NPOS / 4;               // 16-byte K pieces per lane per token
-  static constexpr int HALVES = 128 / D;             // token halves in the P.V layout
-  static constexpr int PAIRS = kChunk / 2 / HALVES;  // token pairs per lane per chunk
+  static constexpr int WAVE_LDS = NSTAGE * STB + QB;
+  static constexpr int KS = D / 32;                  // 16x16x32 steps over head_dim
+  static constexpr int DB = D / 16;                  // 16-column blocks of head_dim
+  // merge scratch (fp32): m[G], l[G], then O rows of MS floats from ACC0
+  static constexpr int ACC0 = (2 * G + 3) & ~3;
+  static constexpr int MS = D + 4;
   static_assert(WAVE_LDS % 16 == 0, "alignment");
-  static_assert(2 * G + G * D <= (NSTAGE * STB) / 4, "merge scratch fits in the stages");
+  static_assert((ACC0 + G * MS) * 4 <= NSTAGE * STB, "merge scratch fits in the stages");
 };
 
 template <int D, int G, int NSTAGE>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   using Lay = DecodeLayout<D, G, NSTAGE>;
   constexpr int ROWB = Lay::ROWB, NPOS = Lay::NPOS, CHB = Lay::CHB, NDMA = Lay::NDMA;
-  constexpr int STB = Lay::STB, KPL = Lay::KPL, PAIRS = Lay::PAIRS;
+  constexpr int STB = Lay::STB, KS = Lay::KS, DB = Lay::DB, ACC0 = Lay::ACC0, MS = Lay::MS;
   __shared__ __attribute__((aligned(1024))) char smem[kWaves * Lay::WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
@@ -115,7 +127,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 
   char *my = smem + wave * Lay::WAVE_LDS;
   char *qlds = my + NSTAGE * STB;
-  char *plds = qlds + Lay::QB;
   const uint32_t my_off = lds_offset(my);
   const uint32_t q_off = lds_offset(qlds);
 
@@ -173,13 +184,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  float m[G], l_lane[G], acc[G][2];
+  // Lane roles in the matrix tiles: column hh = the q head, qd = the group
+  // of 4 tokens (scores) or of 4 head_dim entries (output).
+  const int hh = lane & 15, qd = lane >> 4;
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[DB];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l_lane[h] = 0.f;
-    acc[h][0] = acc[h][1] = 0.f;
-  }
+  for (int d = 0; d < DB; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (n_my > 0) {
     // q rows of the group -> LDS (clamped lanes re-read the last 16 bytes).
@@ -187,102 +198,81 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
       const char *qsrc = (const char *)a.q + head0 * ROWB;
 #pragma unroll
       for (int j = 0; j < Lay::NQDMA; ++j) {
-        uint32_t o = (uint32_t)(j * 1024 + lane * 16);
-        o = o < (uint32_t)(G * ROWB) ? o : (uint32_t)(G * ROWB - 16);
-        dma16(q_off + j * 1024, qsrc, o);
+        uint32_t off = (uint32_t)(j * 1024 + lane * 16);
+        off = off < (uint32_t)(G * ROWB) ? off : (uint32_t)(G * ROWB - 16);
+        dma16(q_off + j * 1024, qsrc, off);
       }
     }
 #pragma unroll
     for (int s = 0; s < NSTAGE; ++s)
       if (s < n_my) issue_chunk(wave + kWaves * s, s, blk_first[s]);
 
-    const int r = lane >> 2, u = lane & 3;
-    const int swr = row_swizzle<D>(r);
-    // P.V lane geometry
-    const int half = (D == 128) ? 0 : (lane >> 5);
-    const int dl = (D == 128) ? lane : (lane & 31);
-    const uint32_t v_in_chunk = (uint32_t)(dl & 3) * 4;
-    const int v_c = dl >> 2;
+    // LDS read offsets: K fragment kk of this lane is row hh, head_dim
+    // 32 kk + 8 qd .. + 7; V^T fragment db is 8 bytes of row 4 qd + hh / 4 at
+    // head_dim 16 db + 4 (hh % 4).
+    uint32_t k_off[KS], v_off[DB];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      k_off[kk] = (uint32_t)(hh * ROWB + (((4 * kk + qd) ^ row_swizzle<D>(hh)) * 16));
+    {
+      const int vr = 4 * qd + (hh >> 2);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        v_off[db] = (uint32_t)(CHB + vr * ROWB +
+                               (((2 * db + ((hh & 3) >> 1)) ^ row_swizzle<D>(vr)) * 16) +
+                               (hh & 1) * 8);
+    }
 
-    uint4 qreg[G][KPL];
+    uint4 qf[KS];
     for (int i = 0; i < n_my; ++i) {
       wait_vmcnt_steps<2 * NDMA, NSTAGE - 1>(min(NSTAGE - 1, n_my - 1 - i));
       if (i == 0) {
+        // Q^T fragments: head hh (zero for hh >= G), head_dim 32 kk + 8 qd ...
+        const char *qrow = qlds + min(hh, G - 1) * ROWB + qd * 16;
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int k = 0; k < KPL; ++k)
-            qreg[h][k] = *(const uint4 *)(qlds + h * ROWB + (u + 4 * k) * 16);
+        for (int kk = 0; kk < KS; ++kk) {
+          const uint4 v = *(const uint4 *)(qrow + kk * 64);
+          qf[kk] = hh < G ? v : uint4{0u, 0u, 0u, 0u};
+        }
       }
       const int ci = wave + kWaves * i;
       const int tc = t0 + ci * kChunk;
       const char *st = my + (i % NSTAGE) * STB;
 
-      // ---- scores for the G heads, 4 lanes per token ----
-      float s[G];
+      // ---- S^T = K Q^T: lane holds head hh, tokens 4 qd + e ----
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = 0.f;
-#pragma unroll
-      for (int k = 0; k < KPL; ++k) {
-        const int p = (u + 4 * k) ^ swr;
-        const uint4 kv = *(const uint4 *)(st + r * ROWB + p * 16);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          s[h] = dot2(qreg[h][k].x, kv.x, s[h]);
-          s[h] = dot2(qreg[h][k].y, kv.y, s[h]);
-          s[h] = dot2(qreg[h][k].z, kv.z, s[h]);
-          s[h] = dot2(qreg[h][k].w, kv.w, s[h]);
-        }
-      }
+      for (int kk = 0; kk < KS; ++kk) sc = mfma_k32(*(const uint4 *)(st + k_off[kk]), qf[kk], sc);
+
       // ---- online softmax, exp2 domain, lazily rescaled ----
       // The running max m only moves when some score of the chunk exceeds it
       // by more than kSlack (one wave ballot decides); otherwise the weights
-      // exp2(x - m) <= 2^kSlack stay well inside fp32/bf16 range and no
-      // cross-lane max or rescale is needed.  The result is the same up to
-      // rounding: numerator and denominator share the factor 2^-m.
-      const bool valid = tc + r < t1;
-      float x[G];
-      bool grow = false;
+      // exp2(x - m) <= 2^kSlack stay well inside fp32/bf16 range.  The result
+      // is the same up to rounding: numerator and denominator share 2^-m.
+      const int tok = tc + 4 * qd;
+      float x[4];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        x[h] = valid ? quad_sum(s[h]) * a.scale_log2 : -INFINITY;
-        grow |= x[h] > m[h] + kSlack;
-      }
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      for (int e = 0; e < 4; ++e) x[e] = tok + e < t1 ? sc[e] * a.scale_log2 : -INFINITY;
+      const float cmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__builtin_amdgcn_ballot_w64(hh < G && cmax > m + kSlack) != 0) {
+        float mx = fmaxf(m, cmax);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float alpha = mx == -INFINITY ? 1.f : exp2_fast(m - mx);
+        m = mx;
+        lsum *= alpha;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float m_new = fmaxf(m[h], max_over_quads(x[h]));
-          const float alpha = exp2_fast(m[h] - m_new);
-          m[h] = m_new;
-          l_lane[h] *= alpha;
-          acc[h][0] *= alpha;
-          acc[h][1] *= alpha;
-        }
+        for (int d = 0; d < DB; ++d) o[d] *= alpha;
       }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint32_t pk = pack_bf16(exp2_fast(x[h] - m[h]), 0.f);
-        l_lane[h] += bf16_lo(pk);
-        // the 4 lanes of a token hold the same weight and all store it
-        *(u16_alias *)(plds + h * (kChunk * 2) + r * 2) = (uint16_t)pk;
-      }
+      const float mm = m == -INFINITY ? 0.f : m;
+      const uint32_t p01 = pack_bf16(exp2_fast(x[0] - mm), exp2_fast(x[1] - mm));
+      const uint32_t p23 = pack_bf16(exp2_fast(x[2] - mm), exp2_fast(x[3] - mm));
+      lsum += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+      const uint2 pb = {p01, p23};
 
-      // ---- P.V: lanes own head_dim columns, tokens in pairs ----
-      const char *vst = st + CHB;
+      // ---- O^T += V^T P^T: lane holds head hh, head_dim 16 db + 4 qd + i ----
 #pragma unroll
-      for (int jj = 0; jj < PAIRS; ++jj) {
-        const int j = half * PAIRS + jj;
-        const int ta = 2 * j, tb = 2 * j + 1;
-        const uint32_t va = *(const uint32_t *)(vst + ta * ROWB + ((v_c ^ row_swizzle<D>(ta)) * 16) + v_in_chunk);
-        const uint32_t vb = *(const uint32_t *)(vst + tb * ROWB + ((v_c ^ row_swizzle<D>(tb)) * 16) + v_in_chunk);
-        const uint32_t lo = lo_pair(va, vb), hi = hi_pair(va, vb);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const uint32_t pp = *(const u32_alias *)(plds + h * (kChunk * 2) + j * 4);
-          acc[h][0] = dot2(pp, lo, acc[h][0]);
-          acc[h][1] = dot2(pp, hi, acc[h][1]);
-        }
-      }
+      for (int db = 0; db < DB; ++db) o[db] = mfma_k16(read_tr(st + v_off[db]), pb, o[db]);
 
       if (i + NSTAGE < n_my) {
         const int cn = ci + kWaves * NSTAGE;
@@ -292,64 +282,66 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   }
 
   // ---- merge the 4 waves through LDS ----
-  float lsum[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    lsum[h] = sum_over_quads(l_lane[h]);
-    if constexpr (D == 64) {
-      acc[h][0] += __shfl_xor(acc[h][0], 32);
-      acc[h][1] += __shfl_xor(acc[h][1], 32);
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  float *mrg = (float *)my;  // [m: G][l: G] .. [O: G rows of MS floats from ACC0]
+  if (hh < G) {
+    if (qd == 0) {
+      mrg[hh] = m;
+      mrg[G + hh] = lsum;
     }
-  }
-  float *mrg = (float *)my;  // [m: G][l: G][acc: G][D]
-  if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      mrg[h] = m[h];
-      mrg[G + h] = lsum[h];
-    }
-  }
-  {
-    const int dl = (D == 128) ? lane : (lane & 31);
-    if (D == 128 || lane < 32) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float2 v2 = {acc[h][0], acc[h][1]};
-        *(float2 *)(mrg + 2 * G + h * D + 2 * dl) = v2;
-      }
-    }
+    for (int d = 0; d < DB; ++d) *(f32x4 *)(mrg + ACC0 + hh * MS + 16 * d + 4 * qd) = o[d];
   }
   __syncthreads();
 
-  const bool direct = a.o_part == nullptr;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D;
-    float mw[kWaves];
-    float M = -INFINITY;
+  // Each thread finishes column pairs of the G rows.  All LDS reads of a
+  // thread are issued before any arithmetic so the merge costs one LDS round
+  // trip; a clamped index keeps the reads of idle threads inside the table.
+  constexpr int NPAIR = G * D / 2;
+  constexpr int NIT = (NPAIR + 255) / 256;
+  float mw[NIT][kWaves], lw[NIT][kWaves];
+  float2 aw[NIT][kWaves];
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int pi = min((int)threadIdx.x + 256 * k, NPAIR - 1);
+    const int h = pi / (D / 2), c = 2 * (pi % (D / 2));
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      mw[w] = ((const float *)(smem + w * Lay::WAVE_LDS))[h];
-      M = fmaxf(M, mw[w]);
+      const float *wb = (const float *)(smem + w * Lay::WAVE_LDS);
+      mw[k][w] = wb[h];
+      lw[k][w] = wb[G + h];
+      aw[k][w] = *(const float2 *)(wb + ACC0 + h * MS + c);
     }
-    float den = 0.f, num = 0.f;
+  }
+  const bool direct = a.o_part == nullptr;
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int pi = (int)threadIdx.x + 256 * k;
+    if (NPAIR % 256 != 0 && pi >= NPAIR) break;
+    const int h = pi / (D / 2), c = 2 * (pi % (D / 2));
+    float M = mw[k][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[k][w]);
+    float den = 0.f, n0 = 0.f, n1 = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float *mw_base = (const float *)(smem + w * Lay::WAVE_LDS);
-        const float e = exp2_fast(mw[w] - M);
-        den += e * mw_base[G + h];
-        num += e * mw_base[2 * G + idx];
+        const float e = exp2_fast(mw[k][w] - M);
+        den += e * lw[k][w];
+        n0 += e * aw[k][w].x;
+        n1 += e * aw[k][w].y;
       }
     }
     // den is 0 only when no wave saw a token (empty sequence); a NaN read from
     // the cache propagates to the output.
-    const float o = den != 0.f ? num / den : 0.f;
+    const float inv = den != 0.f ? 1.f / den : 0.f;
     if (direct) {
-      a.out[head0 * D + idx] = (uint16_t)pack_bf16(o, 0.f);
+      *(uint32_t *)(a.out + (head0 + h) * D + c) = pack_bf16(n0 * inv, n1 * inv);
     } else {
       const size_t row = (head0 + h) * a.num_splits + split;
-      a.o_part[row * D + (idx % D)] = o;
-      if (idx % D == 0) a.lse_part[row] = den != 0.f ? M + log2_fast(den) : -INFINITY;
+      *(float2 *)(a.o_part + row * D + c) = float2{n0 * inv, n1 * inv};
+      if (c == 0) a.lse_part[row] = den != 0.f ? M + log2_fast(den) : -INFINITY;
     }
   }
 }
@@ -357,9 +349,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 // Merge the pieces of one (sequence, q head) row; one 256-thread workgroup
 // per row.  Thread t reads lse of piece t; the workgroup max and the weights
 // 2^(lse_s - M) go through LDS.  For the weighted sum, thread t owns float4
-// column group t % (D/4) and pieces s = t / (D/4) (mod 256 / (D/4)); all of
-// its piece loads are issued before the weights are known, so the row costs
-// one memory round trip rather than one per piece.
+// column group t % (D/4) and pieces s = t / (D/4) (mod 256 / (D/4)).  Every
+// load of the first batch (pieces, lse and the context length) is issued at
+// once, before the number of non-empty pieces is known: rows of pieces past
+// the sequence end lie inside the workspace and are dropped by a select, so
+// the row costs one memory round trip.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int NV = D / 4;        // float4 column groups per row
@@ -370,25 +364,27 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float4 red[SG][NV];
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int L = as_const(a.context_lens)[b];
   const int S = a.num_splits;
   const size_t row = (size_t)b * a.num_q_heads + h;
+  const int v = tid % NV, sg = tid / NV;
+  const float4 *op = (const float4 *)(a.o_part + row * (size_t)S * D) + v;
+
+  const int L = as_const(a.context_lens)[b];
+  float4 ov[BATCH];
+#pragma unroll
+  for (int k = 0; k < BATCH; ++k) {
+    const int s = sg + k * SG;
+    ov[k] = s < S ? op[(size_t)s * NV] : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float lse_raw = tid < S ? a.lse_part[row * S + tid] : -INFINITY;
+
   uint16_t *out = a.out + row * D;
   if (L <= 0) {
     if (tid < D) out[tid] = 0;
     return;
   }
   const int ns = min(S, (L + a.split_len - 1) / a.split_len);
-  const int v = tid % NV, sg = tid / NV;
-  const float4 *op = (const float4 *)(a.o_part + row * (size_t)S * D) + v;
-
-  float4 ov[BATCH];
-#pragma unroll
-  for (int k = 0; k < BATCH; ++k) {
-    const int s = sg + k * SG;
-    ov[k] = s < ns ? op[(size_t)s * NV] : float4{0.f, 0.f, 0.f, 0.f};
-  }
-  const float lse = tid < ns ? a.lse_part[row * S + tid] : -INFINITY;
+  const float lse = tid < ns ? lse_raw : -INFINITY;
   float M = wave_max(lse);
   if (lane == 0) red_max[wv] = M;
   __syncthreads();
@@ -406,8 +402,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   float4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < BATCH; ++k) {
-    const float wk = w_lds[min(sg + k * SG, 255)];
-    acc.x += wk * ov[k].x; acc.y += wk * ov[k].y; acc.z += wk * ov[k].z; acc.w += wk * ov[k].w;
+    const int s = sg + k * SG;
+    if (s < ns) {
+      const float wk = w_lds[s];
+      acc.x += wk * ov[k].x; acc.y += wk * ov[k].y; acc.z += wk * ov[k].z; acc.w += wk * ov[k].w;
+    }
   }
   for (int s0 = BATCH * SG; s0 < ns; s0 += BATCH * SG) {
 #pragma unroll

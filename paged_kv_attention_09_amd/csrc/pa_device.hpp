@@ -8,7 +8,11 @@
 namespace pa {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // LDS scratch is written and read back at different widths (bf16 weights
 // stored singly, read in pairs); these types keep type-based alias analysis
@@ -51,6 +55,30 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
                                                                0xF, 0xF, false));
+}
+
+// Matrix-core products on 16x16 fp32 tiles (wave64 operand layouts, lane l):
+//   A[row = l % 16][k = K/4 * (l / 16) + e], B[k = K/4 * (l / 16) + e][col = l % 16],
+//   C/D[row = 4 * (l / 16) + i][col = l % 16], e < K/4, i < 4.
+// mfma_k32: v_mfma_f32_16x16x32_bf16 (8 bf16 of A and of B per lane).
+__device__ __forceinline__ f32x4 mfma_k32(const uint4 &a, const uint4 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// mfma_k16: v_mfma_f32_16x16x16_bf16 (4 bf16 of A and of B per lane).
+__device__ __forceinline__ f32x4 mfma_k16(const uint2 &a, const uint2 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: each lane names 8 bytes (4 bf16) of LDS; within every
+// group of 16 lanes, lane i receives as element j (j < 4) element i % 4 of
+// the 8 bytes named by lane 4 j + i / 4.  Reading 4 rows x 16 columns of a
+// row-major bf16 tile this way hands lane i column i of those 4 rows.
+__device__ __forceinline__ uint2 read_tr(const char *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(__attribute__((address_space(3))) void *)p);
+  return __builtin_bit_cast(uint2, v);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -38,18 +38,9 @@ namespace pa {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kQRows = 32;   // query positions per workgroup (two 16-row MFMA blocks)
 constexpr int kKeys = 64;    // keys per LDS tile
 constexpr float kSlackP = 8.f;
-
-__device__ __forceinline__ f32x4 mfma16(const uint4 &a, const uint4 &b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 // v_max3_f32 without the input canonicalisation the compiler adds for fmaxf
 // in IEEE mode (inputs here are matrix-core results, never signalling NaNs).
@@ -57,12 +48,6 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
-}
-
-__device__ __forceinline__ uint2 read_tr(const char *p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(__attribute__((address_space(3))) void *)p);
-  return __builtin_bit_cast(uint2, v);
 }
 
 template <int D>
@@ -249,16 +234,16 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const uint4 kf = *(const uint4 *)(Kt + k_off[0] + mb * 16 * ROWB);
-      s[mb][0] = mfma16(kf, qf[0][0], zero4);
-      s[mb][1] = mfma16(kf, qf[1][0], zero4);
+      s[mb][0] = mfma_k32(kf, qf[0][0], zero4);
+      s[mb][1] = mfma_k32(kf, qf[1][0], zero4);
     }
 #pragma unroll
     for (int ks = 1; ks < KS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const uint4 kf = *(const uint4 *)(Kt + k_off[ks] + mb * 16 * ROWB);
-        s[mb][0] = mfma16(kf, qf[0][ks], s[mb][0]);
-        s[mb][1] = mfma16(kf, qf[1][ks], s[mb][1]);
+        s[mb][0] = mfma_k32(kf, qf[0][ks], s[mb][0]);
+        s[mb][1] = mfma_k32(kf, qf[1][ks], s[mb][1]);
       }
     }
 
@@ -343,11 +328,11 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
         const uint2 lo = read_tr(vp);
         const uint2 hi = read_tr(vp + 16 * ROWB);
         const uint4 vf = uint4{lo.x, lo.y, hi.x, hi.y};
-        o[db][0] = mfma16(vf, pf[0][kk], o[db][0]);
-        o[db][1] = mfma16(vf, pf[1][kk], o[db][1]);
+        o[db][0] = mfma_k32(vf, pf[0][kk], o[db][0]);
+        o[db][1] = mfma_k32(vf, pf[1][kk], o[db][1]);
       }
-      ol[0] = mfma16(kOnes, pf[0][kk], ol[0]);
-      ol[1] = mfma16(kOnes, pf[1][kk], ol[1]);
+      ol[0] = mfma_k32(kOnes, pf[0][kk], ol[0]);
+      ol[1] = mfma_k32(kOnes, pf[1][kk], ol[1]);
     }
   }
 
