@@ -15,22 +15,29 @@
 //    is a scalar load and each DMA instruction has a scalar base address.
 //  * K and V rows of a chunk (16 x head_dim bf16 each) stream HBM -> LDS with
 //    global_load_lds_dwordx4 (16 bytes per lane, no VGPRs held in flight),
-//    NSTAGE chunks deep per wave.  The 16-byte positions of each row are
-//    XOR-swizzled by a rotation of the row index, so both LDS read patterns
-//    below touch every bank once.
-//  * The G q heads that share the kv head are the 16 columns of one matrix
-//    tile (columns G..15 are zero).  Scores S^T = K Q^T come from
-//    v_mfma_f32_16x16x32_bf16 (K rows from LDS, Q^T held in registers), which
-//    leaves lane l with head l % 16 and tokens 4 (l / 16) + i of the chunk.
+//    two chunks deep per wave.  The 16-byte positions of each row are XOR
+//    swizzled by row so the LDS reads of the compute path are bank-conflict
+//    free.
 //  * Online softmax per head in the exp2 domain with a lazily moved running
 //    max: the max moves (exact cross-lane max and rescale) only when a score
-//    exceeds it by more than kSlack; a wave ballot decides.  The weights are
-//    rounded to bf16 in place, and in place they are exactly the B operand
-//    of the second product.
-//  * O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, with V^T fragments taken
-//    from the row-major V chunk by ds_read_b64_tr_b16.  Per-head statistics
-//    and the output column of a head live in the same lanes, so a rescale
-//    is lane-local.
+//    exceeds it by more than kSlack; a wave ballot decides.  Weights are
+//    rounded to bf16 before the weighted V sum, and the denominator adds the
+//    same rounded weights.
+//  * Two compute paths for the per-chunk products, chosen by the group size
+//    G (q heads per kv head):
+//    - vector path (G <= 2): 4 lanes per token dot a quarter of the K row
+//      each against the G query rows with v_dot2c_f32_bf16 and a DPP quad
+//      sum; each lane owns 2 head_dim columns (1 for head_dim 64) and pairs
+//      the V values of adjacent tokens with a byte permute, one v_dot2c per
+//      token pair and head.
+//    - matrix path (G >= 3): the G heads are the columns of a 16x16 tile
+//      (columns G..15 zero).  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 leaves
+//      lane l with head l % 16 and tokens 4 (l / 16) + i; the bf16 weights,
+//      in place, are the B operand of O^T += V^T P^T on
+//      v_mfma_f32_16x16x16_bf16, with V^T read by ds_read_b64_tr_b16.  A
+//      head's statistics and output column share lanes, so a rescale is
+//      lane-local.  On the vector path the loop's ALU work grows with G and
+//      at G = 6..7 it, not the memory system, set the pace.
 //  * The 4 waves' (m, l, O) are merged through LDS; the workgroup writes
 //    either the final bf16 rows (one piece) or fp32 partials plus their
 //    base-2 log-sum-exp for the combine kernel.
@@ -46,14 +53,27 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kChunk = 16;     // tokens per wave step
+constexpr int kStages = 2;     // chunks in flight per wave
 constexpr float kSlack = 8.f;  // log2 headroom before the running max moves
+constexpr int kMaxVectorGroup = 2;
 
-// LDS position of 16-byte chunk c of row r is c ^ row_swizzle(r): a rotation
-// of the row index over the position bits (for head_dim 64 two rows share a
-// 256-byte bank line, so the row pair index is rotated).
-template <int D>
+template <int G>
+constexpr bool use_matrix_path() {
+  return G > kMaxVectorGroup;
+}
+
+// LDS position of 16-byte chunk c of row r is c ^ row_swizzle(r).
+//  vector path: lanes 4r..4r+3 read row r at positions u + 4k, so rows are
+//    shifted by 4 positions each;
+//  matrix path: 16 lanes read one position of rows 0..15, and the transposed
+//    V reads take 8 rows x 2 adjacent positions per 32 lanes; a rotation of
+//    the row index over the position bits serves both (for head_dim 64 two
+//    rows share a 256-byte bank line, so the row pair index is rotated).
+template <int D, bool MF>
 __device__ __forceinline__ int row_swizzle(int r) {
-  if constexpr (D == 128) {
+  if constexpr (!MF) {
+    return (r * 4) & (D / 8 - 1);
+  } else if constexpr (D == 128) {
     return ((r << 1) | (r >> 3)) & 15;
   } else {
     const int s = r >> 1;
@@ -61,8 +81,9 @@ __device__ __forceinline__ int row_swizzle(int r) {
   }
 }
 
-template <int D, int G, int NSTAGE>
+template <int D, int G>
 struct DecodeLayout {
+  static constexpr bool MF = use_matrix_path<G>();
   static constexpr int ROWB = D * 2;                 // bytes of one token row (one kv head)
   static constexpr int NPOS = D / 8;                 // 16-byte positions per row
   static constexpr int CHB = kChunk * ROWB;          // bytes of one chunk of K (or V)
@@ -70,21 +91,29 @@ struct DecodeLayout {
   static constexpr int STB = 2 * CHB;                // one stage: K chunk then V chunk
   static constexpr int QB = ((G * ROWB + 1023) / 1024) * 1024;
   static constexpr int NQDMA = QB / 1024;
-  static constexpr int WAVE_LDS = NSTAGE * STB + QB;
-  static constexpr int KS = D / 32;                  // 16x16x32 steps over head_dim
-  static constexpr int DB = D / 16;                  // 16-column blocks of head_dim
+  // vector path: bf16 weights of a chunk, [G][16]
+  static constexpr int PB = MF ? 0 : ((G * kChunk * 2 + 15) / 16) * 16;
+  static constexpr int WAVE_LDS = kStages * STB + QB + PB;
+  static constexpr int KS = D / 32;                  // matrix path: 16x16x32 steps over head_dim
+  static constexpr int DB = D / 16;                  // matrix path: 16-column blocks of head_dim
+  static constexpr int KPL = NPOS / 4;               // vector path: K pieces per lane per token
+  static constexpr int HALVES = 128 / D;             // vector path: token halves in P.V
+  static constexpr int PAIRS = kChunk / 2 / HALVES;  // vector path: token pairs per lane
   // merge scratch (fp32): m[G], l[G], then O rows of MS floats from ACC0
   static constexpr int ACC0 = (2 * G + 3) & ~3;
   static constexpr int MS = D + 4;
   static_assert(WAVE_LDS % 16 == 0, "alignment");
-  static_assert((ACC0 + G * MS) * 4 <= NSTAGE * STB, "merge scratch fits in the stages");
+  static_assert((ACC0 + G * MS) * 4 <= kStages * STB, "merge scratch fits in the stages");
 };
 
-template <int D, int G, int NSTAGE>
+template <int D, int G>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
-  using Lay = DecodeLayout<D, G, NSTAGE>;
+  using Lay = DecodeLayout<D, G>;
+  constexpr bool MF = Lay::MF;
+  constexpr int NSTAGE = kStages;
   constexpr int ROWB = Lay::ROWB, NPOS = Lay::NPOS, CHB = Lay::CHB, NDMA = Lay::NDMA;
   constexpr int STB = Lay::STB, KS = Lay::KS, DB = Lay::DB, ACC0 = Lay::ACC0, MS = Lay::MS;
+  constexpr int KPL = Lay::KPL, PAIRS = Lay::PAIRS;
   __shared__ __attribute__((aligned(1024))) char smem[kWaves * Lay::WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
@@ -127,6 +156,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 
   char *my = smem + wave * Lay::WAVE_LDS;
   char *qlds = my + NSTAGE * STB;
+  char *plds = qlds + Lay::QB;  // vector path only
   const uint32_t my_off = lds_offset(my);
   const uint32_t q_off = lds_offset(qlds);
 
@@ -159,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   for (int j = 0; j < NDMA; ++j) {
     const int r = j * (1024 / ROWB) + lane / NPOS;
     const int p = lane % NPOS;
-    const int c = p ^ row_swizzle<D>(r);
+    const int c = p ^ row_swizzle<D, MF>(r);
     dma_row[j] = r;
     dma_pos[j] = (uint32_t)c * 16;
     dma_voff[j] = (uint32_t)r * RS + (uint32_t)c * 16;
@@ -184,13 +214,24 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  // Lane roles in the matrix tiles: column hh = the q head, qd = the group
-  // of 4 tokens (scores) or of 4 head_dim entries (output).
+  // Softmax state and accumulators.  Matrix path: lane l holds head hh =
+  // l % 16 (m, partial l) and O^T[16 db + 4 qd + i][hh].  Vector path: every
+  // lane holds all G heads' m and partial l, and head_dim columns of acc.
   const int hh = lane & 15, qd = lane >> 4;
-  float m = -INFINITY, lsum = 0.f;
-  f32x4 o[DB];
+  float m_mf = -INFINITY, l_mf = 0.f;
+  f32x4 o[MF ? DB : 1];
+  float m_v[MF ? 1 : G], l_v[MF ? 1 : G], acc[MF ? 1 : G][2];
+  if constexpr (MF) {
 #pragma unroll
-  for (int d = 0; d < DB; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < DB; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m_v[h] = -INFINITY;
+      l_v[h] = 0.f;
+      acc[h][0] = acc[h][1] = 0.f;
+    }
+  }
 
   if (n_my > 0) {
     // q rows of the group -> LDS (clamped lanes re-read the last 16 bytes).
@@ -207,91 +248,207 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     for (int s = 0; s < NSTAGE; ++s)
       if (s < n_my) issue_chunk(wave + kWaves * s, s, blk_first[s]);
 
-    // LDS read offsets: K fragment kk of this lane is row hh, head_dim
-    // 32 kk + 8 qd .. + 7; V^T fragment db is 8 bytes of row 4 qd + hh / 4 at
-    // head_dim 16 db + 4 (hh % 4).
-    uint32_t k_off[KS], v_off[DB];
+    if constexpr (MF) {
+      // LDS read offsets: K fragment kk of this lane is row hh, head_dim
+      // 32 kk + 8 qd .. + 7; V^T fragment db is 8 bytes of row 4 qd + hh / 4
+      // at head_dim 16 db + 4 (hh % 4).
+      uint32_t k_off[KS], v_off[DB];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      k_off[kk] = (uint32_t)(hh * ROWB + (((4 * kk + qd) ^ row_swizzle<D>(hh)) * 16));
-    {
-      const int vr = 4 * qd + (hh >> 2);
+      for (int kk = 0; kk < KS; ++kk)
+        k_off[kk] = (uint32_t)(hh * ROWB + (((4 * kk + qd) ^ row_swizzle<D, MF>(hh)) * 16));
+      {
+        const int vr = 4 * qd + (hh >> 2);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        v_off[db] = (uint32_t)(CHB + vr * ROWB +
-                               (((2 * db + ((hh & 3) >> 1)) ^ row_swizzle<D>(vr)) * 16) +
-                               (hh & 1) * 8);
-    }
+        for (int db = 0; db < DB; ++db)
+          v_off[db] = (uint32_t)(CHB + vr * ROWB +
+                                 (((2 * db + ((hh & 3) >> 1)) ^ row_swizzle<D, MF>(vr)) * 16) +
+                                 (hh & 1) * 8);
+      }
 
-    uint4 qf[KS];
-    for (int i = 0; i < n_my; ++i) {
-      wait_vmcnt_steps<2 * NDMA, NSTAGE - 1>(min(NSTAGE - 1, n_my - 1 - i));
-      if (i == 0) {
-        // Q^T fragments: head hh (zero for hh >= G), head_dim 32 kk + 8 qd ...
-        const char *qrow = qlds + min(hh, G - 1) * ROWB + qd * 16;
+      uint4 qf[KS];
+      for (int i = 0; i < n_my; ++i) {
+        wait_vmcnt_steps<2 * NDMA, NSTAGE - 1>(min(NSTAGE - 1, n_my - 1 - i));
+        if (i == 0) {
+          // Q^T fragments: head hh (zero for hh >= G), head_dim 32 kk + 8 qd ...
+          const char *qrow = qlds + min(hh, G - 1) * ROWB + qd * 16;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const uint4 v = *(const uint4 *)(qrow + kk * 64);
-          qf[kk] = hh < G ? v : uint4{0u, 0u, 0u, 0u};
+          for (int kk = 0; kk < KS; ++kk) {
+            const uint4 v = *(const uint4 *)(qrow + kk * 64);
+            qf[kk] = hh < G ? v : uint4{0u, 0u, 0u, 0u};
+          }
+        }
+        const int ci = wave + kWaves * i;
+        const int tc = t0 + ci * kChunk;
+        const char *st = my + (i % NSTAGE) * STB;
+
+        // ---- S^T = K Q^T: lane holds head hh, tokens 4 qd + e ----
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          sc = mfma_k32(*(const uint4 *)(st + k_off[kk]), qf[kk], sc);
+
+        // ---- online softmax, lazily rescaled (see the file comment) ----
+        const int tok = tc + 4 * qd;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = tok + e < t1 ? sc[e] * a.scale_log2 : -INFINITY;
+        const float cmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        if (__builtin_amdgcn_ballot_w64(hh < G && cmax > m_mf + kSlack) != 0) {
+          float mx = fmaxf(m_mf, cmax);
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float alpha = mx == -INFINITY ? 1.f : exp2_fast(m_mf - mx);
+          m_mf = mx;
+          l_mf *= alpha;
+#pragma unroll
+          for (int d = 0; d < DB; ++d) o[d] *= alpha;
+        }
+        const float mm = m_mf == -INFINITY ? 0.f : m_mf;
+        const uint32_t p01 = pack_bf16(exp2_fast(x[0] - mm), exp2_fast(x[1] - mm));
+        const uint32_t p23 = pack_bf16(exp2_fast(x[2] - mm), exp2_fast(x[3] - mm));
+        l_mf += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+        const uint2 pb = {p01, p23};
+
+        // ---- O^T += V^T P^T: lane holds head hh, head_dim 16 db + 4 qd + i ----
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = mfma_k16(read_tr(st + v_off[db]), pb, o[db]);
+
+        if (i + NSTAGE < n_my) {
+          const int cn = ci + kWaves * NSTAGE;
+          issue_chunk(cn, i % NSTAGE, table[(t0 + cn * kChunk) >> bs_shift]);
         }
       }
-      const int ci = wave + kWaves * i;
-      const int tc = t0 + ci * kChunk;
-      const char *st = my + (i % NSTAGE) * STB;
+    } else {
+      const int r = lane >> 2, u = lane & 3;
+      const int swr = row_swizzle<D, MF>(r);
+      // P.V lane geometry
+      const int half = (D == 128) ? 0 : (lane >> 5);
+      const int dl = (D == 128) ? lane : (lane & 31);
+      const uint32_t v_in_chunk = (uint32_t)(dl & 3) * 4;
+      const int v_c = dl >> 2;
 
-      // ---- S^T = K Q^T: lane holds head hh, tokens 4 qd + e ----
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      uint4 qreg[G][KPL];
+      for (int i = 0; i < n_my; ++i) {
+        wait_vmcnt_steps<2 * NDMA, NSTAGE - 1>(min(NSTAGE - 1, n_my - 1 - i));
+        if (i == 0) {
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) sc = mfma_k32(*(const uint4 *)(st + k_off[kk]), qf[kk], sc);
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int k = 0; k < KPL; ++k)
+              qreg[h][k] = *(const uint4 *)(qlds + h * ROWB + (u + 4 * k) * 16);
+        }
+        const int ci = wave + kWaves * i;
+        const int tc = t0 + ci * kChunk;
+        const char *st = my + (i % NSTAGE) * STB;
 
-      // ---- online softmax, exp2 domain, lazily rescaled ----
-      // The running max m only moves when some score of the chunk exceeds it
-      // by more than kSlack (one wave ballot decides); otherwise the weights
-      // exp2(x - m) <= 2^kSlack stay well inside fp32/bf16 range.  The result
-      // is the same up to rounding: numerator and denominator share 2^-m.
-      const int tok = tc + 4 * qd;
-      float x[4];
+        // ---- scores for the G heads, 4 lanes per token ----
+        float s[G];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = tok + e < t1 ? sc[e] * a.scale_log2 : -INFINITY;
-      const float cmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (__builtin_amdgcn_ballot_w64(hh < G && cmax > m + kSlack) != 0) {
-        float mx = fmaxf(m, cmax);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float alpha = mx == -INFINITY ? 1.f : exp2_fast(m - mx);
-        m = mx;
-        lsum *= alpha;
+        for (int h = 0; h < G; ++h) s[h] = 0.f;
 #pragma unroll
-        for (int d = 0; d < DB; ++d) o[d] *= alpha;
-      }
-      const float mm = m == -INFINITY ? 0.f : m;
-      const uint32_t p01 = pack_bf16(exp2_fast(x[0] - mm), exp2_fast(x[1] - mm));
-      const uint32_t p23 = pack_bf16(exp2_fast(x[2] - mm), exp2_fast(x[3] - mm));
-      lsum += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-      const uint2 pb = {p01, p23};
+        for (int k = 0; k < KPL; ++k) {
+          const int p = (u + 4 * k) ^ swr;
+          const uint4 kv = *(const uint4 *)(st + r * ROWB + p * 16);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            s[h] = dot2(qreg[h][k].x, kv.x, s[h]);
+            s[h] = dot2(qreg[h][k].y, kv.y, s[h]);
+            s[h] = dot2(qreg[h][k].z, kv.z, s[h]);
+            s[h] = dot2(qreg[h][k].w, kv.w, s[h]);
+          }
+        }
+        // ---- online softmax, lazily rescaled (see the file comment) ----
+        const bool valid = tc + r < t1;
+        float x[G];
+        bool grow = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          x[h] = valid ? quad_sum(s[h]) * a.scale_log2 : -INFINITY;
+          grow |= x[h] > m_v[h] + kSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float m_new = fmaxf(m_v[h], max_over_quads(x[h]));
+            const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_v[h] - m_new);
+            m_v[h] = m_new;
+            l_v[h] *= alpha;
+            acc[h][0] *= alpha;
+            acc[h][1] *= alpha;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float mm = m_v[h] == -INFINITY ? 0.f : m_v[h];
+          const uint32_t pk = pack_bf16(exp2_fast(x[h] - mm), 0.f);
+          l_v[h] += bf16_lo(pk);
+          // the 4 lanes of a token hold the same weight and all store it
+          *(u16_alias *)(plds + h * (kChunk * 2) + r * 2) = (uint16_t)pk;
+        }
 
-      // ---- O^T += V^T P^T: lane holds head hh, head_dim 16 db + 4 qd + i ----
+        // ---- P.V: lanes own head_dim columns, tokens in pairs ----
+        const char *vst = st + CHB;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = mfma_k16(read_tr(st + v_off[db]), pb, o[db]);
+        for (int jj = 0; jj < PAIRS; ++jj) {
+          const int j = half * PAIRS + jj;
+          const int ta = 2 * j, tb = 2 * j + 1;
+          const uint32_t va = *(const uint32_t *)(vst + ta * ROWB +
+                                                  ((v_c ^ row_swizzle<D, MF>(ta)) * 16) + v_in_chunk);
+          const uint32_t vb = *(const uint32_t *)(vst + tb * ROWB +
+                                                  ((v_c ^ row_swizzle<D, MF>(tb)) * 16) + v_in_chunk);
+          const uint32_t lo = lo_pair(va, vb), hi = hi_pair(va, vb);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const uint32_t pp = *(const u32_alias *)(plds + h * (kChunk * 2) + j * 4);
+            acc[h][0] = dot2(pp, lo, acc[h][0]);
+            acc[h][1] = dot2(pp, hi, acc[h][1]);
+          }
+        }
 
-      if (i + NSTAGE < n_my) {
-        const int cn = ci + kWaves * NSTAGE;
-        issue_chunk(cn, i % NSTAGE, table[(t0 + cn * kChunk) >> bs_shift]);
+        if (i + NSTAGE < n_my) {
+          const int cn = ci + kWaves * NSTAGE;
+          issue_chunk(cn, i % NSTAGE, table[(t0 + cn * kChunk) >> bs_shift]);
+        }
       }
     }
   }
 
   // ---- merge the 4 waves through LDS ----
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
   float *mrg = (float *)my;  // [m: G][l: G] .. [O: G rows of MS floats from ACC0]
-  if (hh < G) {
-    if (qd == 0) {
-      mrg[hh] = m;
-      mrg[G + hh] = lsum;
-    }
+  if constexpr (MF) {
+    l_mf += __shfl_xor(l_mf, 16);
+    l_mf += __shfl_xor(l_mf, 32);
+    if (hh < G) {
+      if (qd == 0) {
+        mrg[hh] = m_mf;
+        mrg[G + hh] = l_mf;
+      }
 #pragma unroll
-    for (int d = 0; d < DB; ++d) *(f32x4 *)(mrg + ACC0 + hh * MS + 16 * d + 4 * qd) = o[d];
+      for (int d = 0; d < DB; ++d) *(f32x4 *)(mrg + ACC0 + hh * MS + 16 * d + 4 * qd) = o[d];
+    }
+  } else {
+    float lsum[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      lsum[h] = sum_over_quads(l_v[h]);
+      if constexpr (D == 64) {
+        acc[h][0] += __shfl_xor(acc[h][0], 32);
+        acc[h][1] += __shfl_xor(acc[h][1], 32);
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        mrg[h] = m_v[h];
+        mrg[G + h] = lsum[h];
+      }
+    }
+    const int dl = (D == 128) ? lane : (lane & 31);
+    if (D == 128 || lane < 32) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        *(float2 *)(mrg + ACC0 + h * MS + 2 * dl) = float2{acc[h][0], acc[h][1]};
+    }
   }
   __syncthreads();
 
@@ -436,12 +593,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
 }
 
-constexpr int kStages = 2;
-
 template <int D, int G>
 hipError_t launch_split_dg(const DecodeArgs &a, int num_seqs, hipStream_t stream) {
   dim3 grid(num_seqs * a.num_kv_heads, a.num_splits);
-  hipLaunchKernelGGL((decode_split_kernel<D, G, kStages>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

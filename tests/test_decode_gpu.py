@@ -78,11 +78,14 @@ def test_split_sweep(name):
 @pytest.mark.parametrize("D,G,bs", [(64, 1, 16), (64, 3, 256), (64, 8, 16), (128, 1, 256),
                                     (128, 2, 16), (128, 5, 16), (128, 8, 256)])
 def test_shape_matrix(D, G, bs):
-    """Every supported head_dim and group size, both block sizes, ragged lengths."""
+    """Every supported head_dim and group size, both block sizes, ragged lengths.
+    Small split counts give a grid of at most one workgroup per compute unit
+    (the 4-deep DMA pipeline); 64 pieces of 64 tokens give 640 workgroups
+    (the 2-deep pipeline, two workgroups per compute unit)."""
     spec = W.DecodeSpec(f"m{D}_{G}_{bs}", 5, 2 * G, 2, D, bs, 200, 4096 // bs,
                         context_lens=(1, 15, 16, 17, 700 if bs == 16 else 2049), seed=D + G + bs)
     case = DecodeCase(W.make_decode_inputs(spec))
-    for S in (1, 5, 0):
+    for S in (1, 5, 64, 0):
         assert_close(_run(case, S), case.ref, what=f"D{D} G{G} bs{bs} S{S}")
 
 
