@@ -52,6 +52,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["paged_kv_attention_09_amd/csrc/pa_decode.hip",
                   "paged_kv_attention_09_amd/csrc/pa_device.hpp"]
+PREFILL_SOURCES = ["paged_kv_attention_09_amd/csrc/pa_prefill.hip",
+                   "paged_kv_attention_09_amd/csrc/pa_device.hpp"]
 
 
 def parse_args(argv=None):
@@ -60,7 +62,8 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="c2b8",
-                   choices=["c2b8", "c2b1", "c3", "c4", "c5d"])
+                   choices=["c2b8", "c2b1", "c3", "c4", "c5d", "c5p"],
+                   help="decode workload timed; c5p (the prefill chunk) only with --kernel-loop")
     p.add_argument("--splits", type=int, default=0, help="0 = automatic")
     p.add_argument("--rotate-gib", type=float, default=2.0)
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -77,14 +80,16 @@ def parse_args(argv=None):
                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR",
                             "COPY_MIB", "KERNEL_CMD", "COPY_CMD"),
                    help="write profiles/decode_split_<workload>_hbm_counters.{json,md}")
+    p.add_argument("--ingest-sq", nargs=4, metavar=("DIR", "KERNEL", "NAME", "COMMAND"),
+                   help="write profiles/NAME.{md,json} from a rocprofv3 --pmc pass of SQ counters")
     p.add_argument("--copy-calibration", type=int, default=0,
                    help="profiling mode: run a plain device copy of this many MiB, 20 times")
     return p.parse_args(argv)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -499,6 +504,68 @@ def ingest_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_m
     print(base + ".json")
 
 
+def ingest_sq(directory: str, kernel: str, out_name: str, command: str, flop_per_call=None):
+    """Per-dispatch medians of SQ/GRBM counters for one kernel, from one
+    rocprofv3 --pmc pass, with rocprofv3's own derived formulas:
+    MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) and
+    MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
+    import statistics
+    rows = [r for r in _read_csv(directory, "counter_collection.csv") if kernel in r["Kernel_Name"]]
+    if not rows:
+        raise SystemExit(f"no rows for {kernel}")
+    per = {}
+    for r in rows:
+        per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+        per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    med = {c: statistics.median(v.values()) for c, v in per.items()}
+    # rocprofv3 writes each counter summed over its hardware instances; the
+    # GRBM counters have one instance per XCD and rocprofv3's own formulas
+    # take their maximum, i.e. about the sum over the XCD count.
+    gpu = [a for a in _read_csv(directory, "agent_info.csv") if a.get("Agent_Type") == "GPU"][0]
+    nxcc, simds = int(gpu["Num_Xcc"]), int(gpu["Simd_Count"])
+    for c in list(med):
+        if c.startswith("GRBM_"):
+            med[c] = med[c] / nxcc
+    durs = {}
+    for r in rows:
+        durs[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    med["dispatch_ns"] = statistics.median(durs.values())
+    lines = [f"# SQ counters: {out_name}", "", f"Kernel `{kernel}`; per-dispatch medians over "
+             f"{len(next(iter(per.values())))} dispatches.", "", "Command (run from /tmp with "
+             "TMPDIR=/tmp):", "", "```", command, "```", "", "| counter | value |", "|---|---|"]
+    lines += [f"| {c}{' (per XCD)' if c.startswith('GRBM_') else ''} | {v:.0f} |"
+              for c, v in sorted(med.items())]
+    rec = {"kernel": kernel, "counters": med, "command": command}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
+        util = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * simds)
+        rec["mfma_util"] = util
+        lines.append(f"| MfmaUtil = MFMA busy / (GUI active x {simds} SIMDs) | {100 * util:.1f} % |")
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+        ex = med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        rec["mfma_flop_executed"] = ex
+        lines.append(f"| bf16 MFMA flop executed per dispatch (MOPS x 512) | {ex:.4g} |")
+        lines.append(f"| executed MFMA rate over the dispatch | {ex / med['dispatch_ns'] / 1e3:.0f} "
+                     "TFLOP/s |")
+        if flop_per_call:
+            rec["flop_algorithmic"] = flop_per_call
+            lines.append(f"| algorithmic flop per call (unmasked pairs) | {flop_per_call:.4g} |")
+            lines.append(f"| executed / algorithmic | {ex / flop_per_call:.3f} |")
+            lines.append(f"| algorithmic rate over the dispatch | "
+                         f"{flop_per_call / med['dispatch_ns'] / 1e3:.0f} TFLOP/s |")
+    if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med:
+        c, a = med["SQ_LDS_BANK_CONFLICT"], med["SQ_LDS_IDX_ACTIVE"]
+        rec["lds_bank_conflict_rate"] = c / max(a - c, 1.0)
+        lines.append(f"| LDS bank conflict cycles / conflict-free LDS cycles | {c / max(a - c, 1.0):.4f} |")
+    rec["kernel_source_sha256_16"] = kernel_source_hash(
+        PREFILL_SOURCES if "prefill" in kernel else KERNEL_SOURCES)
+    lines.append(f"| kernel sources sha256[:16] | {rec['kernel_source_sha256_16']} |")
+    with open(os.path.join(PROFILES, out_name + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(PROFILES, out_name + ".json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(os.path.join(PROFILES, out_name + ".md"))
+
+
 def load_traffic(workload: str):
     path = os.path.join(PROFILES, f"decode_split_{workload}_hbm_counters.json")
     if not os.path.exists(path):
@@ -561,6 +628,8 @@ def measure(name, args, steps, warmup, with_kernel=True):
 
 def main(argv=None):
     args = parse_args(argv)
+    if args.workload == "c5p" and not args.kernel_loop:
+        raise SystemExit("--workload c5p is a profiling mode: use it with --kernel-loop")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding of this path is a design note, not a measured configuration.",
@@ -568,6 +637,17 @@ def main(argv=None):
         sys.exit(2)
     if args.ingest_trace:
         ingest_trace(*args.ingest_trace)
+        return
+    if args.ingest_sq:
+        d, k, name, cmd = args.ingest_sq
+        flop = None
+        if k == "prefill_kernel":
+            import numpy as np
+            import workloads as W
+            ps = W.PREFILL_CONFIGS["c5p"]
+            pos = np.concatenate([np.arange(L - n, L) for L, n in zip(ps.total_lens, ps.chunk_lens)])
+            flop = 4 * ps.head_dim * ps.num_q_heads * int((pos + 1).sum())
+        ingest_sq(d, k, name, cmd, flop)
         return
     if args.ingest_counters:
         a = args.ingest_counters
@@ -584,6 +664,14 @@ def main(argv=None):
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": n, "launches": 20}))
+        return
+    if args.kernel_loop and args.workload == "c5p":
+        wl = PrefillWorkload(W.PREFILL_CONFIGS["c5p"], None, args.rotate_gib)
+        for i in range(args.kernel_loop):
+            wl.prefill(i % wl.R)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": "c5p", "kernel_launches": args.kernel_loop,
+                          "splits": wl.S, "flop_per_call": wl.flop}))
         return
     if args.kernel_loop:
         wl = DecodeWorkload(W.CONFIGS[args.workload], args.rotate_gib, args.splits)
