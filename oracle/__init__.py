@@ -5,7 +5,7 @@ baseline leg of ``bench.py`` may import this package.  The HIP library and its
 Python binding never do.
 """
 from .paged_attention import (append, attend, bf16_bits_to_f64, block_and_offset, decode,
-                              gather_sequence, kv_head_of, prefill)
+                              decode_multi, gather_sequence, kv_head_of, prefill)
 
-__all__ = ["append", "attend", "bf16_bits_to_f64", "block_and_offset", "decode",
+__all__ = ["append", "attend", "bf16_bits_to_f64", "block_and_offset", "decode", "decode_multi",
            "gather_sequence", "kv_head_of", "prefill"]

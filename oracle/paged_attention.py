@@ -27,6 +27,15 @@ What it computes, and where the pages state it:
   Capabilities at a Glance" table, row "Prompt Ingestion (v0.2.1)".  Query i
   of an n-token chunk of a sequence of total length L sits at position
   L - n + i and sees keys 0 .. L - n + i.
+* ``decode_multi`` - several query tokens per sequence in one decode step,
+  causal among themselves: the target model's parallel verification of a
+  speculative draft ("Speculative Decoding: K-token draft proposals with
+  parallel target verification", mini-infer docs, "Core Capabilities at a
+  Glance" table, row "Generation Speed"; draft-model speculative decoding,
+  zingnex.cn mini-infer thread, feature list item 5).  The draft tokens are
+  already in the cache, so query token j of q_len sits at position
+  L - q_len + j and sees keys 0 .. L - q_len + j; a position below 0 (a
+  sequence shorter than its query window) sees no key and gives a zero row.
 
 Readings taken where the pages are silent (listed with the rest in the design
 notes): q head h reads kv head h // (Hq / Hkv); ``context_lens`` counts every
@@ -117,6 +126,29 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_tables
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             out[b, h] = attend(qf[b, h], K[:, g, :], V[:, g, :], sc)
+    return out
+
+
+def decode_multi(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                 block_tables: np.ndarray, context_lens: np.ndarray, scale) -> np.ndarray:
+    """q: bf16 bits [B, q_len, Hq, D]; context_lens [B] count the q_len query
+    tokens, whose K/V are already in the pool.  Returns fp64 [B, q_len, Hq, D]:
+    query token j attends keys 0 .. context_lens[b] - q_len + j."""
+    B, QL, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    sc = np.float64(np.float32(scale))
+    qf = bf16_bits_to_f64(q)
+    out = np.zeros((B, QL, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        K = bf16_bits_to_f64(gather_sequence(k_cache, block_tables[b], L))
+        V = bf16_bits_to_f64(gather_sequence(v_cache, block_tables[b], L))
+        for j in range(QL):
+            p = L - QL + j                     # absolute position of query token j
+            n_keys = p + 1 if p >= 0 else 0
+            for h in range(Hq):
+                g = kv_head_of(h, Hq, Hkv)
+                out[b, j, h] = attend(qf[b, j, h], K[:n_keys, g, :], V[:n_keys, g, :], sc)
     return out
 
 

@@ -312,6 +312,50 @@ def pin_prefill(oracle, seed=16):
     assert np.array_equal(one, dec)
 
 
+def _sdpa_window(qb, Kb, Vb, scale):
+    """torch fp64 SDPA of a window of query tokens at the end of one logical
+    sequence: qb [QL, Hq, D], Kb/Vb [L, Hkv, D] (bf16 bits, L >= QL); token j
+    may see keys 0 .. L - QL + j (explicit boolean mask)."""
+    QL, Hq, D = qb.shape
+    L, Hkv, _ = Kb.shape
+    G = Hq // Hkv
+    qt = torch.from_numpy(_f64(qb)).permute(1, 0, 2)[None]                         # [1, Hq, QL, D]
+    kt = torch.from_numpy(_f64(Kb)).permute(1, 0, 2).repeat_interleave(G, 0)[None]  # [1, Hq, L, D]
+    vt = torch.from_numpy(_f64(Vb)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    mask = torch.arange(L)[None, :] <= (L - QL + torch.arange(QL))[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask,
+                                                         scale=float(scale))
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def pin_decode_multi(oracle, seed=17):
+    """P12: several query tokens per sequence (the speculative verify step):
+    (a) against a masked library SDPA on the contiguous sequence, GQA by
+    torch's head repetition, for ragged lengths and 4 query tokens; (b) one
+    query token is decode, exactly; (c) a sequence shorter than its window:
+    tokens before position 0 give zero rows, the token at position 0 returns
+    V[0] exactly."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D, bs, QL = 6, 2, 8, 4, 4
+    lens = (4, 9, 17)
+    _, Ks, Vs = _logical_case(rng, lens, Hq, Hkv, D)
+    q = W.f32_to_bf16_bits(rng.standard_normal((len(lens), QL, Hq, D), dtype=np.float32))
+    kp, tables = _page_blockwise(np.random.default_rng(4), Ks, bs, 16)
+    vp, _ = _page_blockwise(np.random.default_rng(4), Vs, bs, 16)
+    sc = np.float32(0.3)
+    lens_a = np.array(lens, np.int32)
+    got = oracle.decode_multi(q, kp, vp, tables, lens_a, sc)
+    for b in range(len(lens)):
+        ref = _sdpa_window(q[b], Ks[b], Vs[b], np.float64(sc))
+        assert np.abs(got[b] - ref).max() < 1e-12, b
+    one = oracle.decode_multi(q[:, :1], kp, vp, tables, lens_a, sc)
+    assert np.array_equal(one[:, 0], oracle.decode(q[:, 0], kp, vp, tables, lens_a, sc))
+    short = oracle.decode_multi(q[:1], kp, vp, tables, np.array([2], np.int32), sc)
+    assert np.array_equal(short[0, :2], np.zeros((2, Hq, D)))
+    for h in range(Hq):
+        assert np.array_equal(short[0, 2, h], _f64(Vs[0][0, h // (Hq // Hkv)]))
+
+
 ALL_PINS = [pin_sdpa_decode, pin_loops_decode, pin_two_token_closed_form, pin_permutation,
             pin_block_size, pin_ctx1_returns_v, pin_constant_v, pin_histogram, pin_gqa_mapping,
-            pin_poison_untouched, pin_empty_sequence, pin_append, pin_prefill]
+            pin_poison_untouched, pin_empty_sequence, pin_append, pin_prefill, pin_decode_multi]

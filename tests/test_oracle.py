@@ -31,6 +31,9 @@ MUTANTS = {
     "q_head_fixed": ("attend(qf[b, h], K[:, g, :]", "attend(qf[b, 0], K[:, g, :]"),
     "prefill_top_left": ("p = L - n + i ", "p = i "),
     "prefill_excludes_self": ("K[:p + 1, g, :], V[:p + 1, g, :]", "K[:p, g, :], V[:p, g, :]"),
+    "multi_window_shifted": ("p = L - QL + j ", "p = L - QL + j + 1 "),
+    "multi_negative_wraps": ("n_keys = p + 1 if p >= 0 else 0", "n_keys = p + 1"),
+    "multi_query_token_fixed": ("attend(qf[b, j, h]", "attend(qf[b, 0, h]"),
     "append_transposed": ("kc[s // bs, s % bs] = new_k[i]", "kc[s % bs, s // bs] = new_k[i]"),
     "append_negative_written": ("if s < 0:", "if s < -1:"),
     "append_v_from_k": ("vc[s // bs, s % bs] = new_v[i]", "vc[s // bs, s % bs] = new_k[i]"),
