@@ -68,7 +68,7 @@ def parse_args(argv=None):
     p.add_argument("--rotate-gib", type=float, default=2.0)
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--others", default="c2b1,c3,c4,c5d,c5p,c5mix",
+    p.add_argument("--others", default="c2b1,c3,c4,c5d,c5p,c5mix,c2b8q2,c2b8q4,c3q4",
                    help="comma list of extra workloads measured into 'workloads' ('' = none)")
     p.add_argument("--kernel-loop", type=int, default=0,
                    help="profiling mode: launch only the split kernel this many times and exit")
@@ -101,7 +101,7 @@ def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
 class DecodeWorkload:
     """Device-resident inputs of one decode workload with R block rotations."""
 
-    def __init__(self, spec, rotate_gib: float, splits: int, seed: int = 1234):
+    def __init__(self, spec, rotate_gib: float, splits: int, seed: int = 1234, q_len: int = 1):
         import numpy as np
         import torch
 
@@ -146,16 +146,20 @@ class DecodeWorkload:
             slots.append(torch.from_numpy(last).to(dev))
         self.tables, self.slots = tables, slots
         self.lens = torch.from_numpy(self.lens_np).to(dev)
-        self.q = torch.randn((B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+        self.q_len = q_len
+        qshape = (B, Hq, D) if q_len == 1 else (B, q_len, Hq, D)
+        self.q = torch.randn(qshape, generator=g, device=dev).to(torch.bfloat16)
         self.new_k = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
         self.new_v = torch.randn((B, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
-        self.out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty(qshape, dtype=torch.bfloat16, device=dev)
         self.scale = float(spec.scale_f32)
         self.S = splits if splits > 0 else pa.auto_splits(B, Hkv, W_, bs, dev)
-        ws = pa.decode_workspace_size(B, Hq, D, self.S)
+        ws = pa.decode_multi_workspace_size(B, q_len, Hq, D, self.S)
         self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         self.pa = pa
-        self.decode_bytes = W.algorithmic_decode_bytes(self.lens_np, Hq, Hkv, D, bs)
+        # q and out once per query token; the cache once whatever q_len
+        self.decode_bytes = (W.algorithmic_decode_bytes(self.lens_np, Hq, Hkv, D, bs)
+                             + (q_len - 1) * B * Hq * D * 2 * 2)
         self.append_bytes = B * Hkv * D * 2 * 2 * 2 + B * 8
         self.decode_flop = 4 * D * Hq * int(self.lens_np.sum())
 
@@ -165,6 +169,16 @@ class DecodeWorkload:
         ws = self.pa.decode_workspace_size(self.spec.num_seqs, self.spec.num_q_heads,
                                            self.spec.head_dim, S)
         self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=self.dev)
+
+    def step_multi(self, r: int):
+        """Multi-token decode: q_len query tokens per sequence, causal."""
+        self.pa.decode_multi(self.q, self.k_cache, self.v_cache, self.tables[r], self.lens,
+                             self.scale, self.S, self.out, workspace=self.ws)
+
+    def step_plain(self, r: int):
+        """Single-token decode without the append."""
+        self.pa.decode(self.q, self.k_cache, self.v_cache, self.tables[r], self.lens, self.scale,
+                       self.S, self.out, workspace=self.ws)
 
     def step(self, r: int):
         """Append of each sequence's new row fused with the decode."""
@@ -626,6 +640,30 @@ def measure(name, args, steps, warmup, with_kernel=True):
     return wl, rec
 
 
+MULTI_WORKLOADS = {"c2b8q2": ("c2b8", 2), "c2b8q4": ("c2b8", 4), "c3q4": ("c3", 4)}
+
+
+def measure_multi(name, args, steps, warmup):
+    """Multi-token decode (the speculative verify step) on a decode workload's
+    shapes and lengths, against single-token decode of the same batch."""
+    import torch
+    import workloads as W
+    base, q_len = MULTI_WORKLOADS[name]
+    spec = W.CONFIGS[base]
+    wl = DecodeWorkload(spec, args.rotate_gib, args.splits, q_len=q_len)
+    ms = time_graph(wl.step_multi, wl.R, steps, warmup)
+    rec = {"workload": name, "base_workload": base, "q_len": q_len,
+           "us_per_call": ms * 1e3, "gbps": wl.decode_bytes / (ms * 1e-3) / 1e9,
+           "decode_bytes": wl.decode_bytes, "splits": wl.S, "rotations": wl.R}
+    del wl
+    torch.cuda.empty_cache()
+    one = DecodeWorkload(spec, args.rotate_gib, args.splits)
+    ms1 = time_graph(one.step_plain, one.R, steps, warmup)
+    rec["single_token_us_per_call"] = ms1 * 1e3
+    rec["ratio_to_single_token"] = ms / ms1
+    return one, rec
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.workload == "c5p" and not args.kernel_loop:
@@ -721,7 +759,12 @@ def main(argv=None):
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         del wl
         torch.cuda.empty_cache()
-        if name in ("c5p", "c5mix"):
+        if name in MULTI_WORKLOADS:
+            wl, rec = measure_multi(name, args, min(args.steps, 100), min(args.warmup, 10))
+            msg = (f"q_len {rec['q_len']}: {rec['us_per_call']:.2f} us/call, {rec['gbps']:.1f} GB/s;"
+                   f" single-token {rec['single_token_us_per_call']:.2f} us "
+                   f"(x{rec['ratio_to_single_token']:.2f})")
+        elif name in ("c5p", "c5mix"):
             wl, rec = measure_prefill(args, min(args.steps, 50), min(args.warmup, 5),
                                       with_decode=(name == "c5mix"))
             msg = f"prefill {rec['prefill_us']:.2f} us ({rec['prefill_tflops']:.0f} TFLOP/s)"

@@ -61,6 +61,7 @@ enum {
 };
 
 #define PA_MAX_SPLITS 256
+#define PA_MAX_QUERY_TOKENS 8
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
 int pa_version(void);
@@ -136,6 +137,43 @@ int pa_append_decode(const void *q, const void *new_k, const void *new_v, void *
                      void *stream);
 
 /*
+ * Multi-token decode: q_len query tokens per sequence, causal among
+ * themselves, attend the paged cache in one pass - the target model's
+ * parallel verification of a speculative draft of q_len - 1 tokens
+ * ("Speculative Decoding: K-token draft proposals with parallel target
+ * verification", mini-infer docs, "Core Capabilities at a Glance" table, row
+ * "Generation Speed"; draft-model speculative decoding, zingnex.cn mini-infer
+ * thread, feature list item 5).  The q_len tokens' K/V rows must already be
+ * in the cache (pa_reshape_and_cache), and context_lens[b] counts them.
+ * Query token j of sequence b sits at position p = context_lens[b] - q_len + j
+ * and attends the keys t <= p of its sequence:
+ *   out[b, j, h] = softmax_{t <= p}(scale * q[b, j, h] . K_b[t, g]) V_b[t, g].
+ * A query token with p < 0 (a sequence shorter than q_len) gets a zero row.
+ * q_len = 1 computes what pa_decode computes.  Split-KV as for pa_decode; the
+ * pieces of a sequence serve all its query tokens, so the cache is read once
+ * per step whatever q_len.
+ *   q, out        bf16 [num_seqs, q_len, num_q_heads, head_dim]
+ *   workspace     at least pa_decode_multi_workspace_size(num_seqs, q_len,
+ *                 num_q_heads, head_dim, S) bytes for the S used.
+ * Limits: 1 <= q_len <= PA_MAX_QUERY_TOKENS (else PA_ERR_SHAPE), and
+ * (num_q_heads / num_kv_heads) * q_len <= 32 (else PA_ERR_UNSUPPORTED);
+ * the other arguments and limits are those of pa_decode.
+ */
+int pa_decode_multi(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, float scale,
+                    int num_splits, void *out, int num_seqs, int q_len, int num_q_heads,
+                    int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                    int max_blocks_per_seq, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Workspace bytes pa_decode_multi needs: fp32 partial rows
+ * [num_seqs, q_len, num_q_heads, S, head_dim], then (256-byte aligned) their
+ * base-2 log-sum-exp [num_seqs, q_len, num_q_heads, S].  0 when
+ * num_splits <= 1 or for invalid arguments. */
+size_t pa_decode_multi_workspace_size(int num_seqs, int q_len, int num_q_heads, int head_dim,
+                                      int num_splits);
+
+/*
  * The two passes of pa_decode as separate calls, for callers that merge
  * pieces themselves (for example pieces of one sequence computed on
  * different devices) or time the passes apart.  Arguments mean what they mean
@@ -173,9 +211,11 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int
 
 /* Split count that pa_decode uses for num_splits = 0 on a device with
  * num_cus compute units.  Pure host arithmetic on the shapes (context
- * lengths are device-resident and are not read): it aims for enough
- * (sequence, kv head, piece) work units to fill the device.  Returns a value
- * in [1, PA_MAX_SPLITS], or a negative status for invalid arguments. */
+ * lengths are device-resident and are not read): it aims for about one
+ * (sequence, kv head, piece) work unit per compute unit, so S = 1 once the
+ * (sequence, kv head) pairs alone reach num_cus; pieces never go below 64
+ * tokens.  Returns a value in [1, PA_MAX_SPLITS], or a negative status for
+ * invalid arguments. */
 int pa_decode_plan_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
                           int block_size, int num_cus);
 

@@ -12,10 +12,13 @@ Calls (argument order as in the C ABI):
          stream=None, workspace=None)
   append_decode(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, scale,
                 num_splits, out, stream=None, workspace=None)
+  decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
+               stream=None, workspace=None): q_len query tokens per sequence, causal
   decode_partials(...), decode_merge(...): the two passes of decode
   prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, out,
           max_q_len, num_splits=0, stream=None, workspace=None)
   decode_workspace_size(num_seqs, num_q_heads, head_dim, num_splits)
+  decode_multi_workspace_size(num_seqs, q_len, num_q_heads, head_dim, num_splits)
   plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus)
   auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, device=None)
 """
@@ -32,6 +35,7 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libpagedattn.so")
 
 PA_OK = 0
 PA_MAX_SPLITS = 256
+PA_MAX_QUERY_TOKENS = 8
 
 # Every symbol include/pagedattn.h declares, with its ctypes signature.
 _VP, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -44,6 +48,9 @@ SIGNATURES = {
     "pa_append_decode": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F, _I, _VP, _I, _I, _I, _I, _I,
                               _I64, _I, _VP, _SZ, _VP]),
     "pa_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "pa_decode_multi": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _I, _VP, _I, _I, _I, _I, _I, _I, _I64, _I,
+                             _VP, _SZ, _VP]),
+    "pa_decode_multi_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "pa_decode_plan_splits": (_I, [_I, _I, _I, _I, _I]),
     "pa_decode_auto_splits": (_I, [_I, _I, _I, _I, _I]),
     "pa_decode_partials": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _I, _I, _I, _I, _I, _I, _I64, _I, _VP,
@@ -137,6 +144,12 @@ def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, num_sp
     return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, num_splits))
 
 
+def decode_multi_workspace_size(num_seqs: int, q_len: int, num_q_heads: int, head_dim: int,
+                                num_splits: int) -> int:
+    return int(lib().pa_decode_multi_workspace_size(num_seqs, q_len, num_q_heads, head_dim,
+                                                    num_splits))
+
+
 def plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus) -> int:
     r = int(lib().pa_decode_plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
                                         num_cus))
@@ -184,6 +197,34 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_sp
     return out
 
 
+def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_splits: int,
+                 out, stream=None, workspace: Optional[torch.Tensor] = None):
+    """q, out: [B, q_len, Hq, D].  Query token j of sequence b sits at position
+    context_lens[b] - q_len + j and attends the keys up to that position (the
+    q_len tokens' K/V must already be in the cache).  The cache is read once
+    for all q_len tokens."""
+    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _need(q, "q", torch.bfloat16, 4, dev)
+    _need(out, "out", torch.bfloat16, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, QL, Hq, Dq = (int(x) for x in q.shape)
+    if Dq != D or tuple(out.shape) != (B, QL, Hq, D):
+        raise ValueError(f"q/out must be [{B}, {QL}, {Hq}, {D}]")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables/context_lens batch differs from q")
+    W = int(block_tables.shape[1])
+    if num_splits == 0 and B > 0:
+        num_splits = auto_splits(B, Hkv, W, bs, dev)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace, q_len=QL)
+    _check("pa_decode_multi", lib().pa_decode_multi(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), float(scale), int(num_splits), out.data_ptr(), B, QL, Hq, Hkv,
+        D, bs, NB, W, ws_ptr, ws_bytes, _stream_ptr(stream, dev)))
+    return out
+
+
 def append_decode(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, scale: float,
                   num_splits: int, out, stream=None, workspace: Optional[torch.Tensor] = None):
     """One decode step with the append fused in: new_k[b], new_v[b] ([B, Hkv, D])
@@ -207,8 +248,8 @@ def append_decode(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
-def _workspace(B, Hq, D, num_splits, dev, workspace):
-    need = decode_workspace_size(B, Hq, D, num_splits) if B > 0 else 0
+def _workspace(B, Hq, D, num_splits, dev, workspace, q_len=1):
+    need = decode_multi_workspace_size(B, q_len, Hq, D, num_splits) if B > 0 else 0
     if not need:
         return None, 0, workspace
     if workspace is None:

@@ -10,6 +10,8 @@
 #include "pa_kernels.hpp"
 #include "pagedattn.h"
 
+static_assert(PA_MAX_QUERY_TOKENS == pa::kMaxQueryTokens, "query token limit");
+
 namespace {
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
@@ -105,9 +107,14 @@ int pa_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mappi
 }
 
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int num_splits) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  return pa_decode_multi_workspace_size(num_seqs, 1, num_q_heads, head_dim, num_splits);
+}
+
+size_t pa_decode_multi_workspace_size(int num_seqs, int q_len, int num_q_heads, int head_dim,
+                                      int num_splits) {
+  if (num_seqs <= 0 || q_len <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
   if (num_splits <= 1 || num_splits > PA_MAX_SPLITS) return 0;
-  const size_t rows = (size_t)num_seqs * num_q_heads * num_splits;
+  const size_t rows = (size_t)num_seqs * q_len * num_q_heads * num_splits;
   const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
   return o_bytes + (rows * sizeof(float) + 255) / 256 * 256;
 }
@@ -119,8 +126,11 @@ int pa_decode_plan_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq
   if (st != PA_OK) return st;
   const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  // Aim for about two resident workgroups per compute unit.
-  const int64_t target = 2 * (int64_t)num_cus;
+  // Aim for about one workgroup per compute unit: measured on the
+  // ctx-4096 batches, the 7B batch and the 64-sequence mixed decode, it beats
+  // two per compute unit (fewer partials to merge, and no merge launch at
+  // all once the (sequence, kv head) units alone fill the device).
+  const int64_t target = (int64_t)num_cus;
   int64_t s = 1;
   if (units < target) s = (target + units - 1) / units;
   if (s > PA_MAX_SPLITS) s = PA_MAX_SPLITS;
@@ -180,14 +190,16 @@ int resolve_decode(const void *q, const void *k_cache, const void *v_cache,
   a->bs_shift = log2_exact(block_size);
   a->split_len = split_len;
   a->num_splits = num_pieces(max_tokens, split_len);
+  a->q_len = 1;
   return PA_OK;
 }
 
 int attach_workspace(pa::DecodeArgs *a, int num_seqs, int head_dim, const void *workspace,
                      size_t workspace_bytes) {
-  const size_t need = pa_decode_workspace_size(num_seqs, a->num_q_heads, head_dim, a->num_splits);
+  const size_t need = pa_decode_multi_workspace_size(num_seqs, a->q_len, a->num_q_heads, head_dim,
+                                                     a->num_splits);
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-  const size_t rows = (size_t)num_seqs * a->num_q_heads * a->num_splits;
+  const size_t rows = (size_t)num_seqs * a->q_len * a->num_q_heads * a->num_splits;
   const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
   a->o_part = (float *)workspace;
   a->lse_part = (float *)((char *)workspace + o_bytes);
@@ -239,6 +251,31 @@ int pa_append_decode(const void *q, const void *new_k, const void *new_v, void *
   a.out = (uint16_t *)out;
   a.new_k = (const uint16_t *)new_k;
   a.new_v = (const uint16_t *)new_v;
+  if (a.num_splits > 1) {
+    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+  }
+  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
+                                (hipStream_t)stream);
+}
+
+int pa_decode_multi(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, float scale,
+                    int num_splits, void *out, int num_seqs, int q_len, int num_q_heads,
+                    int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                    int max_blocks_per_seq, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  if (q_len < 1 || q_len > PA_MAX_QUERY_TOKENS) return PA_ERR_SHAPE;
+  pa::DecodeArgs a;
+  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, &a);
+  if (st != PA_OK) return st;
+  if ((num_q_heads / num_kv_heads) * q_len > pa::kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out) return PA_ERR_NULL;
+  a.q_len = q_len;
+  a.out = (uint16_t *)out;
   if (a.num_splits > 1) {
     st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
     if (st != PA_OK) return st;

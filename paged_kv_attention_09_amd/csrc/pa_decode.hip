@@ -57,11 +57,6 @@ constexpr int kStages = 2;     // chunks in flight per wave
 constexpr float kSlack = 8.f;  // log2 headroom before the running max moves
 constexpr int kMaxVectorGroup = 2;
 
-template <int G>
-constexpr bool use_matrix_path() {
-  return G > kMaxVectorGroup;
-}
-
 // LDS position of 16-byte chunk c of row r is c ^ row_swizzle(r).
 //  vector path: lanes 4r..4r+3 read row r at positions u + 4k, so rows are
 //    shifted by 4 positions each;
@@ -81,40 +76,60 @@ __device__ __forceinline__ int row_swizzle(int r) {
   }
 }
 
-template <int D, int G>
-struct DecodeLayout {
-  static constexpr bool MF = use_matrix_path<G>();
+template <int D>
+struct DecodeGeom {
   static constexpr int ROWB = D * 2;                 // bytes of one token row (one kv head)
   static constexpr int NPOS = D / 8;                 // 16-byte positions per row
   static constexpr int CHB = kChunk * ROWB;          // bytes of one chunk of K (or V)
   static constexpr int NDMA = CHB / 1024;            // DMA instructions per tensor per chunk
   static constexpr int STB = 2 * CHB;                // one stage: K chunk then V chunk
-  static constexpr int QB = ((G * ROWB + 1023) / 1024) * 1024;
-  static constexpr int NQDMA = QB / 1024;
-  // vector path: bf16 weights of a chunk, [G][16]
-  static constexpr int PB = MF ? 0 : ((G * kChunk * 2 + 15) / 16) * 16;
-  static constexpr int WAVE_LDS = kStages * STB + QB + PB;
   static constexpr int KS = D / 32;                  // matrix path: 16x16x32 steps over head_dim
   static constexpr int DB = D / 16;                  // matrix path: 16-column blocks of head_dim
   static constexpr int KPL = NPOS / 4;               // vector path: K pieces per lane per token
   static constexpr int HALVES = 128 / D;             // vector path: token halves in P.V
   static constexpr int PAIRS = kChunk / 2 / HALVES;  // vector path: token pairs per lane
-  // merge scratch (fp32): m[G], l[G], then O rows of MS floats from ACC0
-  static constexpr int ACC0 = (2 * G + 3) & ~3;
-  static constexpr int MS = D + 4;
-  static_assert(WAVE_LDS % 16 == 0, "alignment");
-  static_assert((ACC0 + G * MS) * 4 <= kStages * STB, "merge scratch fits in the stages");
+  static constexpr int MS = D + 4;                   // merge scratch: floats per O row
 };
 
-template <int D, int G>
+// Per-wave LDS of the split kernel.  One query token: the DMA stages, the G
+// q rows (staged by DMA, read once into registers) and, on the vector path,
+// the bf16 weights of a chunk.  Several query tokens: the DMA stages only (the
+// q rows go straight to registers).  The four-wave merge reuses the same
+// bytes, in passes of at most `pass_rows` rows: m and l of the pass's rows,
+// then its O rows; decode_merge_fits checks that they fit.
+template <int D>
+constexpr int decode_wave_lds(int q_rows, bool vector_path) {
+  using Ge = DecodeGeom<D>;
+  return kStages * Ge::STB + (q_rows * Ge::ROWB + 1023) / 1024 * 1024 +
+         (vector_path ? (q_rows * kChunk * 2 + 15) / 16 * 16 : 0);
+}
+template <int D>
+constexpr bool decode_merge_fits(int pass_rows, int wave_lds) {
+  return (((2 * pass_rows + 3) & ~3) + pass_rows * DecodeGeom<D>::MS) * 4 <= wave_lds;
+}
+static_assert(decode_merge_fits<128>(8, decode_wave_lds<128>(1, false)) &&
+                  decode_merge_fits<64>(8, decode_wave_lds<64>(1, false)) &&
+                  decode_merge_fits<128>(16, decode_wave_lds<128>(0, false)) &&
+                  decode_merge_fits<64>(16, decode_wave_lds<64>(0, false)) &&
+                  decode_merge_fits<128>(kMaxVectorGroup, decode_wave_lds<128>(1, true)) &&
+                  decode_merge_fits<64>(kMaxVectorGroup, decode_wave_lds<64>(1, true)),
+              "merge scratch fits in the wave's LDS");
+
+// MF selects the matrix path; NT is its number of 16-column tiles, which
+// hold the G * q_len query rows (column c = query token c / G, head c % G).
+// MULTI: q_len comes from the arguments, the q rows go straight to
+// registers and the merge runs in passes of 16 rows; without it q_len is 1.
+// The vector path handles one query token and NT = 1.
+template <int D, int G, bool MF, int NT, bool MULTI>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
-  using Lay = DecodeLayout<D, G>;
-  constexpr bool MF = Lay::MF;
+  using Ge = DecodeGeom<D>;
   constexpr int NSTAGE = kStages;
-  constexpr int ROWB = Lay::ROWB, NPOS = Lay::NPOS, CHB = Lay::CHB, NDMA = Lay::NDMA;
-  constexpr int STB = Lay::STB, KS = Lay::KS, DB = Lay::DB, ACC0 = Lay::ACC0, MS = Lay::MS;
-  constexpr int KPL = Lay::KPL, PAIRS = Lay::PAIRS;
-  __shared__ __attribute__((aligned(1024))) char smem[kWaves * Lay::WAVE_LDS];
+  constexpr int ROWB = Ge::ROWB, NPOS = Ge::NPOS, CHB = Ge::CHB, NDMA = Ge::NDMA;
+  constexpr int STB = Ge::STB, KS = Ge::KS, DB = Ge::DB, MS = Ge::MS;
+  constexpr int KPL = Ge::KPL, PAIRS = Ge::PAIRS;
+  constexpr int WAVE_LDS = decode_wave_lds<D>(MULTI ? 0 : G, !MF);
+  constexpr int RC = MULTI ? 16 : G;   // rows per merge pass
+  __shared__ __attribute__((aligned(1024))) char smem[kWaves * WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -125,8 +140,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   const int g = blockIdx.x % a.num_kv_heads, b = blockIdx.x / a.num_kv_heads;
   const int split = blockIdx.y;
   const int Hq = a.num_q_heads;
+  const int QL = MULTI ? a.q_len : 1;
+  const int R = G * QL;                                   // query rows of this workgroup
   const int t0 = split * a.split_len;
-  const size_t head0 = (size_t)b * Hq + (size_t)g * G;  // first q head of the group
+  const size_t seq_row0 = (size_t)b * QL * Hq;            // first output row of the sequence
+  // output row of query row r (token r / G, head g G + r % G)
+  auto out_row = [&](int r) { return seq_row0 + (size_t)(r / G) * Hq + (size_t)g * G + r % G; };
   const int bs_shift = a.bs_shift;
   const int bs_mask = (1 << bs_shift) - 1;
   const int Wm1 = a.max_blocks_per_seq - 1;
@@ -146,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     // split 0; writing the output directly (one piece) this workgroup owns
     // the rows and writes zeros.  The merge never reads an empty piece.
     if (split == 0 && a.o_part == nullptr) {
-      for (int i = threadIdx.x; i < G * D; i += 256) a.out[head0 * D + i] = 0;
+      for (int i = threadIdx.x; i < R * D; i += 256) a.out[out_row(i / D) * D + i % D] = 0;
     }
     return;
   }
@@ -154,9 +173,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   const int nck = (t1 - t0 + kChunk - 1) / kChunk;
   const int n_my = nck > wave ? (nck - wave + kWaves - 1) / kWaves : 0;
 
-  char *my = smem + wave * Lay::WAVE_LDS;
+  constexpr int QB = MULTI ? 0 : (G * ROWB + 1023) / 1024 * 1024;
+  char *my = smem + wave * WAVE_LDS;
   char *qlds = my + NSTAGE * STB;
-  char *plds = qlds + Lay::QB;  // vector path only
+  char *plds = qlds + QB;  // vector path only
   const uint32_t my_off = lds_offset(my);
   const uint32_t q_off = lds_offset(qlds);
 
@@ -164,10 +184,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   const char *kbase = (const char *)a.k_cache + (size_t)g * ROWB;
   const char *vbase = (const char *)a.v_cache + (size_t)g * ROWB;
 
-  // Fused append: the wave that owns the sequence's last token writes the new
-  // K/V row of this kv head to that token's slot, and waits for the stores to
-  // complete before it issues any load of the chunk holding the row.  Only
-  // this wave reads that row in this launch.
+  // Fused append (single query token only): the wave that owns the
+  // sequence's last token writes the new K/V row of this kv head to that
+  // token's slot, and waits for the stores to complete before it issues any
+  // load of the chunk holding the row.  Only this wave reads that row in this
+  // launch.
   if (a.new_k != nullptr && t1 == L && wave == (nck - 1) % kWaves) {
     const int tl = L - 1;
     const size_t row = ((size_t)(uint32_t)table[tl >> bs_shift] << bs_shift) + (tl & bs_mask);
@@ -214,16 +235,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  // Softmax state and accumulators.  Matrix path: lane l holds head hh =
-  // l % 16 (m, partial l) and O^T[16 db + 4 qd + i][hh].  Vector path: every
-  // lane holds all G heads' m and partial l, and head_dim columns of acc.
+  // Softmax state and accumulators.  Matrix path: in tile t, lane l holds
+  // query row 16 t + l % 16 (m, partial l) and O^T[16 db + 4 qd + i][row].
+  // Vector path: every lane holds all G heads' m and partial l, and head_dim
+  // columns of acc.
   const int hh = lane & 15, qd = lane >> 4;
-  float m_mf = -INFINITY, l_mf = 0.f;
-  f32x4 o[MF ? DB : 1];
+  float m_mf[NT], l_mf[NT];
+  f32x4 o[MF ? NT : 1][MF ? DB : 1];
   float m_v[MF ? 1 : G], l_v[MF ? 1 : G], acc[MF ? 1 : G][2];
   if constexpr (MF) {
 #pragma unroll
-    for (int d = 0; d < DB; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) {
+      m_mf[t] = -INFINITY;
+      l_mf[t] = 0.f;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   } else {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -233,12 +260,29 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     }
   }
 
+  // Q^T fragments of the matrix path: query row 16 t + hh (zero past the
+  // last row), head_dim 32 kk + 8 qd .. + 7.
+  uint4 qf[MF ? NT : 1][MF ? KS : 1];
   if (n_my > 0) {
-    // q rows of the group -> LDS (clamped lanes re-read the last 16 bytes).
-    {
-      const char *qsrc = (const char *)a.q + head0 * ROWB;
+    if constexpr (MULTI) {
+      // straight to registers, issued before any DMA, so the first DMA wait
+      // below also covers them
 #pragma unroll
-      for (int j = 0; j < Lay::NQDMA; ++j) {
+      for (int t = 0; t < NT; ++t) {
+        const int col = 16 * t + hh;
+        const char *qrow = (const char *)a.q + out_row(min(col, R - 1)) * ROWB + qd * 16;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const uint4 v = *(const uint4 *)(qrow + kk * 64);
+          qf[t][kk] = col < R ? v : uint4{0u, 0u, 0u, 0u};
+        }
+      }
+    } else {
+      // the G query rows -> LDS: 16 bytes per lane (clamped lanes re-read the
+      // last 16 bytes)
+      const char *qsrc = (const char *)a.q + out_row(0) * ROWB;
+#pragma unroll
+      for (int j = 0; j < QB / 1024; ++j) {
         uint32_t off = (uint32_t)(j * 1024 + lane * 16);
         off = off < (uint32_t)(G * ROWB) ? off : (uint32_t)(G * ROWB - 16);
         dma16(q_off + j * 1024, qsrc, off);
@@ -264,54 +308,87 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
                                  (((2 * db + ((hh & 3) >> 1)) ^ row_swizzle<D, MF>(vr)) * 16) +
                                  (hh & 1) * 8);
       }
+      // Per tile: is this lane's column a query row, and the last key its
+      // query token may see (query token j sits at position L - q_len + j).
+      bool colv[NT];
+      int lim[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int col = 16 * t + hh;
+        colv[t] = col < R;
+        lim[t] = MULTI ? L - QL + col / G : L;
+      }
 
-      uint4 qf[KS];
       for (int i = 0; i < n_my; ++i) {
         wait_vmcnt_steps<2 * NDMA, NSTAGE - 1>(min(NSTAGE - 1, n_my - 1 - i));
-        if (i == 0) {
-          // Q^T fragments: head hh (zero for hh >= G), head_dim 32 kk + 8 qd ...
-          const char *qrow = qlds + min(hh, G - 1) * ROWB + qd * 16;
+        if constexpr (!MULTI) {
+          if (i == 0) {
+            const char *qrow = qlds + min(hh, G - 1) * ROWB + qd * 16;
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) {
-            const uint4 v = *(const uint4 *)(qrow + kk * 64);
-            qf[kk] = hh < G ? v : uint4{0u, 0u, 0u, 0u};
+            for (int kk = 0; kk < KS; ++kk) {
+              const uint4 v = *(const uint4 *)(qrow + kk * 64);
+              qf[0][kk] = colv[0] ? v : uint4{0u, 0u, 0u, 0u};
+            }
           }
         }
         const int ci = wave + kWaves * i;
         const int tc = t0 + ci * kChunk;
         const char *st = my + (i % NSTAGE) * STB;
 
-        // ---- S^T = K Q^T: lane holds head hh, tokens 4 qd + e ----
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        // ---- S^T = K Q^T: lane holds query row 16 t + hh, tokens 4 qd + e ----
+        f32x4 sc[NT];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          sc = mfma_k32(*(const uint4 *)(st + k_off[kk]), qf[kk], sc);
+        for (int t = 0; t < NT; ++t) sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const uint4 kf = *(const uint4 *)(st + k_off[kk]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) sc[t] = mfma_k32(kf, qf[t][kk], sc[t]);
+        }
 
         // ---- online softmax, lazily rescaled (see the file comment) ----
         const int tok = tc + 4 * qd;
-        float x[4];
+        float x[NT][4], cmax[NT];
+        bool grow = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = tok + e < t1 ? sc[e] * a.scale_log2 : -INFINITY;
-        const float cmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        if (__builtin_amdgcn_ballot_w64(hh < G && cmax > m_mf + kSlack) != 0) {
-          float mx = fmaxf(m_mf, cmax);
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float alpha = mx == -INFINITY ? 1.f : exp2_fast(m_mf - mx);
-          m_mf = mx;
-          l_mf *= alpha;
+        for (int t = 0; t < NT; ++t) {
 #pragma unroll
-          for (int d = 0; d < DB; ++d) o[d] *= alpha;
+          for (int e = 0; e < 4; ++e)
+            x[t][e] = (tok + e < t1 && (!MULTI || tok + e <= lim[t])) ? sc[t][e] * a.scale_log2
+                                                                      : -INFINITY;
+          cmax[t] = fmaxf(fmaxf(x[t][0], x[t][1]), fmaxf(x[t][2], x[t][3]));
+          grow |= colv[t] && cmax[t] > m_mf[t] + kSlack;
         }
-        const float mm = m_mf == -INFINITY ? 0.f : m_mf;
-        const uint32_t p01 = pack_bf16(exp2_fast(x[0] - mm), exp2_fast(x[1] - mm));
-        const uint32_t p23 = pack_bf16(exp2_fast(x[2] - mm), exp2_fast(x[3] - mm));
-        l_mf += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-        const uint2 pb = {p01, p23};
-
-        // ---- O^T += V^T P^T: lane holds head hh, head_dim 16 db + 4 qd + i ----
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma_k16(read_tr(st + v_off[db]), pb, o[db]);
+          for (int t = 0; t < NT; ++t) {
+            float mx = fmaxf(m_mf[t], cmax[t]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float alpha = mx == -INFINITY ? 1.f : exp2_fast(m_mf[t] - mx);
+            m_mf[t] = mx;
+            l_mf[t] *= alpha;
+#pragma unroll
+            for (int d = 0; d < DB; ++d) o[t][d] *= alpha;
+          }
+        }
+        uint2 pb[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float mm = m_mf[t] == -INFINITY ? 0.f : m_mf[t];
+          const uint32_t p01 = pack_bf16(exp2_fast(x[t][0] - mm), exp2_fast(x[t][1] - mm));
+          const uint32_t p23 = pack_bf16(exp2_fast(x[t][2] - mm), exp2_fast(x[t][3] - mm));
+          l_mf[t] += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+          pb[t] = uint2{p01, p23};
+        }
+
+        // ---- O^T += V^T P^T: lane holds query row 16 t + hh, head_dim 16 db + 4 qd + i ----
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint2 vf = read_tr(st + v_off[db]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) o[t][db] = mfma_k16(vf, pb[t], o[t][db]);
+        }
 
         if (i + NSTAGE < n_my) {
           const int cn = ci + kWaves * NSTAGE;
@@ -414,17 +491,85 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   }
 
   // ---- merge the 4 waves through LDS ----
-  float *mrg = (float *)my;  // [m: G][l: G] .. [O: G rows of MS floats from ACC0]
-  if constexpr (MF) {
-    l_mf += __shfl_xor(l_mf, 16);
-    l_mf += __shfl_xor(l_mf, 32);
-    if (hh < G) {
-      if (qd == 0) {
-        mrg[hh] = m_mf;
-        mrg[G + hh] = l_mf;
-      }
+  // Scratch per wave and pass: m[RC], l[RC], then from ACC0 one row of MS
+  // floats per query row of the pass.  Each thread then finishes column
+  // pairs of the pass's rows: all its LDS reads are issued before any
+  // arithmetic (one LDS round trip), and a clamped index keeps the reads of
+  // idle threads inside the table.
+  constexpr int ACC0 = (2 * RC + 3) & ~3;
+  constexpr int NIT = (RC * D / 2 + 255) / 256;
+  float *mrg = (float *)my;
+  const bool direct = a.o_part == nullptr;
+  auto finish_rows = [&](int row_base, int rows) {
+    const int npair = rows * D / 2;
+    float mw[NIT][kWaves], lw[NIT][kWaves];
+    float2 aw[NIT][kWaves];
 #pragma unroll
-      for (int d = 0; d < DB; ++d) *(f32x4 *)(mrg + ACC0 + hh * MS + 16 * d + 4 * qd) = o[d];
+    for (int k = 0; k < NIT; ++k) {
+      const int pi = min((int)threadIdx.x + 256 * k, npair - 1);
+      const int r = pi / (D / 2), c = 2 * (pi % (D / 2));
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float *wb = (const float *)(smem + w * WAVE_LDS);
+        mw[k][w] = wb[r];
+        lw[k][w] = wb[RC + r];
+        aw[k][w] = *(const float2 *)(wb + ACC0 + r * MS + c);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const int pi = (int)threadIdx.x + 256 * k;
+      if (pi >= npair) break;
+      const int r = pi / (D / 2), c = 2 * (pi % (D / 2));
+      float M = mw[k][0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[k][w]);
+      float den = 0.f, n0 = 0.f, n1 = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float e = exp2_fast(mw[k][w] - M);
+          den += e * lw[k][w];
+          n0 += e * aw[k][w].x;
+          n1 += e * aw[k][w].y;
+        }
+      }
+      // den is 0 only when no wave saw a key (an empty sequence, or a query
+      // token whose keys all lie in other pieces); a NaN read from the cache
+      // propagates to the output.
+      const float inv = den != 0.f ? 1.f / den : 0.f;
+      const size_t orow = out_row(row_base + r);
+      if (direct) {
+        *(uint32_t *)(a.out + orow * D + c) = pack_bf16(n0 * inv, n1 * inv);
+      } else {
+        const size_t row = orow * a.num_splits + split;
+        *(float2 *)(a.o_part + row * D + c) = float2{n0 * inv, n1 * inv};
+        if (c == 0) a.lse_part[row] = den != 0.f ? M + log2_fast(den) : -INFINITY;
+      }
+    }
+  };
+
+  if constexpr (MF) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      l_mf[t] += __shfl_xor(l_mf[t], 16);
+      l_mf[t] += __shfl_xor(l_mf[t], 32);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      // pass t: query rows 16 t .. 16 t + 15 (single token: the G heads)
+      const int rows = min(RC, R - 16 * t);
+      if (t > 0) __syncthreads();  // the previous pass has read the scratch
+      if (hh < rows) {
+        if (qd == 0) {
+          mrg[hh] = m_mf[t];
+          mrg[RC + hh] = l_mf[t];
+        }
+#pragma unroll
+        for (int d = 0; d < DB; ++d) *(f32x4 *)(mrg + ACC0 + hh * MS + 16 * d + 4 * qd) = o[t][d];
+      }
+      __syncthreads();
+      finish_rows(16 * t, rows);
     }
   } else {
     float lsum[G];
@@ -449,62 +594,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
       for (int h = 0; h < G; ++h)
         *(float2 *)(mrg + ACC0 + h * MS + 2 * dl) = float2{acc[h][0], acc[h][1]};
     }
-  }
-  __syncthreads();
-
-  // Each thread finishes column pairs of the G rows.  All LDS reads of a
-  // thread are issued before any arithmetic so the merge costs one LDS round
-  // trip; a clamped index keeps the reads of idle threads inside the table.
-  constexpr int NPAIR = G * D / 2;
-  constexpr int NIT = (NPAIR + 255) / 256;
-  float mw[NIT][kWaves], lw[NIT][kWaves];
-  float2 aw[NIT][kWaves];
-#pragma unroll
-  for (int k = 0; k < NIT; ++k) {
-    const int pi = min((int)threadIdx.x + 256 * k, NPAIR - 1);
-    const int h = pi / (D / 2), c = 2 * (pi % (D / 2));
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float *wb = (const float *)(smem + w * Lay::WAVE_LDS);
-      mw[k][w] = wb[h];
-      lw[k][w] = wb[G + h];
-      aw[k][w] = *(const float2 *)(wb + ACC0 + h * MS + c);
-    }
-  }
-  const bool direct = a.o_part == nullptr;
-#pragma unroll
-  for (int k = 0; k < NIT; ++k) {
-    const int pi = (int)threadIdx.x + 256 * k;
-    if (NPAIR % 256 != 0 && pi >= NPAIR) break;
-    const int h = pi / (D / 2), c = 2 * (pi % (D / 2));
-    float M = mw[k][0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[k][w]);
-    float den = 0.f, n0 = 0.f, n1 = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float e = exp2_fast(mw[k][w] - M);
-        den += e * lw[k][w];
-        n0 += e * aw[k][w].x;
-        n1 += e * aw[k][w].y;
-      }
-    }
-    // den is 0 only when no wave saw a token (empty sequence); a NaN read from
-    // the cache propagates to the output.
-    const float inv = den != 0.f ? 1.f / den : 0.f;
-    if (direct) {
-      *(uint32_t *)(a.out + (head0 + h) * D + c) = pack_bf16(n0 * inv, n1 * inv);
-    } else {
-      const size_t row = (head0 + h) * a.num_splits + split;
-      *(float2 *)(a.o_part + row * D + c) = float2{n0 * inv, n1 * inv};
-      if (c == 0) a.lse_part[row] = den != 0.f ? M + log2_fast(den) : -INFINITY;
-    }
+    __syncthreads();
+    finish_rows(0, G);
   }
 }
 
-// Merge the pieces of one (sequence, q head) row; one 256-thread workgroup
-// per row.  Thread t reads lse of piece t; the workgroup max and the weights
+// Merge the pieces of one (sequence, query token, q head) row; one 256-thread
+// workgroup per row.  Thread t reads lse of piece t; the workgroup max and the weights
 // 2^(lse_s - M) go through LDS.  For the weighted sum, thread t owns float4
 // column group t % (D/4) and pieces s = t / (D/4) (mod 256 / (D/4)).  Every
 // load of the first batch (pieces, lse and the context length) is issued at
@@ -519,10 +615,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float w_lds[256];
   __shared__ float red_max[4], red_sum[4];
   __shared__ float4 red[SG][NV];
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int h = blockIdx.x, b = blockIdx.y;  // h: (query token, q head) of the sequence
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int S = a.num_splits;
-  const size_t row = (size_t)b * a.num_q_heads + h;
+  const size_t row = (size_t)b * a.q_len * a.num_q_heads + h;
   const int v = tid % NV, sg = tid / NV;
   const float4 *op = (const float4 *)(a.o_part + row * (size_t)S * D) + v;
 
@@ -546,7 +642,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   if (lane == 0) red_max[wv] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
-  const float w = tid < ns ? exp2_fast(lse - M) : 0.f;
+  // M = -inf: no piece saw a key (a query token before position 0); the
+  // weights are then 0, or NaN for a NaN partial, which must propagate.
+  const float Mm = M == -INFINITY ? 0.f : M;
+  const float w = tid < ns ? exp2_fast(lse - Mm) : 0.f;
   w_lds[tid] = w;
   float ws = w;
   ws += dpp<0xB1>(ws);
@@ -585,7 +684,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     for (int k = 1; k < SG; ++k) {
       t.x += red[k][tid].x; t.y += red[k][tid].y; t.z += red[k][tid].z; t.w += red[k][tid].w;
     }
-    const float inv = 1.f / den;
+    const float inv = den != 0.f ? 1.f / den : 0.f;
     uint2 pk;
     pk.x = pack_bf16(t.x * inv, t.y * inv);
     pk.y = pack_bf16(t.z * inv, t.w * inv);
@@ -593,11 +692,31 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
 }
 
+template <int D, int G, bool MF, int NT, bool MULTI>
+hipError_t launch_split_variant(const DecodeArgs &a, int num_seqs, hipStream_t stream) {
+  dim3 grid(num_seqs * a.num_kv_heads, a.num_splits);
+  hipLaunchKernelGGL((decode_split_kernel<D, G, MF, NT, MULTI>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Path choice: one query token with a group of at most kMaxVectorGroup heads
+// takes the vector path, other single-token groups the matrix path with one
+// tile; several query tokens take the matrix path with one tile per 16 rows.
 template <int D, int G>
 hipError_t launch_split_dg(const DecodeArgs &a, int num_seqs, hipStream_t stream) {
-  dim3 grid(num_seqs * a.num_kv_heads, a.num_splits);
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
+  if (a.q_len == 1) {
+    if constexpr (G <= kMaxVectorGroup)
+      return launch_split_variant<D, G, false, 1, false>(a, num_seqs, stream);
+    else
+      return launch_split_variant<D, G, true, 1, false>(a, num_seqs, stream);
+  }
+  const int rows = G * a.q_len;
+  if (rows <= 16) return launch_split_variant<D, G, true, 1, true>(a, num_seqs, stream);
+  if constexpr (G * kMaxQueryTokens > 16) {
+    if (rows <= kMaxDecodeRows)
+      return launch_split_variant<D, G, true, 2, true>(a, num_seqs, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D>
@@ -626,7 +745,7 @@ hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, int group, int
 
 hipError_t launch_decode_combine(const DecodeArgs &a, int head_dim, int num_seqs,
                                  hipStream_t stream) {
-  dim3 grid(a.num_q_heads, num_seqs);
+  dim3 grid(a.num_q_heads * a.q_len, num_seqs);
   if (head_dim == 128)
     hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(256), 0, stream, a);
   else if (head_dim == 64)

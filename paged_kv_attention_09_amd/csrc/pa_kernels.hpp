@@ -16,21 +16,22 @@ struct AppendArgs {
 };
 
 struct DecodeArgs {
-  const uint16_t *q;          // [B, Hq, D]
+  const uint16_t *q;          // [B, q_len, Hq, D]
   const uint16_t *k_cache;    // [NB, bs, Hkv, D]
   const uint16_t *v_cache;
   const int32_t *block_tables;  // [B, W]
-  const int32_t *context_lens;  // [B]
-  const uint16_t *new_k;      // [B, Hkv, D] rows appended at token L_b - 1, or null
+  const int32_t *context_lens;  // [B], including the q_len query tokens
+  const uint16_t *new_k;      // [B, Hkv, D] rows appended at token L_b - 1, or null (q_len 1)
   const uint16_t *new_v;
-  uint16_t *out;              // [B, Hq, D]        (num_splits == 1)
-  float *o_part;              // [B, Hq, S, D]     (num_splits > 1)
-  float *lse_part;            // [B, Hq, S], base-2 log-sum-exp of scaled scores
+  uint16_t *out;              // [B, q_len, Hq, D]        (num_splits == 1)
+  float *o_part;              // [B, q_len, Hq, S, D]     (num_splits > 1)
+  float *lse_part;            // [B, q_len, Hq, S], base-2 log-sum-exp of scaled scores
   float scale_log2;           // scale * log2(e)
   int num_q_heads, num_kv_heads, max_blocks_per_seq;
   int bs_shift;               // log2(block_size)
   int split_len;              // tokens per split, multiple of 64
   int num_splits;
+  int q_len;                  // query tokens per sequence (1 = single-token decode)
 };
 
 struct PrefillArgs {
@@ -50,7 +51,10 @@ struct PrefillArgs {
 };
 
 hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t stream);
-// Returns hipErrorInvalidValue for an unsupported (head_dim, group).
+// Returns hipErrorInvalidValue for an unsupported (head_dim, group, q_len):
+// group * q_len must not exceed kMaxDecodeRows.
+constexpr int kMaxDecodeRows = 32;
+constexpr int kMaxQueryTokens = 8;
 hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, int group, int num_seqs,
                                hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs &a, int head_dim, int num_seqs,

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -55,6 +55,36 @@ def _decode(**kw):
 ])
 def test_decode_argument_checks(kw, code):
     assert _decode(**kw) == code
+
+
+def _multi(**kw):
+    a = dict(q=P, k=P, v=P, tables=P, lens=P, scale=0.1, S=1, out=P, B=2, QL=4, Hq=28, Hkv=4,
+             D=128, bs=256, NB=100, W=16, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return pa.lib().pa_decode_multi(a["q"], a["k"], a["v"], a["tables"], a["lens"], a["scale"],
+                                    a["S"], a["out"], a["B"], a["QL"], a["Hq"], a["Hkv"], a["D"],
+                                    a["bs"], a["NB"], a["W"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(QL=0), SHAPE), (dict(QL=9), SHAPE), (dict(QL=-1), SHAPE),
+    (dict(Hq=32, Hkv=4, QL=5), UNSUP),            # 8 heads x 5 tokens > 32 rows
+    (dict(Hq=32, Hkv=4, QL=4, B=0), OK),         # 32 rows: supported
+    (dict(Hq=28, Hkv=4, QL=5, B=0), UNSUP),       # 35 rows, even with nothing to do
+    (dict(D=96), UNSUP), (dict(bs=32), UNSUP), (dict(S=300), SPLITS), (dict(out=None), NULL),
+    (dict(q=None), NULL), (dict(S=4), WS), (dict(S=4, ws=P, wsb=1000), WS), (dict(B=0), OK),
+])
+def test_decode_multi_argument_checks(kw, code):
+    assert _multi(**kw) == code
+
+
+def test_decode_multi_workspace_size():
+    ws = pa.lib().pa_decode_multi_workspace_size
+    rows = 8 * 4 * 28 * 16
+    want = (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    assert ws(8, 4, 28, 128, 16) == want
+    assert ws(8, 1, 28, 128, 16) == pa.lib().pa_decode_workspace_size(8, 28, 128, 16)
+    assert ws(8, 0, 28, 128, 16) == 0 and ws(8, 4, 28, 128, 1) == 0
 
 
 def test_partials_and_merge_argument_checks():
@@ -126,9 +156,10 @@ def test_plan_splits():
     plan = pa.lib().pa_decode_plan_splits
     # many (sequence, kv head) units already fill the device: one piece each
     assert plan(256, 8, 5, 256, 256) == 1
-    # few units: enough pieces for ~2 workgroups per compute unit, 64-token multiples
-    s = plan(8, 2, 256, 16, 256)
-    assert 16 <= s <= 64
+    # few units: about one workgroup per compute unit, 64-token multiples
+    assert plan(8, 2, 256, 16, 256) == 16        # 16 units x 16 pieces of 256 tokens
+    assert plan(8, 4, 16, 256, 256) == 8         # 32 units x 8 pieces of 512 tokens
+    assert plan(64, 4, 16, 256, 256) == 1        # 256 units fill 256 compute units
     assert plan(1, 2, 256, 16, 256) == 64        # pieces cannot go below 64 tokens
     for args in [(4, 1, 16, 16, 256), (8, 4, 16, 256, 256), (64, 4, 16, 256, 256)]:
         s = plan(*args)
