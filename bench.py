@@ -396,6 +396,36 @@ def time_kernel_events(fn, n: int, rotations: int):
     return s.elapsed_time(e) / n
 
 
+def time_steps_eager(wl, steps: int, warmup: int) -> float:
+    """The fused append + decode step launched from the host every time (no
+    graph), through the raw C function with prebuilt ctypes arguments so the
+    binding's Python checks are not timed.  Returns milliseconds per step
+    (HIP events around the loop) and the host's issue time per call."""
+    import ctypes
+    import torch
+    f = wl.pa.lib().pa_append_decode
+    sp = torch.cuda.current_stream().cuda_stream
+    B, Hq, D = (int(x) for x in wl.q.shape)
+    NB, bs, Hkv, _ = (int(x) for x in wl.k_cache.shape)
+    W_ = int(wl.tables[0].shape[1])
+    args = [(wl.q.data_ptr(), wl.new_k.data_ptr(), wl.new_v.data_ptr(), wl.k_cache.data_ptr(),
+             wl.v_cache.data_ptr(), t.data_ptr(), wl.lens.data_ptr(), ctypes.c_float(wl.scale),
+             wl.S, wl.out.data_ptr(), B, Hq, Hkv, D, bs, NB, W_, wl.ws.data_ptr(),
+             wl.ws.numel(), sp) for t in wl.tables]
+    for i in range(warmup):
+        assert f(*args[i % wl.R]) == 0
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        f(*args[i % wl.R])
+    host = time.perf_counter() - t0
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps, host * 1e3 / steps
+
+
 def time_steps_graph(wl, steps: int, warmup: int, fused: bool = True):
     """Warm up eagerly, capture `steps` steps in one graph, replay it between events."""
     import torch
@@ -633,6 +663,10 @@ def measure(name, args, steps, warmup, with_kernel=True):
            "context_tokens": int(wl.lens_np.sum())}
     ms_unfused, _ = time_steps_graph(wl, steps, 2, fused=False)
     rec["unfused_us_per_step"] = ms_unfused * 1e3
+    ms_eager, ms_host = time_steps_eager(wl, steps, warmup)
+    rec["eager_us_per_step"] = ms_eager * 1e3
+    rec["host_issue_us_per_call"] = ms_host * 1e3
+    rec["graph_saving"] = 1.0 - ms_step / ms_eager
     if with_kernel:
         avg = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
         rec["kernel_avg_us"] = avg * 1e3
@@ -753,8 +787,10 @@ def main(argv=None):
     print(f"[bench] {args.workload}: building inputs", file=sys.stderr, flush=True)
     wl, main_rec = measure(args.workload, args, args.steps, args.warmup)
     print(f"[bench] {args.workload}: {main_rec['us_per_call']:.2f} us/step, "
-          f"{main_rec['gbps']:.1f} GB/s; kernel {main_rec['kernel_avg_us']:.2f} us",
-          file=sys.stderr, flush=True)
+          f"{main_rec['gbps']:.1f} GB/s; kernel {main_rec['kernel_avg_us']:.2f} us; eager "
+          f"{main_rec['eager_us_per_step']:.2f} us (graph saves "
+          f"{100 * main_rec['graph_saving']:.0f}%, host issue "
+          f"{main_rec['host_issue_us_per_call']:.2f} us/call)", file=sys.stderr, flush=True)
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         del wl
@@ -774,7 +810,9 @@ def main(argv=None):
         else:
             wl, rec = measure(name, args, min(args.steps, 100), min(args.warmup, 10))
             msg = (f"{rec['us_per_call']:.2f} us/step, {rec['gbps']:.1f} GB/s; "
-                   f"kernel {rec['kernel_avg_us']:.2f} us ({rec['kernel_gbps']:.0f} GB/s)")
+                   f"kernel {rec['kernel_avg_us']:.2f} us ({rec['kernel_gbps']:.0f} GB/s); "
+                   f"eager {rec['eager_us_per_step']:.2f} us (graph saves "
+                   f"{100 * rec['graph_saving']:.0f}%)")
         others[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rec.items()
                         if k not in ("wall_s",)}
         print(f"[bench] {name}: {msg}", file=sys.stderr, flush=True)
@@ -803,6 +841,8 @@ def main(argv=None):
                    "context_tokens": main_rec["context_tokens"], "num_splits": main_rec["splits"],
                    "rotations": main_rec["rotations"], "step": "append fused into split-KV decode, then merge",
                    "unfused_us_per_step": round(main_rec["unfused_us_per_step"], 3),
+                   "eager_us_per_step": round(main_rec["eager_us_per_step"], 3),
+                   "host_issue_us_per_call": round(main_rec["host_issue_us_per_call"], 3),
                    "timing": "HIP graph of the timed steps between HIP events; kernel: HIP "
                              "events around back-to-back launches behind a primed queue"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
