@@ -674,6 +674,47 @@ def measure(name, args, steps, warmup, with_kernel=True):
     return wl, rec
 
 
+def measure_block_manager(seed: int = 77):
+    """Host cost of the native block manager on the 256-sequence pool shape
+    (17166 blocks of 256 tokens, 5 blocks per sequence): admission of 256
+    prompts that share a 512-token system prompt, then decode steps (one
+    token for every sequence, pa_bm_decode_step) and the 256 block-table rows
+    each step feeds to the kernels.  Microseconds per call, median of 200."""
+    import statistics
+    import numpy as np
+    import paged_kv_attention_09_amd as pa
+    import workloads as W
+    rng = np.random.default_rng(seed)
+    bm = pa.BlockManager(W.C4_NUM_BLOCKS, 256, 5, prefix_cache=True)
+    system = rng.integers(0, 32000, 512).astype(np.int32)
+    ids = np.arange(1, 257, dtype=np.int64)
+    t_admit, cached = [], 0
+    for k in ids:
+        prompt = np.concatenate([system, rng.integers(0, 32000, int(rng.integers(1, 512)))])
+        t0 = time.perf_counter()
+        c, _ = bm.admit(int(k), 0, prompt)
+        t_admit.append(time.perf_counter() - t0)
+        cached += c
+        if k == 1:
+            bm.decode_step(ids[:1], np.zeros(1, np.int32))   # the system prompt becomes shareable
+    t_step, t_tab = [], []
+    for _ in range(200):
+        toks = rng.integers(0, 32000, 256).astype(np.int32)
+        t0 = time.perf_counter()
+        bm.decode_step(ids, toks)
+        t1 = time.perf_counter()
+        bm.block_tables(ids)
+        t2 = time.perf_counter()
+        t_step.append(t1 - t0)
+        t_tab.append(t2 - t1)
+    free, cached_b, used, running = bm.stats()
+    return {"admit_us": round(statistics.median(t_admit) * 1e6, 2),
+            "decode_step_us_256_seqs": round(statistics.median(t_step) * 1e6, 2),
+            "block_tables_us_256_seqs": round(statistics.median(t_tab) * 1e6, 2),
+            "prefix_cached_tokens": int(cached), "used_blocks": used,
+            "note": "host time through the Python binding (one ctypes call per operation)"}
+
+
 MULTI_WORKLOADS = {"c2b8q2": ("c2b8", 2), "c2b8q4": ("c2b8", 4), "c3q4": ("c3", 4)}
 
 
@@ -816,6 +857,13 @@ def main(argv=None):
         others[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rec.items()
                         if k not in ("wall_s",)}
         print(f"[bench] {name}: {msg}", file=sys.stderr, flush=True)
+
+    bm_rec = measure_block_manager()
+    print(f"[bench] block manager: decode step {bm_rec['decode_step_us_256_seqs']:.1f} us, "
+          f"tables {bm_rec['block_tables_us_256_seqs']:.1f} us for 256 sequences; admit "
+          f"{bm_rec['admit_us']:.1f} us; {bm_rec['prefix_cached_tokens']} prompt tokens from the "
+          "prefix cache", file=sys.stderr, flush=True)
+    others["host_block_manager"] = bm_rec
 
     spec = W.CONFIGS[args.workload]
     achieved = main_rec["kernel_gbps"]

@@ -57,7 +57,10 @@ enum {
   PA_ERR_UNSUPPORTED = -3, /* head_dim / block_size / group not supported     */
   PA_ERR_SPLITS = -4,      /* num_splits outside [0, PA_MAX_SPLITS]           */
   PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required      */
-  PA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed      */
+  PA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed      */
+  PA_ERR_NO_BLOCKS = -7,   /* block manager: the pool cannot supply the blocks */
+  PA_ERR_STATE = -8        /* block manager: unknown/duplicate sequence, or a
+                              forbidden state change                          */
 };
 
 #define PA_MAX_SPLITS 256

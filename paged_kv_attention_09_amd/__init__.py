@@ -21,6 +21,8 @@ Calls (argument order as in the C ABI):
   decode_multi_workspace_size(num_seqs, q_len, num_q_heads, head_dim, num_splits)
   plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus)
   auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, device=None)
+  BlockManager(num_blocks, block_size, max_blocks_per_seq, prefix_cache): the host-side
+      pool manager (admit / append / truncate / release / preempt / block_tables / stats)
 """
 from __future__ import annotations
 
@@ -60,6 +62,17 @@ SIGNATURES = {
                         _I, _VP, _SZ, _VP]),
     "pa_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "pa_prefill_plan_splits": (_I, [_I, _I, _I, _I, _I, _I]),
+    # host-side block manager (include/pa_block_manager.h)
+    "pa_bm_create": (_VP, [_I64, _I, _I, _I]),
+    "pa_bm_destroy": (None, [_VP]),
+    "pa_bm_admit": (_I, [_VP, _I64, _I, _VP, _I64, _VP, _VP]),
+    "pa_bm_append": (_I, [_VP, _I64, _VP, _I64, _VP]),
+    "pa_bm_decode_step": (_I, [_VP, _VP, _I, _VP, _VP]),
+    "pa_bm_truncate": (_I, [_VP, _I64, _I64]),
+    "pa_bm_release": (_I, [_VP, _I64]),
+    "pa_bm_preempt": (_I, [_VP, _VP]),
+    "pa_bm_block_tables": (_I, [_VP, _VP, _I, _VP, _VP]),
+    "pa_bm_stats": (_I, [_VP, _VP, _VP, _VP, _VP]),
 }
 
 _lib = None
@@ -365,3 +378,91 @@ def prefill_auto_splits(num_seqs, max_q_len, num_kv_heads, max_blocks_per_seq, b
 __all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "decode_merge", "prefill",
            "prefill_workspace_size", "prefill_auto_splits", "decode_workspace_size", "plan_splits",
            "auto_splits", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError", "PA_MAX_SPLITS"]
+
+
+class BlockManager:
+    """The library's host-side KV pool manager (include/pa_block_manager.h):
+    slots for pa_reshape_and_cache and block tables for the decode and prefill
+    calls.  Token ids and results are numpy arrays in host memory.  Errors
+    raise PagedAttnError with the status code."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_blocks_per_seq: int,
+                 prefix_cache: bool = True):
+        import numpy as np
+        self._np = np
+        self.block_size, self.max_blocks_per_seq = block_size, max_blocks_per_seq
+        h = lib().pa_bm_create(num_blocks, block_size, max_blocks_per_seq, int(bool(prefix_cache)))
+        if not h:
+            raise ValueError("pa_bm_create refused its arguments")
+        self._h = ctypes.c_void_p(h)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.pa_bm_destroy(h)
+            self._h = None
+
+    def _tok(self, tokens):
+        t = self._np.ascontiguousarray(tokens, dtype=self._np.int32)
+        return t, t.ctypes.data_as(ctypes.c_void_p)
+
+    def admit(self, seq_id: int, priority: int, tokens):
+        """Returns (num_cached_tokens, slots of the uncached prompt tokens)."""
+        t, tp = self._tok(tokens)
+        slots = self._np.empty(max(len(t), 1), dtype=self._np.int64)
+        cached = ctypes.c_int64(0)
+        _check("pa_bm_admit", lib().pa_bm_admit(self._h, seq_id, priority, tp, len(t),
+                                                ctypes.byref(cached),
+                                                slots.ctypes.data_as(ctypes.c_void_p)))
+        return int(cached.value), slots[:len(t) - cached.value]
+
+    def append(self, seq_id: int, tokens):
+        """Returns the slots of the new tokens."""
+        t, tp = self._tok(tokens)
+        slots = self._np.empty(max(len(t), 1), dtype=self._np.int64)
+        _check("pa_bm_append", lib().pa_bm_append(self._h, seq_id, tp, len(t),
+                                                  slots.ctypes.data_as(ctypes.c_void_p)))
+        return slots[:len(t)]
+
+    def decode_step(self, seq_ids, tokens=None):
+        """One token per listed sequence (all or nothing); returns the slots."""
+        ids = self._np.ascontiguousarray(seq_ids, dtype=self._np.int64)
+        n = len(ids)
+        slots = self._np.empty(max(n, 1), dtype=self._np.int64)
+        tp = None
+        if tokens is not None:
+            t, tp = self._tok(tokens)
+            if len(t) != n:
+                raise ValueError("one token per sequence")
+        _check("pa_bm_decode_step", lib().pa_bm_decode_step(
+            self._h, ids.ctypes.data_as(ctypes.c_void_p), n, tp,
+            slots.ctypes.data_as(ctypes.c_void_p)))
+        return slots[:n]
+
+    def truncate(self, seq_id: int, new_len: int) -> None:
+        _check("pa_bm_truncate", lib().pa_bm_truncate(self._h, seq_id, new_len))
+
+    def release(self, seq_id: int) -> None:
+        _check("pa_bm_release", lib().pa_bm_release(self._h, seq_id))
+
+    def preempt(self) -> int:
+        v = ctypes.c_int64(0)
+        _check("pa_bm_preempt", lib().pa_bm_preempt(self._h, ctypes.byref(v)))
+        return int(v.value)
+
+    def block_tables(self, seq_ids):
+        """Returns (tables int32 [n, max_blocks_per_seq], lens int32 [n])."""
+        ids = self._np.ascontiguousarray(seq_ids, dtype=self._np.int64)
+        n = len(ids)
+        tables = self._np.zeros((n, self.max_blocks_per_seq), dtype=self._np.int32)
+        lens = self._np.zeros(n, dtype=self._np.int32)
+        _check("pa_bm_block_tables", lib().pa_bm_block_tables(
+            self._h, ids.ctypes.data_as(ctypes.c_void_p), n,
+            tables.ctypes.data_as(ctypes.c_void_p), lens.ctypes.data_as(ctypes.c_void_p)))
+        return tables, lens
+
+    def stats(self):
+        """(free, cached, used) blocks and the number of running sequences."""
+        v = [ctypes.c_int64(0) for _ in range(4)]
+        _check("pa_bm_stats", lib().pa_bm_stats(self._h, *[ctypes.byref(x) for x in v]))
+        return tuple(int(x.value) for x in v)

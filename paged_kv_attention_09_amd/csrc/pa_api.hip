@@ -82,6 +82,8 @@ const char *pa_status_string(int status) {
     case PA_ERR_SPLITS: return "PA_ERR_SPLITS: num_splits outside [0, PA_MAX_SPLITS]";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP call or kernel launch failed";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: the KV pool cannot supply the blocks";
+    case PA_ERR_STATE: return "PA_ERR_STATE: unknown or duplicate sequence, or forbidden change";
     default: return "unknown pagedattn status";
   }
 }

@@ -1,0 +1,400 @@
+"""The host-side block manager (no GPU).
+
+1. Its plain model (oracle/block_manager.py) is pinned by invariants and
+   worked scenarios, and copies of the model with planted slips are rejected.
+2. The library's native manager equals the model status for status and slot
+   for slot over random operation sequences (integer work: exact).
+3. A paged layout built by the native manager, prefix sharing included,
+   gives the oracle's attention the same result as contiguous K/V.
+"""
+import inspect
+import itertools
+import types
+from collections import Counter
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.block_manager as real_model
+import paged_kv_attention_09_amd as pa
+import workloads as W
+
+OK, NULL, SHAPE, NO_BLOCKS, STATE = 0, -1, -2, -7, -8
+
+
+# --------------------------------------------------------------------------
+# invariants and pins of the model (each takes the model module, so that
+# planted slips can be run through the same pins)
+# --------------------------------------------------------------------------
+
+def check_invariants(m):
+    free, cached, used, running = m.stats()
+    assert free + cached + used == m.nb
+    assert running == len(m.seqs)
+    holders = Counter(b for s in m.seqs.values() for b in s["blocks"])
+    for b in range(m.nb):
+        assert m.ref[b] == holders.get(b, 0)
+        assert (b in m.free) + (b in m.lru) + (m.ref[b] > 0) == 1
+    for s in m.seqs.values():
+        assert len(s["blocks"]) == -(-s["len"] // m.bs)
+    # a block held by two sequences sits at the same table index under the
+    # same token prefix
+    for (_, a), (_, c) in itertools.combinations(m.seqs.items(), 2):
+        for i, b in enumerate(a["blocks"]):
+            if b in c["blocks"]:
+                assert m.prefix
+                j = c["blocks"].index(b)
+                assert i == j
+                assert a["tokens"][:(i + 1) * m.bs] == c["tokens"][:(i + 1) * m.bs]
+
+
+def pin_smallest_ids(M):
+    m = M.BlockManager(10, 4, 8, True)
+    st, cached, slots = m.admit(1, 0, list(range(9)))
+    assert st == OK and cached == 0 and slots == list(range(9))
+    st, slots = m.append(1, [50, 51, 52, 53])
+    assert slots == [9, 10, 11, 12]
+    check_invariants(m)
+
+
+def pin_cached_prefix(M):
+    bs = 4
+    m = M.BlockManager(40, bs, 16, True)
+    prompt = list(range(100, 100 + 5 * bs + 3))
+    assert m.admit(1, 0, prompt)[0] == OK
+    assert m.append(1, [7])[0] == OK                # the prompt's full blocks become shareable
+    assert m.release(1) == OK
+    st, cached, slots = m.admit(2, 0, prompt)
+    assert st == OK and cached == 5 * bs and len(slots) == 3
+    # a prompt ending exactly on a block boundary: its last block is computed
+    st, cached, _ = m.admit(3, 0, prompt[:5 * bs])
+    assert st == OK and cached == 4 * bs
+    check_invariants(m)
+
+
+def pin_lru_eviction(M):
+    bs = 2
+    m = M.BlockManager(7, bs, 8, True)
+    A = [1, 2, 3, 4, 5]                             # 2 full blocks + 1
+    B = [6, 7, 8, 9, 10]
+    for k, p in ((1, A), (2, B)):
+        assert m.admit(k, 0, p)[0] == OK
+        assert m.append(k, [0])[0] == OK
+        assert m.release(k) == OK
+    # prompt + one appended token = 3 full blocks each, all cached on release
+    assert len(m.lru) == 6 and len(m.free) == 1
+    # 4 blocks: the free one, then the three released longest ago (A's)
+    assert m.admit(3, 0, list(range(20, 28)))[0] == OK
+    assert m.admit(5, 0, B)[1] == 2 * bs            # B is still cached
+    assert m.release(3) == OK
+    assert m.admit(4, 0, A)[1] == 0                 # A's chain is gone
+    check_invariants(m)
+
+
+def pin_preemption(M):
+    m = M.BlockManager(20, 4, 8, False)
+    for k, prio in ((1, 5), (2, 1), (3, 9), (4, 1), (5, 3)):
+        assert m.admit(k, prio, [0] * 6)[0] == OK
+    assert m.preempt() == (OK, 4)                   # lowest priority, most recently admitted
+    assert m.preempt() == (OK, 2)
+    assert m.preempt() == (OK, 5)
+    assert m.preempt() == (OK, 1)
+    assert m.preempt() == (OK, 3)
+    assert m.preempt()[0] == STATE
+    check_invariants(m)
+
+
+def pin_refusal_changes_nothing(M):
+    m = M.BlockManager(5, 4, 8, True)
+    assert m.admit(1, 0, list(range(12)))[0] == OK  # 3 blocks
+    before = (m.stats(), m.block_tables([1]))
+    assert m.admit(2, 0, list(range(50, 62)))[0] == NO_BLOCKS
+    assert m.append(1, list(range(9)))[0] == NO_BLOCKS
+    assert (m.stats(), m.block_tables([1])) == before
+    assert m.admit(1, 0, [1])[0] == STATE
+    assert m.append(9, [1])[0] == STATE
+    check_invariants(m)
+
+
+def pin_rollback_reuses_slots(M):
+    m = M.BlockManager(20, 4, 8, True)
+    assert m.admit(1, 0, list(range(6)))[0] == OK
+    st, draft = m.append(1, [7, 8, 9, 10])          # a 4-token draft across a block boundary
+    assert st == OK
+    assert m.truncate(1, 7) == OK                   # one draft token accepted
+    st, again = m.append(1, [11, 12, 13])
+    assert st == OK and again == draft[1:]
+    check_invariants(m)
+
+
+def pin_sharing(M):
+    bs = 4
+    m = M.BlockManager(30, bs, 8, True)
+    prompt = list(range(2 * bs + 2))
+    assert m.admit(1, 0, prompt)[0] == OK
+    assert m.append(1, [99])[0] == OK
+    st, cached, _ = m.admit(2, 0, prompt)
+    assert st == OK and cached == 2 * bs
+    t = m.block_tables([1, 2])[1]
+    assert t[0][:2] == t[1][:2] and t[0][2] != t[1][2]
+    check_invariants(m)
+    assert m.release(1) == OK
+    check_invariants(m)
+    # rolling back into a shared block is refused
+    assert m.admit(3, 0, prompt)[1] == 2 * bs
+    assert m.truncate(3, bs - 1) == STATE
+    check_invariants(m)
+
+
+def pin_no_sharing_when_off(M):
+    m = M.BlockManager(30, 4, 8, False)
+    assert m.admit(1, 0, list(range(10)))[0] == OK
+    assert m.append(1, [1])[0] == OK
+    assert m.release(1) == OK
+    assert m.admit(2, 0, list(range(10)))[1] == 0
+    check_invariants(m)
+
+
+def pin_prefix_identity(M):
+    """A block is shared only under the same whole prefix, not the same
+    block of tokens after a different prefix."""
+    bs = 2
+    m = M.BlockManager(30, bs, 8, True)
+    X, X2, Y = [1, 2], [3, 4], [5, 6]
+    for k, p in ((1, X + Y + [9]), (2, X2 + Y + [9])):
+        assert m.admit(k, 0, p)[0] == OK
+        assert m.append(k, [0])[0] == OK
+    st, cached, _ = m.admit(3, 0, X2 + Y + [7])
+    assert st == OK and cached == 2 * bs
+    t = m.block_tables([1, 2, 3])[1]
+    assert t[2][:2] == t[1][:2] and t[2][1] != t[0][1]
+    check_invariants(m)
+
+
+def pin_rollback_forgets_partial_block(M):
+    bs = 4
+    m = M.BlockManager(30, bs, 8, True)
+    p = list(range(2 * bs + 1))
+    assert m.admit(1, 0, p)[0] == OK
+    assert m.append(1, [77])[0] == OK               # blocks 0, 1 shareable
+    assert m.truncate(1, bs + 1) == OK              # block 1 is partial again
+    assert m.admit(2, 0, p)[1] == bs
+    check_invariants(m)
+
+
+PINS = [pin_smallest_ids, pin_cached_prefix, pin_lru_eviction, pin_preemption,
+        pin_refusal_changes_nothing, pin_rollback_reuses_slots, pin_sharing,
+        pin_no_sharing_when_off, pin_prefix_identity, pin_rollback_forgets_partial_block]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_model_pin(pin):
+    pin(real_model)
+
+
+MUTANTS = {
+    "largest_free_id": ("b = min(self.free)", "b = max(self.free)"),
+    "evict_most_recent": ("b = self.lru.pop(0)", "b = self.lru.pop()"),
+    "cache_last_prompt_block": ("for i in range((n - 1) // self.bs):",
+                                "for i in range(n // self.bs):"),
+    "preempt_oldest": ('-self.seqs[k]["order"]', 'self.seqs[k]["order"]'),
+    "key_without_prefix": ("key = (parent, tuple(tokens[i * self.bs:(i + 1) * self.bs]))",
+                           "key = (0, tuple(tokens[i * self.bs:(i + 1) * self.bs]))"),
+    "rollback_keeps_key": ("            self._forget(s[\"blocks\"][keep - 1])\n", "            pass\n"),
+    "release_frees_cached": ("            if self.content[b] is not None:\n                self.lru.append(b)",
+                             "            if False:\n                self.lru.append(b)"),
+}
+
+
+def _mutant(old, new):
+    src = inspect.getsource(real_model)
+    assert src.count(old) == 1, f"anchor not unique/found: {old!r}"
+    mod = types.ModuleType("bm_mutant")
+    exec(compile(src.replace(old, new), "bm_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_model_mutant(name):
+    mod = _mutant(*MUTANTS[name])
+    caught = []
+    for pin in PINS:
+        try:
+            pin(mod)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin rejects {name}"
+
+
+# --------------------------------------------------------------------------
+# native manager == model
+# --------------------------------------------------------------------------
+
+def _status(fn, *a):
+    try:
+        return OK, fn(*a)
+    except pa.PagedAttnError as e:
+        return e.status, None
+
+
+def _lockstep(seed, num_blocks, bs, maxb, prefix, n_ops):
+    rng = np.random.default_rng(seed)
+    model = real_model.BlockManager(num_blocks, bs, maxb, prefix)
+    native = pa.BlockManager(num_blocks, bs, maxb, prefix)
+    canon = [[int(x) for x in rng.integers(0, 50, bs)] for _ in range(4)]
+    next_id = 1
+    counts = Counter()
+    for _ in range(n_ops):
+        ids = sorted(model.seqs)
+        op = str(rng.choice(["admit", "admit", "append", "append", "truncate", "release",
+                             "preempt", "tables", "step"]))
+        counts[op] += 1
+        if op == "admit":
+            if ids and rng.random() < 0.1:
+                k = int(rng.choice(ids))                   # duplicate id: refused
+            else:
+                k, next_id = next_id, next_id + 1
+            head = [t for c in rng.integers(0, 4, int(rng.integers(0, 4))) for t in canon[c]]
+            tail = [int(x) for x in rng.integers(0, 50, int(rng.integers(0, 3 * bs)))]
+            prompt = head + tail or [1]
+            prio = int(rng.integers(0, 4))
+            st_m, cached_m, slots_m = model.admit(k, prio, prompt)
+            st_n, out = _status(native.admit, k, prio, prompt)
+            assert st_m == st_n, ("admit", st_m, st_n)
+            if st_m == OK:
+                counts["admitted"] += 1
+                counts["cached_tokens"] += cached_m
+                assert out[0] == cached_m and list(out[1]) == slots_m
+            elif st_m == NO_BLOCKS:
+                counts["refused"] += 1
+        elif op == "append" and ids:
+            k = int(rng.choice(ids))
+            toks = [int(x) for x in rng.integers(0, 50, int(rng.integers(1, 5)))]
+            st_m, slots_m = model.append(k, toks)
+            st_n, out = _status(native.append, k, toks)
+            assert st_m == st_n, ("append", st_m, st_n)
+            if st_m == OK:
+                assert list(out) == slots_m
+        elif op == "truncate" and ids:
+            k = int(rng.choice(ids))
+            L = model.seqs[k]["len"]
+            new_len = int(rng.integers(max(1, L - 5), L + 1))
+            st_m = model.truncate(k, new_len)
+            st_n, _ = _status(native.truncate, k, new_len)
+            assert st_m == st_n, ("truncate", st_m, st_n)
+        elif op == "release" and ids:
+            k = int(rng.choice(ids)) if rng.random() < 0.9 else 10 ** 9
+            assert model.release(k) == _status(native.release, k)[0]
+        elif op == "preempt":
+            st_m, v_m = model.preempt()
+            st_n, v_n = _status(native.preempt)
+            assert st_m == st_n and (st_m != OK or v_m == v_n)
+            counts["preempted"] += st_m == OK
+        elif op == "step" and ids:
+            pick = [int(x) for x in rng.choice(ids, size=int(rng.integers(1, len(ids) + 1)),
+                                               replace=False)]
+            if rng.random() < 0.05:
+                pick = pick + pick[:1]                     # an id listed twice: refused
+            toks = [int(x) for x in rng.integers(0, 50, len(pick))]
+            st_m, slots_m = model.decode_step(pick, toks)
+            st_n, out = _status(native.decode_step, pick, toks)
+            assert st_m == st_n, ("step", st_m, st_n)
+            if st_m == OK:
+                assert list(out) == slots_m
+        elif op == "tables" and ids:
+            pick = [int(x) for x in rng.choice(ids, size=min(len(ids), 5), replace=False)]
+            _, t_m, l_m = model.block_tables(pick)
+            t_n, l_n = native.block_tables(pick)
+            assert t_n.tolist() == t_m and l_n.tolist() == l_m
+        assert native.stats() == model.stats()
+        check_invariants(model)
+    return counts
+
+
+@pytest.mark.parametrize("prefix", [True, False])
+@pytest.mark.parametrize("seed,num_blocks,bs", [(1, 24, 4), (2, 60, 4), (3, 17, 16), (4, 200, 2)])
+def test_native_equals_model(seed, num_blocks, bs, prefix):
+    counts = _lockstep(seed, num_blocks, bs, 12, prefix, 1500)
+    # the sequence exercised what it is meant to
+    assert counts["admitted"] > 50 and counts["preempted"] > 5
+    if prefix:
+        assert counts["cached_tokens"] > 0
+    if num_blocks < 30:
+        assert counts["refused"] > 0
+
+
+def test_native_argument_errors():
+    with pytest.raises(ValueError):
+        pa.BlockManager(0, 16, 4)
+    bm = pa.BlockManager(8, 4, 2, True)
+    for fn, args, code in [(bm.admit, (1, 0, []), SHAPE), (bm.admit, (1, 0, list(range(9))), SHAPE),
+                           (bm.append, (5, [1]), STATE), (bm.truncate, (5, 1), STATE),
+                           (bm.release, (5,), STATE), (bm.preempt, (), STATE),
+                           (bm.block_tables, ([5],), STATE)]:
+        with pytest.raises(pa.PagedAttnError) as e:
+            fn(*args)
+        assert e.value.status == code, fn
+    bm.admit(1, 0, [1, 2, 3])
+    with pytest.raises(pa.PagedAttnError) as e:
+        bm.truncate(1, 4)
+    assert e.value.status == SHAPE
+    L = pa.lib()
+    assert L.pa_bm_admit(None, 1, 0, None, 1, None, None) == NULL
+    assert L.pa_bm_create(10, 0, 4, 1) is None and L.pa_bm_create(10, 4, 0, 1) is None
+
+
+# --------------------------------------------------------------------------
+# a layout built by the native manager serves attention correctly
+# --------------------------------------------------------------------------
+
+def _kv_row(prefix_tokens, Hkv, D, which):
+    """K or V row of a token, a function of the whole prefix up to it (as in a
+    real model), so identical prefixes give identical rows."""
+    h = (hash(tuple(prefix_tokens)) ^ which) & 0xFFFFFFFF
+    x = np.random.default_rng(h).standard_normal((Hkv, D), dtype=np.float32)
+    return W.f32_to_bf16_bits(x)
+
+
+def test_manager_layout_gives_contiguous_attention():
+    rng = np.random.default_rng(9)
+    bs, Hq, Hkv, D, NB = 4, 4, 2, 16, 64
+    bm = pa.BlockManager(NB, bs, 16, True)
+    kc = np.full((NB, bs, Hkv, D), W.BF16_NAN, np.uint16)
+    vc = kc.copy()
+    system = [int(x) for x in rng.integers(0, 30, 3 * bs)]     # a shared system prompt
+    seqs = {}
+
+    def write(tokens, first, slots):
+        for j, s in enumerate(slots):
+            t = first + j
+            kc[s // bs, s % bs] = _kv_row(tokens[:t + 1], Hkv, D, 0)
+            vc[s // bs, s % bs] = _kv_row(tokens[:t + 1], Hkv, D, 1)
+
+    for k in range(1, 5):
+        prompt = system + [int(x) for x in rng.integers(0, 30, int(rng.integers(1, 7)))]
+        cached, slots = bm.admit(k, 0, prompt)
+        assert k == 1 or cached >= 2 * bs                       # later prompts reuse the system prompt
+        write(prompt, cached, slots)
+        for _ in range(int(rng.integers(1, 4))):                # a few decode steps
+            tok = [int(rng.integers(0, 30))]
+            slot = bm.append(k, tok)
+            prompt = prompt + tok
+            write(prompt, len(prompt) - 1, slot)
+        seqs[k] = prompt
+    ids = sorted(seqs)
+    tables, lens = bm.block_tables(ids)
+    q = W.f32_to_bf16_bits(rng.standard_normal((len(ids), Hq, D), dtype=np.float32))
+    got = oracle.decode(q, kc, vc, tables, lens, np.float32(0.25))
+    G = Hq // Hkv
+    for i, k in enumerate(ids):
+        toks = seqs[k]
+        K = np.stack([_kv_row(toks[:t + 1], Hkv, D, 0) for t in range(len(toks))])
+        V = np.stack([_kv_row(toks[:t + 1], Hkv, D, 1) for t in range(len(toks))])
+        f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+        qt = torch.from_numpy(f(q[i]))[:, None, :]                                     # [Hq, 1, D]
+        kt = torch.from_numpy(f(K)).permute(1, 0, 2).repeat_interleave(G, 0)
+        vt = torch.from_numpy(f(V)).permute(1, 0, 2).repeat_interleave(G, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.25)[:, 0]
+        assert np.abs(got[i] - ref.numpy()).max() < 1e-12, k
