@@ -359,3 +359,94 @@ def pin_decode_multi(oracle, seed=17):
 ALL_PINS = [pin_sdpa_decode, pin_loops_decode, pin_two_token_closed_form, pin_permutation,
             pin_block_size, pin_ctx1_returns_v, pin_constant_v, pin_histogram, pin_gqa_mapping,
             pin_poison_untouched, pin_empty_sequence, pin_append, pin_prefill, pin_decode_multi]
+
+
+# --------------------------------------------------------------------------
+# FP8 KV pages (oracle/kv_fp8.py): pins take that module
+# --------------------------------------------------------------------------
+
+def _torch_e4m3(x32: np.ndarray) -> np.ndarray:
+    """Library routine: torch's float8_e4m3fn conversion (round to nearest
+    even), as uint8 codes."""
+    return torch.from_numpy(np.ascontiguousarray(x32, np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def pin_fp8_codec(kv):
+    """F1: every code decodes to torch's float8_e4m3fn value; encoding equals
+    torch's conversion on every bf16 value in [-448, 448], on ties and on
+    subnormals; every finite code survives a round trip."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = kv.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(ref)], ref[~np.isnan(ref)])
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) <= 448)]
+    assert np.array_equal(kv.e4m3_encode(x), _torch_e4m3(x))
+    finite = ref[~np.isnan(ref)]
+    mids = (np.sort(np.unique(finite))[1:] + np.sort(np.unique(finite))[:-1]) / 2   # exact ties
+    ties = mids.astype(np.float32)
+    ties = ties[ties.astype(np.float64) == mids]
+    assert np.array_equal(kv.e4m3_encode(ties), _torch_e4m3(ties))
+    fc = codes[~np.isnan(ref)]
+    back = kv.e4m3_encode(kv.e4m3_decode(fc).astype(np.float32))
+    zero = (fc == 0x80)                                   # -0 keeps its sign
+    assert np.array_equal(back[~zero], fc[~zero]) and (back[zero] == 0x80).all()
+
+
+def pin_fp8_quantize_and_append(kv, seed=18):
+    """F2: the appended codes are torch's conversion of clamp(x * (1/scale))
+    with the reciprocal and product in fp32, written at the slots (negative
+    slots skip)."""
+    rng = np.random.default_rng(seed)
+    Hkv, D, bs, NB = 2, 8, 4, 6
+    nk = W.f32_to_bf16_bits(rng.standard_normal((5, Hkv, D), dtype=np.float32) * 300)
+    nv = W.f32_to_bf16_bits(rng.standard_normal((5, Hkv, D), dtype=np.float32))
+    kc = np.full((NB, bs, Hkv, D), 0x7F, np.uint8)
+    vc = kc.copy()
+    slots = np.array([3, -1, 9, 22, 4], np.int64)
+    ks, vs = np.float32(0.37), np.float32(0.011)
+    k2, v2 = kv.append_fp8(nk, nv, slots, kc, vc, ks, vs)
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        for new, cache, sc in ((nk, k2, ks), (nv, v2, vs)):
+            x = (new[i].astype(np.uint32) << np.uint32(16)).view(np.float32)
+            y = np.clip(x * (np.float32(1) / sc), np.float32(-448), np.float32(448))
+            assert np.array_equal(cache[s // bs, s % bs], _torch_e4m3(y))
+    untouched = np.ones((NB, bs), bool)
+    for s in slots[slots >= 0]:
+        untouched[s // bs, s % bs] = False
+    assert (k2[untouched] == 0x7F).all() and (v2[untouched] == 0x7F).all()
+    assert (k2[~untouched] != 0x7F).any()
+    # values beyond the range clamp to the largest finite code
+    big = W.f32_to_bf16_bits(np.array([1e6, -1e6], np.float32))
+    assert kv.quantize(big, np.float32(1.0)).tolist() == [0x7E, 0xFE]
+
+
+def pin_fp8_decode_reduces_to_bf16(kv, seed=19):
+    """F3: with power-of-two scales every dequantised value is exactly a bf16
+    value, so decode over fp8 pools equals the (pinned) bf16 decode over the
+    dequantised pools, bit for bit."""
+    import oracle.paged_attention as pa_oracle
+    rng = np.random.default_rng(seed)
+    NB, bs, Hkv, D, B, Hq = 12, 4, 2, 8, 3, 6
+    codes = rng.integers(0, 256, (NB, bs, Hkv, D)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                  # no NaN codes
+    vcodes = rng.integers(0, 256, (NB, bs, Hkv, D)).astype(np.uint8)
+    vcodes[(vcodes & 0x7F) == 0x7F] = 0x40
+    ks, vs = 2.0 ** -4, 2.0 ** 3
+    kbf = W.f32_to_bf16_bits((kv.e4m3_decode(codes) * ks).astype(np.float32))
+    vbf = W.f32_to_bf16_bits((kv.e4m3_decode(vcodes) * vs).astype(np.float32))
+    assert np.array_equal(_f64(kbf), kv.e4m3_decode(codes) * ks)       # exact in bf16
+    tables = rng.permutation(NB)[:B * 4].reshape(B, 4).astype(np.int32)
+    lens = np.array([1, 9, 16], np.int32)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    got = kv.decode_fp8(q, codes, vcodes, tables, lens, np.float32(0.3), ks, vs)
+    want = pa_oracle.decode(q, kbf, vbf, tables, lens, np.float32(0.3))
+    assert np.array_equal(got, want)
+
+
+FP8_PINS = [pin_fp8_codec, pin_fp8_quantize_and_append, pin_fp8_decode_reduces_to_bf16]

@@ -58,3 +58,49 @@ def test_pins_catch_mutant(name):
         except Exception as e:          # AssertionError, or a crash the slip causes
             caught.append((pin.__name__, type(e).__name__))
     assert caught, f"no pin rejects mutant {name}"
+
+
+# --------------------------------------------------------------------------
+# FP8 KV pages
+# --------------------------------------------------------------------------
+
+import oracle.kv_fp8 as real_fp8  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", P.FP8_PINS, ids=lambda f: f.__name__)
+def test_fp8_pin(pin):
+    pin(real_fp8)
+
+
+FP8_MUTANTS = {
+    "ties_away": ("code = int(np.rint(a / 2.0 ** -9))", "code = int(np.floor(a / 2.0 ** -9 + 0.5))"),
+    "mantissa_ties_away": ("m = int(np.rint((2.0 * f - 1.0) * 8.0))",
+                           "m = int(np.floor((2.0 * f - 1.0) * 8.0 + 0.5))"),
+    "bias_8": ("code = ((e + 7) << 3) | m", "code = ((e + 8) << 3) | m"),
+    "decode_bias_8": ("np.exp2(e.astype(np.float64) - 7.0)", "np.exp2(e.astype(np.float64) - 8.0)"),
+    "no_clamp": ("y = np.clip(x * inv, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))", "y = x * inv"),
+    "scale_not_inverted": ("inv = np.float32(1.0) / np.float32(scale)", "inv = np.float32(scale)"),
+    "k_scale_dropped": ("K = e4m3_decode(gather_sequence(k_cache8, block_tables[b], L)) * ks",
+                        "K = e4m3_decode(gather_sequence(k_cache8, block_tables[b], L))"),
+    "v_scale_dropped": ("V = e4m3_decode(gather_sequence(v_cache8, block_tables[b], L)) * vs",
+                        "V = e4m3_decode(gather_sequence(v_cache8, block_tables[b], L))"),
+    "subnormal_step": ("sub = m * 2.0 ** -9", "sub = m * 2.0 ** -10"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_pins_catch_mutant(name):
+    old, new = FP8_MUTANTS[name]
+    src = inspect.getsource(real_fp8)
+    assert src.count(old) == 1, f"anchor not unique/found: {old!r}"
+    src = src.replace(old, new).replace("from .paged_attention import",
+                                        "from oracle.paged_attention import")
+    mod = types.ModuleType("fp8_mutant")
+    exec(compile(src, "fp8_mutant", "exec"), mod.__dict__)
+    caught = []
+    for pin in P.FP8_PINS:
+        try:
+            pin(mod)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin rejects {name}"
