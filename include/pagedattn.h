@@ -177,6 +177,48 @@ size_t pa_decode_multi_workspace_size(int num_seqs, int q_len, int num_q_heads, 
                                       int num_splits);
 
 /*
+ * FP8 KV pages.  The pools hold one byte per element: k_cache, v_cache are
+ * [num_blocks, block_size, num_kv_heads, head_dim] uint8 codes of the OCP
+ * 8-bit float format E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals, no infinities, 0x7F / 0xFF NaN, largest finite 448),
+ * halving the pool's bytes and what a decode step reads.  K and V each carry
+ * one fp32 scale for the whole pool: a code c stands for e4m3(c) * scale.
+ * Source: quantised KV cache storage, "Mini-Infer: A High-Performance LLM
+ * Inference Acceleration Engine for Production Environments" (zingnex.cn
+ * thread, English), section "Memory Optimization and KV Cache Management";
+ * the page names no format, so the format and the per-tensor scale are a
+ * reading.
+ *
+ * pa_reshape_and_cache_fp8: the append of pa_reshape_and_cache with
+ * quantisation - element x (bf16) of token i is stored at its slot as
+ * e4m3(clamp(x * (1 / scale), -448, 448)), the reciprocal and the product
+ * rounded to fp32, the conversion rounding to nearest even.  A NaN input
+ * stores a NaN code.  k_scale, v_scale: finite, > 0, with a finite
+ * reciprocal (else PA_ERR_SHAPE).  Other arguments as pa_reshape_and_cache,
+ * with the pools as above.
+ */
+int pa_reshape_and_cache_fp8(const void *k, const void *v, const int64_t *slot_mapping,
+                             void *k_cache, void *v_cache, float k_scale, float v_scale,
+                             int64_t num_tokens, int64_t num_blocks, int block_size,
+                             int num_kv_heads, int head_dim, void *stream);
+
+/*
+ * pa_decode over fp8 pools: computes what pa_decode computes with
+ * K_b[t] = e4m3(k code) * k_scale and V_b[t] = e4m3(v code) * v_scale.  The
+ * codes widen exactly to bf16 inside the kernel; k_scale joins the score
+ * scale (fp32 product scale * k_scale) and v_scale multiplies the normalised
+ * output.  Split-KV, workspace (pa_decode_workspace_size), outputs and limits
+ * as for pa_decode; scale * k_scale * log2(e) must be finite (else
+ * PA_ERR_SHAPE), and k_scale, v_scale follow pa_reshape_and_cache_fp8's rule.
+ */
+int pa_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *block_tables, const int32_t *context_lens, float scale,
+                  float k_scale, float v_scale, int num_splits, void *out, int num_seqs,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                  int64_t num_blocks, int max_blocks_per_seq, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
  * The two passes of pa_decode as separate calls, for callers that merge
  * pieces themselves (for example pieces of one sequence computed on
  * different devices) or time the passes apart.  Arguments mean what they mean

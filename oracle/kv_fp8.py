@@ -67,7 +67,8 @@ def quantize(x_bf16_bits: np.ndarray, scale) -> np.ndarray:
     reciprocal and the product in fp32."""
     x = (np.asarray(x_bf16_bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
     inv = np.float32(1.0) / np.float32(scale)
-    y = np.clip(x * inv, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    with np.errstate(over="ignore", invalid="ignore"):     # inf and NaN inputs
+        y = np.clip(x * inv, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     return e4m3_encode(y)
 
 

@@ -15,6 +15,9 @@ Calls (argument order as in the C ABI):
   decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
                stream=None, workspace=None): q_len query tokens per sequence, causal
   decode_partials(...), decode_merge(...): the two passes of decode
+  reshape_and_cache_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream=None)
+  decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+             num_splits, out, stream=None, workspace=None): fp8 (e4m3) pools
   prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, out,
           max_q_len, num_splits=0, stream=None, workspace=None)
   decode_workspace_size(num_seqs, num_q_heads, head_dim, num_splits)
@@ -62,6 +65,10 @@ SIGNATURES = {
                         _I, _VP, _SZ, _VP]),
     "pa_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "pa_prefill_plan_splits": (_I, [_I, _I, _I, _I, _I, _I]),
+    "pa_reshape_and_cache_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _F, _I64, _I64, _I, _I, _I,
+                                      _VP]),
+    "pa_decode_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _F, _F, _I, _VP, _I, _I, _I, _I, _I, _I64,
+                           _I, _VP, _SZ, _VP]),
     # host-side block manager (include/pa_block_manager.h)
     "pa_bm_create": (_VP, [_I64, _I, _I, _I]),
     "pa_bm_destroy": (None, [_VP]),
@@ -127,9 +134,9 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def _pool_dims(k_cache, v_cache):
-    _need(k_cache, "k_cache", torch.bfloat16, 4)
-    _need(v_cache, "v_cache", torch.bfloat16, 4, k_cache.device)
+def _pool_dims(k_cache, v_cache, dtype=torch.bfloat16):
+    _need(k_cache, "k_cache", dtype, 4)
+    _need(v_cache, "v_cache", dtype, 4, k_cache.device)
     if k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache shapes differ")
     return tuple(int(x) for x in k_cache.shape)     # NB, bs, Hkv, D
@@ -138,7 +145,26 @@ def _pool_dims(k_cache, v_cache):
 def reshape_and_cache(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
     """Write k[i], v[i] ([T, Hkv, D] bf16) to pool row slot_mapping[i] (int64 [T];
     negative = skip)."""
-    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
+    NB, bs, Hkv, D, T, dev = _append_dims(k, v, slot_mapping, k_cache, v_cache, torch.bfloat16)
+    _check("pa_reshape_and_cache", lib().pa_reshape_and_cache(
+        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), T, NB, bs, Hkv, D, _stream_ptr(stream, dev)))
+
+
+def reshape_and_cache_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale: float, v_scale: float,
+                          stream=None) -> None:
+    """As reshape_and_cache into fp8 pools (uint8 e4m3 codes [NB, bs, Hkv, D]):
+    element x is stored as e4m3(clamp(x / scale, -448, 448)), per-tensor fp32
+    scales."""
+    NB, bs, Hkv, D, T, dev = _append_dims(k, v, slot_mapping, k_cache, v_cache, torch.uint8)
+    _check("pa_reshape_and_cache_fp8", lib().pa_reshape_and_cache_fp8(
+        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), float(k_scale), float(v_scale), T, NB, bs, Hkv, D,
+        _stream_ptr(stream, dev)))
+
+
+def _append_dims(k, v, slot_mapping, k_cache, v_cache, pool_dtype):
+    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache, pool_dtype)
     dev = k_cache.device
     _need(k, "k", torch.bfloat16, 3, dev)
     _need(v, "v", torch.bfloat16, 3, dev)
@@ -148,9 +174,7 @@ def reshape_and_cache(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None
         raise ValueError(f"k/v must be [{T}, {Hkv}, {D}]")
     if slot_mapping.shape[0] != T:
         raise ValueError("slot_mapping length differs from the token count")
-    _check("pa_reshape_and_cache", lib().pa_reshape_and_cache(
-        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
-        v_cache.data_ptr(), T, NB, bs, Hkv, D, _stream_ptr(stream, dev)))
+    return NB, bs, Hkv, D, T, dev
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
@@ -207,6 +231,26 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_sp
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), float(scale), int(num_splits), out.data_ptr(), B, Hq, Hkv, D,
         bs, NB, W, ws_ptr, ws_bytes, _stream_ptr(stream, dev)))
+    return out
+
+
+def decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float, k_scale: float,
+               v_scale: float, num_splits: int, out, stream=None,
+               workspace: Optional[torch.Tensor] = None):
+    """decode over fp8 pools (uint8 e4m3 codes [NB, bs, Hkv, D]): K and V are
+    the codes' values times k_scale and v_scale."""
+    NB, bs, Hkv, D, B, Hq, W, dev = _decode_dims(q, k_cache, v_cache, block_tables, context_lens,
+                                                 torch.uint8)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError(f"out must be [{B}, {Hq}, {D}]")
+    if num_splits == 0 and B > 0:
+        num_splits = auto_splits(B, Hkv, W, bs, dev)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace)
+    _check("pa_decode_fp8", lib().pa_decode_fp8(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), float(scale), float(k_scale), float(v_scale), int(num_splits),
+        out.data_ptr(), B, Hq, Hkv, D, bs, NB, W, ws_ptr, ws_bytes, _stream_ptr(stream, dev)))
     return out
 
 
@@ -272,8 +316,8 @@ def _workspace(B, Hq, D, num_splits, dev, workspace, q_len=1):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
 
 
-def _decode_dims(q, k_cache, v_cache, block_tables, context_lens):
-    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
+def _decode_dims(q, k_cache, v_cache, block_tables, context_lens, pool_dtype=torch.bfloat16):
+    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache, pool_dtype)
     dev = k_cache.device
     _need(q, "q", torch.bfloat16, 3, dev)
     _need(block_tables, "block_tables", torch.int32, 2, dev)
@@ -377,7 +421,9 @@ def prefill_auto_splits(num_seqs, max_q_len, num_kv_heads, max_blocks_per_seq, b
 
 __all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "decode_merge", "prefill",
            "prefill_workspace_size", "prefill_auto_splits", "decode_workspace_size", "plan_splits",
-           "auto_splits", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError", "PA_MAX_SPLITS"]
+           "auto_splits", "decode_multi", "decode_multi_workspace_size", "reshape_and_cache_fp8",
+           "decode_fp8", "BlockManager", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError",
+           "PA_MAX_SPLITS", "PA_MAX_QUERY_TOKENS"]
 
 
 class BlockManager:

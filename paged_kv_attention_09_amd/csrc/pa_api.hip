@@ -16,6 +16,9 @@ namespace {
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 bool supported_block_size(int bs) { return bs == 16 || bs == 256; }
+// fp8 pools: a per-tensor scale is a finite fp32 value > 0 whose reciprocal
+// is finite too.
+bool valid_kv_scale(float s) { return std::isfinite(s) && s > 0.f && std::isfinite(1.0f / s); }
 int log2_exact(int v) {
   int s = 0;
   while ((1 << s) < v) ++s;
@@ -88,24 +91,48 @@ const char *pa_status_string(int status) {
   }
 }
 
-int pa_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
-                         void *v_cache, int64_t num_tokens, int64_t num_blocks, int block_size,
-                         int num_kv_heads, int head_dim, void *stream) {
+namespace {
+
+int append_rows(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
+                void *v_cache, int64_t num_tokens, int64_t num_blocks, int block_size,
+                int num_kv_heads, int head_dim, bool fp8, float k_scale, float v_scale,
+                void *stream) {
   if (!k_cache || !v_cache) return PA_ERR_NULL;
   if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_SHAPE;
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
     return PA_ERR_UNSUPPORTED;
+  if (fp8 && !(valid_kv_scale(k_scale) && valid_kv_scale(v_scale))) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping) return PA_ERR_NULL;
   pa::AppendArgs a;
   a.k = (const uint16_t *)k;
   a.v = (const uint16_t *)v;
   a.slot_mapping = slot_mapping;
-  a.k_cache = (uint16_t *)k_cache;
-  a.v_cache = (uint16_t *)v_cache;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
   a.num_tokens = num_tokens;
   a.row_elems = num_kv_heads * head_dim;
+  a.fp8 = fp8 ? 1 : 0;
+  a.inv_k_scale = fp8 ? 1.0f / k_scale : 1.0f;
+  a.inv_v_scale = fp8 ? 1.0f / v_scale : 1.0f;
   return pa::launch_append(a, head_dim, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+int pa_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
+                         void *v_cache, int64_t num_tokens, int64_t num_blocks, int block_size,
+                         int num_kv_heads, int head_dim, void *stream) {
+  return append_rows(k, v, slot_mapping, k_cache, v_cache, num_tokens, num_blocks, block_size,
+                     num_kv_heads, head_dim, false, 1.0f, 1.0f, stream);
+}
+
+int pa_reshape_and_cache_fp8(const void *k, const void *v, const int64_t *slot_mapping,
+                             void *k_cache, void *v_cache, float k_scale, float v_scale,
+                             int64_t num_tokens, int64_t num_blocks, int block_size,
+                             int num_kv_heads, int head_dim, void *stream) {
+  return append_rows(k, v, slot_mapping, k_cache, v_cache, num_tokens, num_blocks, block_size,
+                     num_kv_heads, head_dim, true, k_scale, v_scale, stream);
 }
 
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int num_splits) {
@@ -176,8 +203,8 @@ int resolve_decode(const void *q, const void *k_cache, const void *v_cache,
   const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
   const int split_len = split_len_for(max_tokens, num_splits);
   a->q = (const uint16_t *)q;
-  a->k_cache = (const uint16_t *)k_cache;
-  a->v_cache = (const uint16_t *)v_cache;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
   a->block_tables = block_tables;
   a->context_lens = context_lens;
   a->new_k = nullptr;
@@ -193,6 +220,8 @@ int resolve_decode(const void *q, const void *k_cache, const void *v_cache,
   a->split_len = split_len;
   a->num_splits = num_pieces(max_tokens, split_len);
   a->q_len = 1;
+  a->kv_fp8 = 0;
+  a->v_scale = 1.0f;
   return PA_OK;
 }
 
@@ -277,6 +306,33 @@ int pa_decode_multi(const void *q, const void *k_cache, const void *v_cache,
   if (num_seqs == 0) return PA_OK;
   if (!out) return PA_ERR_NULL;
   a.q_len = q_len;
+  a.out = (uint16_t *)out;
+  if (a.num_splits > 1) {
+    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+  }
+  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
+                                (hipStream_t)stream);
+}
+
+int pa_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *block_tables, const int32_t *context_lens, float scale,
+                  float k_scale, float v_scale, int num_splits, void *out, int num_seqs,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                  int64_t num_blocks, int max_blocks_per_seq, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  if (!(valid_kv_scale(k_scale) && valid_kv_scale(v_scale))) return PA_ERR_SHAPE;
+  pa::DecodeArgs a;
+  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!out) return PA_ERR_NULL;
+  // scores are q . (code k_scale) scale: k_scale joins the score scale
+  a.scale_log2 = (scale * k_scale) * 1.4426950408889634f;
+  if (!std::isfinite(a.scale_log2)) return PA_ERR_SHAPE;
+  a.kv_fp8 = 1;
+  a.v_scale = v_scale;
   a.out = (uint16_t *)out;
   if (a.num_splits > 1) {
     st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);

@@ -8,7 +8,8 @@
 // a Glance" table, row "Batched Paged Decode (v0.2.1)".
 //
 // A pure copy: each lane moves one 16-byte vector of K and the same vector
-// of V, so a wave covers 1 KiB of a row and rows stay coalesced.
+// of V, so a wave covers 1 KiB of a row and rows stay coalesced.  fp8 pools
+// take the quantising variant below.
 #include "pa_device.hpp"
 #include "pa_kernels.hpp"
 
@@ -34,6 +35,43 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int vec_per_r
   }
 }
 
+// fp8 pools: each lane reads 8 bf16 of K and of V (16 bytes each) and
+// writes their 8 codes (8 bytes each).  The code of x is e4m3 of
+// clamp(x * (1 / scale), -448, 448), product in fp32, rounded to nearest
+// even; the comparisons keep a NaN product NaN.
+__device__ __forceinline__ float clamp448(float y) {
+  return y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
+}
+
+__device__ __forceinline__ uint2 quantize8(uint4 x, float inv) {
+  auto lo = [&](uint32_t w) { return clamp448(__uint_as_float(w << 16) * inv); };
+  auto hi = [&](uint32_t w) { return clamp448(__uint_as_float(w & 0xFFFF0000u) * inv); };
+  // word_sel false fills bytes 0-1, true bytes 2-3 (keeping the others)
+  int a = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.x), hi(x.x), 0, false);
+  a = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.y), hi(x.y), a, true);
+  int b = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.z), hi(x.z), 0, false);
+  b = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.w), hi(x.w), b, true);
+  return uint2{(uint32_t)a, (uint32_t)b};
+}
+
+__global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, int vec_per_row) {
+  const int64_t total = a.num_tokens * vec_per_row;
+  const uint4 *k = (const uint4 *)a.k;
+  const uint4 *v = (const uint4 *)a.v;
+  uint2 *kc = (uint2 *)a.k_cache;
+  uint2 *vc = (uint2 *)a.v_cache;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = idx / vec_per_row;
+    const int64_t e = idx - i * vec_per_row;
+    const int64_t s = a.slot_mapping[i];
+    if (s < 0) continue;
+    const int64_t dst = s * vec_per_row + e;
+    kc[dst] = quantize8(k[idx], a.inv_k_scale);
+    vc[dst] = quantize8(v[idx], a.inv_v_scale);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t stream) {
@@ -43,7 +81,12 @@ hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t stream) 
   int64_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, vec_per_row);
+  if (a.fp8)
+    hipLaunchKernelGGL(append_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a,
+                       vec_per_row);
+  else
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a,
+                       vec_per_row);
   return hipGetLastError();
 }
 

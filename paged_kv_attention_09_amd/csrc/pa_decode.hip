@@ -54,6 +54,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kChunk = 16;     // tokens per wave step
 constexpr int kStages = 2;     // chunks in flight per wave
+constexpr int kStages8 = 2;    // the same for fp8 pools
 constexpr float kSlack = 8.f;  // log2 headroom before the running max moves
 constexpr int kMaxVectorGroup = 2;
 
@@ -74,6 +75,23 @@ __device__ __forceinline__ int row_swizzle(int r) {
     const int s = r >> 1;
     return ((s << 1) | (s >> 2)) & 7;
   }
+}
+
+// fp8 pools: LDS position of 16-byte chunk c of stored row r (D bytes) is
+// c ^ row_swizzle8(r).  Lanes of a K fragment read 8 bytes of rows 0..15 at
+// one position; rows sharing a 256-byte bank line get distinct positions.
+template <int D>
+__device__ __forceinline__ int row_swizzle8(int r) {
+  return (r >> (D == 128 ? 1 : 2)) & (D / 16 - 1);
+}
+
+// 8 fp8 (e4m3) codes -> 8 bf16 values (exact: every e4m3 value is a bf16
+// value), element order kept.
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint2 v) {
+  return uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, true))};
 }
 
 template <int D>
@@ -120,14 +138,27 @@ static_assert(decode_merge_fits<128>(8, decode_wave_lds<128>(1, false)) &&
 // MULTI: q_len comes from the arguments, the q rows go straight to
 // registers and the merge runs in passes of 16 rows; without it q_len is 1.
 // The vector path handles one query token and NT = 1.
-template <int D, int G, bool MF, int NT, bool MULTI>
+// KV8: the pools hold fp8 (e4m3) codes; the matrix path converts K fragments
+// to bf16 in registers and each chunk's V into a bf16 LDS buffer, and the
+// per-tensor scales fold into the score scale (K) and the output (V).
+template <int D, int G, bool MF, int NT, bool MULTI, bool KV8>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
+  static_assert(!KV8 || (MF && !MULTI), "fp8 pools: single-token matrix path");
   using Ge = DecodeGeom<D>;
-  constexpr int NSTAGE = kStages;
-  constexpr int ROWB = Ge::ROWB, NPOS = Ge::NPOS, CHB = Ge::CHB, NDMA = Ge::NDMA;
-  constexpr int STB = Ge::STB, KS = Ge::KS, DB = Ge::DB, MS = Ge::MS;
+  constexpr int NSTAGE = KV8 ? kStages8 : kStages;
+  // bf16 rows, as computed on (q, the V^T reads, the merge)
+  constexpr int ROWB = Ge::ROWB, CHB = Ge::CHB, KS = Ge::KS, DB = Ge::DB, MS = Ge::MS;
   constexpr int KPL = Ge::KPL, PAIRS = Ge::PAIRS;
-  constexpr int WAVE_LDS = decode_wave_lds<D>(MULTI ? 0 : G, !MF);
+  // rows as stored in the pool and staged by DMA (1 byte per element for fp8)
+  constexpr int RB = KV8 ? D : ROWB;
+  constexpr int NP = RB / 16;                      // 16-byte positions per stored row
+  constexpr int CHK = kChunk * RB;                 // bytes of one staged chunk of K (or V)
+  constexpr int NDMA = CHK / 1024;                 // DMA instructions per tensor per chunk
+  constexpr int STB = 2 * CHK;                     // one stage: K chunk then V chunk
+  constexpr int CVB = KV8 ? CHB : 0;               // bf16 V conversion buffer
+  constexpr int WAVE_LDS = KV8 ? NSTAGE * STB + CVB + (G * ROWB + 1023) / 1024 * 1024
+                               : decode_wave_lds<D>(MULTI ? 0 : G, !MF);
+  static_assert(!KV8 || decode_merge_fits<D>(G, WAVE_LDS), "merge scratch");
   constexpr int RC = MULTI ? 16 : G;   // rows per merge pass
   __shared__ __attribute__((aligned(1024))) char smem[kWaves * WAVE_LDS];
 
@@ -175,21 +206,23 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 
   constexpr int QB = MULTI ? 0 : (G * ROWB + 1023) / 1024 * 1024;
   char *my = smem + wave * WAVE_LDS;
-  char *qlds = my + NSTAGE * STB;
+  char *cvb = my + NSTAGE * STB;  // fp8 pools: this chunk's V as bf16
+  char *qlds = cvb + CVB;
   char *plds = qlds + QB;  // vector path only
   const uint32_t my_off = lds_offset(my);
   const uint32_t q_off = lds_offset(qlds);
 
-  const uint32_t RS = (uint32_t)a.num_kv_heads * ROWB;  // bytes between token rows
-  const char *kbase = (const char *)a.k_cache + (size_t)g * ROWB;
-  const char *vbase = (const char *)a.v_cache + (size_t)g * ROWB;
+  const uint32_t RS = (uint32_t)a.num_kv_heads * RB;  // bytes between token rows
+  const char *kbase = (const char *)a.k_cache + (size_t)g * RB;
+  const char *vbase = (const char *)a.v_cache + (size_t)g * RB;
 
   // Fused append (single query token only): the wave that owns the
   // sequence's last token writes the new K/V row of this kv head to that
   // token's slot, and waits for the stores to complete before it issues any
   // load of the chunk holding the row.  Only this wave reads that row in this
   // launch.
-  if (a.new_k != nullptr && t1 == L && wave == (nck - 1) % kWaves) {
+  if (!KV8 && a.new_k != nullptr && t1 == L && wave == (nck - 1) % kWaves) {
+    constexpr int NPOS = Ge::NPOS;
     const int tl = L - 1;
     const size_t row = ((size_t)(uint32_t)table[tl >> bs_shift] << bs_shift) + (tl & bs_mask);
     const size_t src = ((size_t)b * a.num_kv_heads + g) * ROWB;
@@ -203,14 +236,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     wait_vmcnt<0>();
   }
 
-  // Per-lane DMA geometry: instruction j moves rows j*(1024/ROWB) + lane/NPOS.
+  // Per-lane DMA geometry: instruction j moves rows j*(1024/RB) + lane/NP.
   uint32_t dma_voff[NDMA], dma_pos[NDMA];
   int dma_row[NDMA];
 #pragma unroll
   for (int j = 0; j < NDMA; ++j) {
-    const int r = j * (1024 / ROWB) + lane / NPOS;
-    const int p = lane % NPOS;
-    const int c = p ^ row_swizzle<D, MF>(r);
+    const int r = j * (1024 / RB) + lane / NP;
+    const int p = lane % NP;
+    const int c = p ^ (KV8 ? row_swizzle8<D>(r) : row_swizzle<D, MF>(r));
     dma_row[j] = r;
     dma_pos[j] = (uint32_t)c * 16;
     dma_voff[j] = (uint32_t)r * RS + (uint32_t)c * 16;
@@ -231,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const uint32_t vo = dma_row[j] < nvalid ? dma_voff[j] : dma_pos[j];
-      dma16(st + CHB + j * 1024, vb, vo);
+      dma16(st + CHK + j * 1024, vb, vo);
     }
   };
 
@@ -296,18 +329,30 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
       // LDS read offsets: K fragment kk of this lane is row hh, head_dim
       // 32 kk + 8 qd .. + 7; V^T fragment db is 8 bytes of row 4 qd + hh / 4
       // at head_dim 16 db + 4 (hh % 4).
+      // fp8 pools: K fragment kk is 8 bytes of the stored row hh, at position
+      // 2 kk + qd / 2, half qd % 2 (row_swizzle8 keeps these reads
+      // conflict-free); the V^T offsets then address the bf16 buffer.
       uint32_t k_off[KS], v_off[DB];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        k_off[kk] = (uint32_t)(hh * ROWB + (((4 * kk + qd) ^ row_swizzle<D, MF>(hh)) * 16));
+      for (int kk = 0; kk < KS; ++kk) {
+        if constexpr (KV8)
+          k_off[kk] = (uint32_t)(hh * RB + (((2 * kk + (qd >> 1)) ^ row_swizzle8<D>(hh)) * 16) +
+                                 (qd & 1) * 8);
+        else
+          k_off[kk] = (uint32_t)(hh * ROWB + (((4 * kk + qd) ^ row_swizzle<D, MF>(hh)) * 16));
+      }
       {
         const int vr = 4 * qd + (hh >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          v_off[db] = (uint32_t)(CHB + vr * ROWB +
+          v_off[db] = (uint32_t)((KV8 ? 0 : CHB) + vr * ROWB +
                                  (((2 * db + ((hh & 3) >> 1)) ^ row_swizzle<D, MF>(vr)) * 16) +
                                  (hh & 1) * 8);
       }
+      // fp8 pools, V conversion: lane converts BPL bytes of stored row lane / 4
+      constexpr int BPL = CHK / 64;
+      const int cv_row = lane >> 2;
+      const int cv_pos = (lane & 3) * (BPL / 16);
       // Per tile: is this lane's column a query row, and the last key its
       // query token may see (query token j sits at position L - q_len + j).
       bool colv[NT];
@@ -341,9 +386,28 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
         for (int t = 0; t < NT; ++t) sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-          const uint4 kf = *(const uint4 *)(st + k_off[kk]);
+          uint4 kf;
+          if constexpr (KV8)
+            kf = fp8x8_to_bf16(*(const uint2 *)(st + k_off[kk]));
+          else
+            kf = *(const uint4 *)(st + k_off[kk]);
 #pragma unroll
           for (int t = 0; t < NT; ++t) sc[t] = mfma_k32(kf, qf[t][kk], sc[t]);
+        }
+        if constexpr (KV8) {
+          // this chunk's V rows, fp8 -> bf16, into the wave's buffer (the
+          // previous chunk's V^T reads were issued before these writes)
+          const char *src = st + CHK + cv_row * RB;
+          char *dst = cvb + cv_row * ROWB;
+#pragma unroll
+          for (int j = 0; j < BPL / 16; ++j) {
+            const int p = cv_pos + j;
+            const uint4 raw = *(const uint4 *)(src + ((p ^ row_swizzle8<D>(cv_row)) * 16));
+            const uint4 lo = fp8x8_to_bf16(uint2{raw.x, raw.y});
+            const uint4 hi = fp8x8_to_bf16(uint2{raw.z, raw.w});
+            *(uint4 *)(dst + (((2 * p) ^ row_swizzle<D, MF>(cv_row)) * 16)) = lo;
+            *(uint4 *)(dst + (((2 * p + 1) ^ row_swizzle<D, MF>(cv_row)) * 16)) = hi;
+          }
         }
 
         // ---- online softmax, lazily rescaled (see the file comment) ----
@@ -385,7 +449,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
         // ---- O^T += V^T P^T: lane holds query row 16 t + hh, head_dim 16 db + 4 qd + i ----
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint2 vf = read_tr(st + v_off[db]);
+          const uint2 vf = read_tr((KV8 ? cvb : st) + v_off[db]);
 #pragma unroll
           for (int t = 0; t < NT; ++t) o[t][db] = mfma_k16(vf, pb[t], o[t][db]);
         }
@@ -537,7 +601,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
       // den is 0 only when no wave saw a key (an empty sequence, or a query
       // token whose keys all lie in other pieces); a NaN read from the cache
       // propagates to the output.
-      const float inv = den != 0.f ? 1.f / den : 0.f;
+      float inv = den != 0.f ? 1.f / den : 0.f;
+      if constexpr (KV8) inv *= a.v_scale;
       const size_t orow = out_row(row_base + r);
       if (direct) {
         *(uint32_t *)(a.out + orow * D + c) = pack_bf16(n0 * inv, n1 * inv);
@@ -692,18 +757,24 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int G, bool MF, int NT, bool MULTI>
+template <int D, int G, bool MF, int NT, bool MULTI, bool KV8 = false>
 hipError_t launch_split_variant(const DecodeArgs &a, int num_seqs, hipStream_t stream) {
   dim3 grid(num_seqs * a.num_kv_heads, a.num_splits);
-  hipLaunchKernelGGL((decode_split_kernel<D, G, MF, NT, MULTI>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, G, MF, NT, MULTI, KV8>), grid, dim3(256), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
 // Path choice: one query token with a group of at most kMaxVectorGroup heads
 // takes the vector path, other single-token groups the matrix path with one
 // tile; several query tokens take the matrix path with one tile per 16 rows.
+// fp8 pools (one query token) always take the matrix path.
 template <int D, int G>
 hipError_t launch_split_dg(const DecodeArgs &a, int num_seqs, hipStream_t stream) {
+  if (a.kv_fp8) {
+    if (a.q_len != 1 || a.new_k != nullptr) return hipErrorInvalidValue;
+    return launch_split_variant<D, G, true, 1, false, true>(a, num_seqs, stream);
+  }
   if (a.q_len == 1) {
     if constexpr (G <= kMaxVectorGroup)
       return launch_split_variant<D, G, false, 1, false>(a, num_seqs, stream);

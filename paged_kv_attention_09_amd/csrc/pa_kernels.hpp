@@ -10,15 +10,17 @@ namespace pa {
 struct AppendArgs {
   const uint16_t *k, *v;
   const int64_t *slot_mapping;
-  uint16_t *k_cache, *v_cache;
+  void *k_cache, *v_cache;    // bf16 pools, or fp8 (e4m3) pools when fp8 is set
   int64_t num_tokens;
-  int row_elems;  // num_kv_heads * head_dim
+  int row_elems;              // num_kv_heads * head_dim
+  int fp8;
+  float inv_k_scale, inv_v_scale;  // fp8: 1 / scale, rounded to fp32
 };
 
 struct DecodeArgs {
   const uint16_t *q;          // [B, q_len, Hq, D]
-  const uint16_t *k_cache;    // [NB, bs, Hkv, D]
-  const uint16_t *v_cache;
+  const void *k_cache;        // [NB, bs, Hkv, D], bf16, or fp8 (e4m3) codes when kv_fp8
+  const void *v_cache;
   const int32_t *block_tables;  // [B, W]
   const int32_t *context_lens;  // [B], including the q_len query tokens
   const uint16_t *new_k;      // [B, Hkv, D] rows appended at token L_b - 1, or null (q_len 1)
@@ -26,12 +28,14 @@ struct DecodeArgs {
   uint16_t *out;              // [B, q_len, Hq, D]        (num_splits == 1)
   float *o_part;              // [B, q_len, Hq, S, D]     (num_splits > 1)
   float *lse_part;            // [B, q_len, Hq, S], base-2 log-sum-exp of scaled scores
-  float scale_log2;           // scale * log2(e)
+  float scale_log2;           // scale * log2(e) (times k_scale for fp8 pools)
   int num_q_heads, num_kv_heads, max_blocks_per_seq;
   int bs_shift;               // log2(block_size)
   int split_len;              // tokens per split, multiple of 64
   int num_splits;
   int q_len;                  // query tokens per sequence (1 = single-token decode)
+  int kv_fp8;                 // pools hold fp8 codes (single query token, no fused append)
+  float v_scale;              // fp8 pools: value of V = code value * v_scale
 };
 
 struct PrefillArgs {

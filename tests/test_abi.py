@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(HEADERS) == 2 and len(names) == 25, names
+    assert len(HEADERS) == 2 and len(names) == 27, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -116,6 +116,42 @@ def test_append_argument_checks():
     assert f(P, P, P, P, P, 1, 10, 16, 1, 80, None) == UNSUP
     assert f(None, None, None, P, P, 0, 10, 16, 1, 64, None) == OK
     assert f(None, P, P, P, P, 3, 10, 16, 1, 64, None) == NULL
+
+
+def test_append_fp8_argument_checks():
+    f = pa.lib().pa_reshape_and_cache_fp8
+    ok = [P, P, P, P, P, 0.5, 2.0, 0, 10, 16, 1, 64, None]      # no tokens: nothing to do
+    assert f(*ok) == OK
+    for i, bad_scale in [(5, 0.0), (6, -1.0), (5, float("inf")), (6, float("nan")),
+                         (5, 1e-45)]:                         # 1 / 1e-45 overflows fp32
+        bad = list(ok); bad[i] = bad_scale
+        assert f(*bad) == SHAPE, (i, bad_scale)
+    bad = list(ok); bad[3] = None
+    assert f(*bad) == NULL
+    bad = list(ok); bad[11] = 96
+    assert f(*bad) == UNSUP
+    bad = list(ok); bad[7] = 2; bad[0] = None
+    assert f(*bad) == NULL
+
+
+def _decode_fp8(**kw):
+    a = dict(q=P, k=P, v=P, tables=P, lens=P, scale=0.1, ks=0.05, vs=0.02, S=1, out=P, B=2, Hq=12,
+             Hkv=2, D=128, bs=16, NB=100, W=8, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return pa.lib().pa_decode_fp8(a["q"], a["k"], a["v"], a["tables"], a["lens"], a["scale"],
+                                  a["ks"], a["vs"], a["S"], a["out"], a["B"], a["Hq"], a["Hkv"],
+                                  a["D"], a["bs"], a["NB"], a["W"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=0.0), SHAPE), (dict(vs=-2.0), SHAPE), (dict(ks=float("nan")), SHAPE),
+    (dict(vs=float("inf")), SHAPE), (dict(scale=1e30, ks=1e30), SHAPE),   # product overflows
+    (dict(D=96), UNSUP), (dict(bs=32), UNSUP), (dict(Hq=18, Hkv=2), UNSUP),
+    (dict(S=300), SPLITS), (dict(out=None), NULL), (dict(k=None), NULL), (dict(S=4), WS),
+    (dict(B=0), OK), (dict(B=0, ks=0.0), SHAPE),
+])
+def test_decode_fp8_argument_checks(kw, code):
+    assert _decode_fp8(**kw) == code
 
 
 def test_prefill_argument_checks():

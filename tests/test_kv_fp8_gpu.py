@@ -1,0 +1,224 @@
+"""FP8 KV pages on the device against the oracle (oracle/kv_fp8.py).
+
+* The quantising append is compared bit for bit with the oracle's codes over
+  every bf16 bit pattern, for several scales (powers of two and not).  A NaN
+  input must store a NaN code (0x7F or 0xFF: the format has two and no page
+  picks one); every other code must match exactly.
+* Decode over fp8 pools is compared with oracle.decode_fp8 at the decode
+  tolerance, over the same shape matrix as bf16 decode (head_dim, group,
+  block size, split counts, ragged and empty sequences) and at the full
+  sizes of the single-token workloads on sampled rows.
+* With power-of-two scales, decode over fp8 codes and decode over a bf16 pool
+  holding the codes' values times the scales run the same arithmetic on the
+  matrix path (group of 3 or more); their outputs must agree bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.kv_fp8 as O8
+import paged_kv_attention_09_amd as pa
+import workloads as W
+from gpu_cases import DEV, assert_close, bf16_tensor, to_bits, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def u8_tensor(a: np.ndarray, device=DEV) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(device)
+
+
+def device_pool8(inp: W.DecodeInputs, k8: np.ndarray, v8: np.ndarray, device=DEV):
+    """Full fp8 pools on the device: NaN codes except the referenced blocks."""
+    shape = (inp.pool.num_blocks,) + k8.shape[1:]
+    k = torch.full(shape, int(W.E4M3_NAN), dtype=torch.uint8, device=device)
+    v = torch.full(shape, int(W.E4M3_NAN), dtype=torch.uint8, device=device)
+    ids = torch.from_numpy(inp.pool.ids).to(device)
+    k.index_copy_(0, ids, u8_tensor(k8, device))
+    v.index_copy_(0, ids, u8_tensor(v8, device))
+    return k, v
+
+
+# ---------------------------------------------------------------------------
+# append
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.0625, 4.0), (0.37, 0.0173),
+                                             (3.1, 1e-3)])
+def test_append_fp8_every_bf16_value(k_scale, v_scale):
+    T, Hkv, D, NB, BS = 128, 4, 128, 16, 16
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    k = allbits.reshape(T, Hkv, D)
+    v = allbits[::-1].copy().reshape(T, Hkv, D)
+    rng = np.random.default_rng(5)
+    slots = rng.permutation(NB * BS)[:T].astype(np.int64)
+    slots[rng.choice(T, 9, replace=False)] = -1          # padding rows write nothing
+    init = rng.integers(0, 256, (NB, BS, Hkv, D), dtype=np.uint8)
+    kc, vc = u8_tensor(init), u8_tensor(init)
+    pa.reshape_and_cache_fp8(bf16_tensor(k), bf16_tensor(v), torch.from_numpy(slots).to(DEV),
+                             kc, vc, k_scale, v_scale)
+    torch.cuda.synchronize()
+    want_k, want_v = O8.append_fp8(k, v, slots, init, init, k_scale, v_scale)
+    for name, got, want, src in (("k", kc, want_k, k), ("v", vc, want_v, v)):
+        got = got.cpu().numpy()
+        # NaN inputs: any NaN code; the slots they land in
+        src_f = W.bf16_bits_to_f32(src)
+        nan_slot = np.zeros(got.shape, bool)
+        for i, s in enumerate(slots):
+            if s >= 0:
+                nan_slot[s // BS, s % BS] = np.isnan(src_f[i])
+        assert np.all((got[nan_slot] & 0x7F) == 0x7F), name
+        diff = (got != want) & ~nan_slot
+        assert not diff.any(), (name, np.argwhere(diff)[:5], got[diff][:5], want[diff][:5])
+
+
+def test_append_fp8_then_decode_end_to_end():
+    """A pool filled through the quantising append from bf16 rows, decoded:
+    the device pool equals the oracle's bit for bit and the decode matches."""
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, D, BS, NB, WM = 5, 12, 2, 128, 16, 64, 12
+    lens = np.array([1, 16, 37, 150, 191], np.int32)
+    perm = rng.permutation(NB)
+    tables = np.zeros((B, WM), np.int32)
+    slots, off = [], 0
+    for b, L in enumerate(lens):
+        n = -(-int(L) // BS)
+        tables[b, :n] = perm[off:off + n]
+        off += n
+        slots += [int(tables[b, t // BS]) * BS + t % BS for t in range(L)]
+    slots = np.asarray(slots, np.int64)
+    T = len(slots)
+    kb = W.f32_to_bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32) * 3)
+    vb = W.f32_to_bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32))
+    ks, vs = 0.011, 0.0042
+    init = np.full((NB, BS, Hkv, D), 0x7F, np.uint8)
+    kc, vc = u8_tensor(init), u8_tensor(init)
+    pa.reshape_and_cache_fp8(bf16_tensor(kb), bf16_tensor(vb), torch.from_numpy(slots).to(DEV),
+                             kc, vc, ks, vs)
+    k8, v8 = O8.append_fp8(kb, vb, slots, init, init, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), k8) and np.array_equal(vc.cpu().numpy(), v8)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    scale = np.float32(1 / np.sqrt(D))
+    for S in (1, 3, 0):
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
+        pa.decode_fp8(bf16_tensor(q), kc, vc, torch.from_numpy(tables).to(DEV),
+                      torch.from_numpy(lens).to(DEV), float(scale), ks, vs, S, out)
+        torch.cuda.synchronize()
+        ref = O8.decode_fp8(q, k8, v8, tables, lens, scale, ks, vs)
+        assert_close(to_f64(out), ref, what=f"S={S}")
+
+
+# ---------------------------------------------------------------------------
+# decode: shape matrix
+# ---------------------------------------------------------------------------
+
+LENS_MIX = (0, 1, 15, 16, 17, 255, 256, 257, 700, 1029)
+
+
+def _small_spec(D, Hq, Hkv, bs, lens, seed):
+    W_ = max(-(-max(lens) // bs), 1) + 1
+    nb = sum(-(-L // bs) for L in lens) + 8
+    return W.DecodeSpec(f"fp8-{D}-{Hq}-{Hkv}-{bs}", len(lens), Hq, Hkv, D, bs, nb, W_,
+                        context_lens=tuple(lens), seed=seed)
+
+
+def _run_fp8(inp, k8, v8, ks, vs, S):
+    s = inp.spec
+    kc, vc = device_pool8(inp, k8, v8)
+    out = torch.empty((s.num_seqs, s.num_q_heads, s.head_dim), dtype=torch.bfloat16, device=DEV)
+    pa.decode_fp8(bf16_tensor(inp.q), kc, vc, torch.from_numpy(inp.block_tables).to(DEV),
+                  torch.from_numpy(inp.context_lens).to(DEV), float(inp.scale), ks, vs, S, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_fp8(inp, k8, v8, ks, vs, rows=None):
+    ct = inp.pool.compact_tables(inp.block_tables, inp.poison_block)
+    if rows is None:
+        return O8.decode_fp8(inp.q, k8, v8, ct, inp.context_lens, inp.scale, ks, vs)
+    out = []
+    for b in rows:
+        out.append(O8.decode_fp8(inp.q[b:b + 1], k8, v8, ct[b:b + 1], inp.context_lens[b:b + 1],
+                                 inp.scale, ks, vs)[0])
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (6, 2), (8, 2), (16, 2)])
+@pytest.mark.parametrize("bs", [16, 256])
+def test_decode_fp8_shapes(D, Hq, Hkv, bs):
+    inp = W.make_decode_inputs(_small_spec(D, Hq, Hkv, bs, LENS_MIX, seed=D + 7 * Hq + bs),
+                               fill="zeros")
+    k8, v8 = W.fp8_codes_like(inp)
+    ks, vs = 0.21, 0.47
+    ref = _oracle_fp8(inp, k8, v8, ks, vs)
+    for S in (1, 4, 0):
+        got = to_f64(_run_fp8(inp, k8, v8, ks, vs, S))
+        assert_close(got, ref, what=f"D={D} Hq={Hq} Hkv={Hkv} bs={bs} S={S}")
+
+
+def test_decode_fp8_many_splits_and_scales():
+    inp = W.make_decode_inputs(_small_spec(128, 28, 4, 16, (3000, 1, 64, 2047), seed=31),
+                               fill="zeros")
+    k8, v8 = W.fp8_codes_like(inp)
+    for ks, vs, S in ((2.0 ** -6, 16.0, 64), (0.9, 0.01, 17), (1.0, 1.0, 256)):
+        ref = _oracle_fp8(inp, k8, v8, ks, vs)
+        assert_close(to_f64(_run_fp8(inp, k8, v8, ks, vs, S)), ref, what=f"{ks} {vs} S={S}")
+
+
+def test_decode_fp8_nan_code_in_context_propagates():
+    inp = W.make_decode_inputs(_small_spec(128, 8, 2, 16, (40, 40), seed=41), fill="zeros")
+    k8, v8 = W.fp8_codes_like(inp)
+    ct = inp.pool.compact_tables(inp.block_tables, inp.poison_block)
+    v8[ct[1, 1], 3, 0, 5] = 0xFF                   # sequence 1, token 19, kv head 0
+    out = to_f64(_run_fp8(inp, k8, v8, 0.5, 0.5, 1))
+    assert np.isnan(out[1, :4, 5]).all()           # the 4 q heads of kv head 0
+    assert np.isfinite(out[0]).all() and np.isfinite(out[1, 4:]).all()
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 12, 4), (128, 16, 2), (64, 24, 4)])
+def test_decode_fp8_equals_bf16_pool_of_its_values(D, Hq, Hkv):
+    """Power-of-two scales: fp8 decode == bf16 decode over the dequantised
+    pool, bit for bit (matrix path on both sides)."""
+    inp = W.make_decode_inputs(_small_spec(D, Hq, Hkv, 16, LENS_MIX, seed=51 + D), fill="zeros")
+    k8, v8 = W.fp8_codes_like(inp)
+    ks, vs = 2.0 ** -3, 2.0 ** 2
+    kb = W.f32_to_bf16_bits((O8.e4m3_decode(k8) * ks).astype(np.float32))
+    vb = W.f32_to_bf16_bits((O8.e4m3_decode(v8) * vs).astype(np.float32))
+    assert np.array_equal(W.bf16_bits_to_f32(kb).astype(np.float64)[k8 != 0x7F],
+                          (O8.e4m3_decode(k8) * ks)[k8 != 0x7F])      # exact in bf16
+    for S in (1, 5):
+        got8 = to_bits(_run_fp8(inp, k8, v8, ks, vs, S))
+        pool = W.CompactPool(inp.pool.num_blocks, inp.pool.ids, kb, vb)
+        shape = (pool.num_blocks,) + kb.shape[1:]
+        nan = torch.tensor(float("nan"), dtype=torch.bfloat16)
+        kc = torch.full(shape, nan, dtype=torch.bfloat16, device=DEV)
+        vc = torch.full(shape, nan, dtype=torch.bfloat16, device=DEV)
+        ids = torch.from_numpy(pool.ids).to(DEV)
+        kc.index_copy_(0, ids, bf16_tensor(kb))
+        vc.index_copy_(0, ids, bf16_tensor(vb))
+        out = torch.empty((len(LENS_MIX), Hq, D), dtype=torch.bfloat16, device=DEV)
+        pa.decode(bf16_tensor(inp.q), kc, vc, torch.from_numpy(inp.block_tables).to(DEV),
+                  torch.from_numpy(inp.context_lens).to(DEV), float(inp.scale), S, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(got8, to_bits(out)), f"S={S}"
+
+
+# ---------------------------------------------------------------------------
+# decode: full-size workloads, sampled rows
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name", ["c2b8", "c3", "c5d"])
+def test_decode_fp8_full_size_sampled(name):
+    spec = W.CONFIGS[name].with_(append=False)
+    inp = W.make_decode_inputs(spec, fill="zeros")
+    k8, v8 = W.fp8_codes_like(inp)
+    ks, vs = 0.3, 0.25
+    got = to_f64(_run_fp8(inp, k8, v8, ks, vs, 0))
+    rows = sorted(set(np.random.default_rng(61).choice(spec.num_seqs, 4, replace=False).tolist()))
+    ref = _oracle_fp8(inp, k8, v8, ks, vs, rows)
+    assert_close(got[rows], ref, what=name)

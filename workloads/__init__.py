@@ -34,7 +34,12 @@ BF16_NAN = np.uint16(0x7FC0)
 BF16_ONE = np.uint16(0x3F80)
 
 # Stream tags: each kind of draw gets its own SeedSequence branch.
-_TAG_LENS, _TAG_PERM, _TAG_Q, _TAG_K, _TAG_V, _TAG_NEWK, _TAG_NEWV = range(7)
+_TAG_LENS, _TAG_PERM, _TAG_Q, _TAG_K, _TAG_V, _TAG_NEWK, _TAG_NEWV, _TAG_K8, _TAG_V8 = range(9)
+
+# fp8 pools store 8-bit float codes (sign bit 7, exponent bits 6..3, mantissa
+# bits 2..0); 0x7F is a NaN code and poisons fp8 storage as BF16_NAN poisons
+# bf16 storage.
+E4M3_NAN = np.uint8(0x7F)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -360,6 +365,34 @@ def make_prefill_inputs(spec: PrefillSpec, *, fill: str = "normal") -> PrefillIn
         nk = normal_bf16(spec.seed, (_TAG_NEWK,), kv_shape)
         nv = normal_bf16(spec.seed, (_TAG_NEWV,), kv_shape)
     return PrefillInputs(spec, q, cu, pool, tables, lens, poison, spec.scale_f32, nk, nv, slots)
+
+
+def random_e4m3_codes(seed: int, tags: Sequence[int], shape) -> np.ndarray:
+    """Random fp8 codes: sign, exponent field uniform in 4..8 and mantissa
+    field uniform in 0..7, so magnitudes lie in [2^-3, 3.75] and no code is
+    NaN."""
+    g = _rng(seed, *tags)
+    sign = g.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    expo = g.integers(4, 9, size=shape, dtype=np.uint8) << 3
+    mant = g.integers(0, 8, size=shape, dtype=np.uint8)
+    return (sign | expo | mant).astype(np.uint8)
+
+
+def fp8_codes_like(inp: "DecodeInputs"):
+    """fp8 pools for the blocks, tables and lengths of ``inp``: each referenced
+    block draws its own codes (streams keyed by seed and block id), and every
+    slot that ``inp``'s bf16 pool poisons holds E4M3_NAN.  Returns the K and V
+    codes, stored densely like ``inp.pool``."""
+    s = inp.spec
+    shape = inp.pool.k.shape
+    k = np.empty(shape, dtype=np.uint8)
+    v = np.empty(shape, dtype=np.uint8)
+    for i, p in enumerate(inp.pool.ids):
+        k[i] = random_e4m3_codes(s.seed, (_TAG_K8, int(p)), shape[1:])
+        v[i] = random_e4m3_codes(s.seed, (_TAG_V8, int(p)), shape[1:])
+    k[inp.pool.k == BF16_NAN] = E4M3_NAN
+    v[inp.pool.v == BF16_NAN] = E4M3_NAN
+    return k, v
 
 
 def algorithmic_decode_bytes(lens, num_q_heads, num_kv_heads, head_dim, block_size) -> int:
