@@ -62,13 +62,15 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="c2b8",
-                   choices=["c2b8", "c2b1", "c3", "c4", "c5d", "c5p"],
-                   help="decode workload timed; c5p (the prefill chunk) only with --kernel-loop")
+                   choices=["c2b8", "c2b1", "c3", "c4", "c5d", "c5p", "c2b8f8", "c4f8"],
+                   help="decode workload timed; c5p (the prefill chunk) and the fp8-pool "
+                        "workloads only with --kernel-loop")
     p.add_argument("--splits", type=int, default=0, help="0 = automatic")
     p.add_argument("--rotate-gib", type=float, default=2.0)
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--others", default="c2b1,c3,c4,c5d,c5p,c5mix,c2b8q2,c2b8q4,c3q4",
+    p.add_argument("--others", default="c2b1,c3,c4,c5d,c5p,c5mix,c2b8q2,c2b8q4,c3q4,"
+                                         "c2b8f8,c3f8,c4f8",
                    help="comma list of extra workloads measured into 'workloads' ('' = none)")
     p.add_argument("--kernel-loop", type=int, default=0,
                    help="profiling mode: launch only the split kernel this many times and exit")
@@ -101,7 +103,8 @@ def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
 class DecodeWorkload:
     """Device-resident inputs of one decode workload with R block rotations."""
 
-    def __init__(self, spec, rotate_gib: float, splits: int, seed: int = 1234, q_len: int = 1):
+    def __init__(self, spec, rotate_gib: float, splits: int, seed: int = 1234, q_len: int = 1,
+                 kv_fp8: bool = False):
         import numpy as np
         import torch
 
@@ -116,20 +119,33 @@ class DecodeWorkload:
             spec.num_q_heads
         nblk = [(int(L) + bs - 1) // bs for L in self.lens_np]
         per_rot = sum(nblk)
-        kv_bytes = int(self.lens_np.sum()) * Hkv * D * 2 * 2
+        elem = 1 if kv_fp8 else 2
+        kv_bytes = int(self.lens_np.sum()) * Hkv * D * elem * 2
         self.R = max(1, math.ceil(rotate_gib * 2**30 / kv_bytes))
         NB = max(spec.num_blocks, self.R * per_rot + 1)
         self.NB = NB
         g = torch.Generator(device=dev)
         g.manual_seed(seed)
         shape = (NB, bs, Hkv, D)
-        self.k_cache = torch.empty(shape, dtype=torch.bfloat16, device=dev)
-        self.v_cache = torch.empty(shape, dtype=torch.bfloat16, device=dev)
-        step = max(1, (256 << 20) // (bs * Hkv * D * 2))
+        self.kv_fp8 = kv_fp8
+        self.k_scale, self.v_scale = 0.25, 0.25
+        dt = torch.uint8 if kv_fp8 else torch.bfloat16
+        self.k_cache = torch.empty(shape, dtype=dt, device=dev)
+        self.v_cache = torch.empty(shape, dtype=dt, device=dev)
+        step = max(1, (256 << 20) // (bs * Hkv * D * elem))
         for i in range(0, NB, step):
             j = min(NB, i + step)
-            self.k_cache[i:j].normal_(generator=g)
-            self.v_cache[i:j].normal_(generator=g)
+            for t in (self.k_cache, self.v_cache):
+                if kv_fp8:
+                    # fp8 codes: random sign and mantissa, exponent field 4..8
+                    # (magnitudes 2^-3 .. 3.75), never NaN
+                    sm = torch.randint(0, 256, t[i:j].shape, generator=g, device=dev,
+                                       dtype=torch.int16) & 0x87
+                    ex = torch.randint(4, 9, t[i:j].shape, generator=g, device=dev,
+                                       dtype=torch.int16) << 3
+                    t[i:j] = (sm | ex).to(torch.uint8)
+                else:
+                    t[i:j].normal_(generator=g)
         perm = torch.randperm(NB, generator=g, device=dev).cpu().numpy()
         W_ = spec.max_blocks_per_seq
         tables, slots = [], []
@@ -157,9 +173,12 @@ class DecodeWorkload:
         ws = pa.decode_multi_workspace_size(B, q_len, Hq, D, self.S)
         self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         self.pa = pa
-        # q and out once per query token; the cache once whatever q_len
+        # q and out once per query token; the cache once whatever q_len; fp8
+        # pools move one byte per K/V element
         self.decode_bytes = (W.algorithmic_decode_bytes(self.lens_np, Hq, Hkv, D, bs)
                              + (q_len - 1) * B * Hq * D * 2 * 2)
+        if kv_fp8:
+            self.decode_bytes -= int(self.lens_np.sum()) * Hkv * D * 2
         self.append_bytes = B * Hkv * D * 2 * 2 * 2 + B * 8
         self.decode_flop = 4 * D * Hq * int(self.lens_np.sum())
 
@@ -174,6 +193,12 @@ class DecodeWorkload:
         """Multi-token decode: q_len query tokens per sequence, causal."""
         self.pa.decode_multi(self.q, self.k_cache, self.v_cache, self.tables[r], self.lens,
                              self.scale, self.S, self.out, workspace=self.ws)
+
+    def step_fp8(self, r: int):
+        """Single-token decode over fp8 pools."""
+        self.pa.decode_fp8(self.q, self.k_cache, self.v_cache, self.tables[r], self.lens,
+                           self.scale, self.k_scale, self.v_scale, self.S, self.out,
+                           workspace=self.ws)
 
     def step_plain(self, r: int):
         """Single-token decode without the append."""
@@ -739,10 +764,35 @@ def measure_multi(name, args, steps, warmup):
     return one, rec
 
 
+FP8_WORKLOADS = {"c2b8f8": "c2b8", "c3f8": "c3", "c4f8": "c4"}
+
+
+def measure_fp8(name, args, steps, warmup):
+    """Single-token decode over fp8 pools on a decode workload's shapes and
+    lengths, against the same decode over bf16 pools."""
+    import torch
+    import workloads as W
+    base = FP8_WORKLOADS[name]
+    spec = W.CONFIGS[base]
+    wl = DecodeWorkload(spec, args.rotate_gib, args.splits, kv_fp8=True)
+    ms = time_graph(wl.step_fp8, wl.R, steps, warmup)
+    rec = {"workload": name, "base_workload": base, "kv": "fp8 e4m3, per-tensor scales",
+           "us_per_call": ms * 1e3, "gbps": wl.decode_bytes / (ms * 1e-3) / 1e9,
+           "decode_bytes": wl.decode_bytes, "splits": wl.S, "rotations": wl.R}
+    del wl
+    torch.cuda.empty_cache()
+    one = DecodeWorkload(spec, args.rotate_gib, args.splits)
+    ms1 = time_graph(one.step_plain, one.R, steps, warmup)
+    rec["bf16_us_per_call"] = ms1 * 1e3
+    rec["speedup_over_bf16"] = ms1 / ms
+    return one, rec
+
+
 def main(argv=None):
     args = parse_args(argv)
-    if args.workload == "c5p" and not args.kernel_loop:
-        raise SystemExit("--workload c5p is a profiling mode: use it with --kernel-loop")
+    if args.workload in ("c5p", "c2b8f8", "c4f8") and not args.kernel_loop:
+        raise SystemExit(f"--workload {args.workload} is a profiling mode: use it with "
+                         "--kernel-loop")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding of this path is a design note, not a measured configuration.",
@@ -785,6 +835,15 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"workload": "c5p", "kernel_launches": args.kernel_loop,
                           "splits": wl.S, "flop_per_call": wl.flop}))
+        return
+    if args.kernel_loop and args.workload in FP8_WORKLOADS:
+        wl = DecodeWorkload(W.CONFIGS[FP8_WORKLOADS[args.workload]], args.rotate_gib, args.splits,
+                            kv_fp8=True)
+        for i in range(args.kernel_loop):
+            wl.step_fp8(i % wl.R)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": args.workload, "calls": args.kernel_loop,
+                          "splits": wl.S, "decode_bytes_per_call": wl.decode_bytes}))
         return
     if args.kernel_loop:
         wl = DecodeWorkload(W.CONFIGS[args.workload], args.rotate_gib, args.splits)
@@ -836,7 +895,11 @@ def main(argv=None):
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         del wl
         torch.cuda.empty_cache()
-        if name in MULTI_WORKLOADS:
+        if name in FP8_WORKLOADS:
+            wl, rec = measure_fp8(name, args, min(args.steps, 100), min(args.warmup, 10))
+            msg = (f"fp8 pools: {rec['us_per_call']:.2f} us/call, {rec['gbps']:.1f} GB/s; bf16 "
+                   f"{rec['bf16_us_per_call']:.2f} us (x{rec['speedup_over_bf16']:.2f})")
+        elif name in MULTI_WORKLOADS:
             wl, rec = measure_multi(name, args, min(args.steps, 100), min(args.warmup, 10))
             msg = (f"q_len {rec['q_len']}: {rec['us_per_call']:.2f} us/call, {rec['gbps']:.1f} GB/s;"
                    f" single-token {rec['single_token_us_per_call']:.2f} us "
