@@ -499,16 +499,25 @@ def _read_csv(directory: str, suffix: str):
 
 def ingest_trace(directory: str, out_name: str, command: str):
     """rocprofv3 --stats CSV -> a short markdown summary under profiles/."""
+    import statistics
     rows = _read_csv(directory, "kernel_stats.csv")
+    # per-dispatch durations for the median and 90th percentile
+    durs = {}
+    for r in _read_csv(directory, "kernel_trace.csv"):
+        k = _short_kernel(r["Kernel_Name"])
+        durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = [f"# Kernel durations: {out_name}", "", "Command (run from /tmp with TMPDIR=/tmp):", "",
              "```", command, "```", "",
-             "| kernel | calls | avg us | min us | max us | % of GPU time |",
-             "|---|---|---|---|---|---|"]
+             "| kernel | calls | avg us | median us | p90 us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|---|---|"]
     for r in rows:
         k = _short_kernel(r["Name"])
         if not k.startswith(("decode", "append", "prefill")):
             continue
+        d = sorted(durs.get(k, [float("nan")]))
+        p90 = d[min(len(d) - 1, int(0.9 * len(d)))]
         lines.append(f"| `{k}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{statistics.median(d):.2f} | {p90:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
     path = os.path.join(PROFILES, out_name + ".md")
@@ -675,6 +684,57 @@ def cpu_baseline(spec, seconds: float):
             "us_per_call": round(t / n * 1e6, 1)}
 
 
+def _oracle_sequence_worker(job):
+    """One sequence of a workload through the oracle, repeatedly, for about
+    `seconds`, in a fresh process with one BLAS thread.  Returns (bytes, s)."""
+    name, b, seconds = job
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import workloads as W
+    spec = W.CONFIGS[name]
+    inp = W.make_decode_inputs(spec)
+    ct = inp.pool.compact_tables(inp.block_tables, inp.poison_block)
+    lens = inp.context_lens[b:b + 1]
+    per_call = W.algorithmic_decode_bytes(lens, spec.num_q_heads, spec.num_kv_heads,
+                                          spec.head_dim, spec.block_size)
+    n = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            oracle.decode(inp.q[b:b + 1], inp.pool.k, inp.pool.v, ct[b:b + 1], lens, inp.scale)
+            n += 1
+            t = time.perf_counter() - t0
+            if t >= seconds:
+                break
+    return per_call * n, t
+
+
+def cpu_baseline_parallel(spec, seconds: float):
+    """The same oracle over the workload's sequences in parallel worker
+    processes (started fresh, not forked from this GPU process), one sequence
+    and one BLAS thread each."""
+    import multiprocessing as mp
+    workers = min(spec.num_seqs, len(os.sched_getaffinity(0)), 16)
+    jobs = [(_config_key(spec), b, seconds) for b in range(spec.num_seqs)]
+    with mp.get_context("spawn").Pool(workers) as pool:
+        res = pool.map(_oracle_sequence_worker, jobs, chunksize=1)
+    total = sum(r[0] for r in res)
+    # sequences beyond the worker count run in later rounds; the wall time is
+    # the sum over rounds of the slowest worker of each round
+    rounds = [max(r[1] for r in res[i:i + workers]) for i in range(0, len(res), workers)]
+    wall = sum(rounds)
+    return {"value": round(total / wall / 1e9, 4), "unit": "GB/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"the same oracle, {spec.num_seqs} sequences over {workers} worker processes "
+                      f"(one BLAS thread each), about {seconds:.0f} s per sequence"}
+
+
+def _config_key(spec):
+    import workloads as W
+    return next(k for k, v in W.CONFIGS.items() if v == spec)
+
+
 def measure(name, args, steps, warmup, with_kernel=True):
     import workloads as W
     spec = W.CONFIGS[name]
@@ -697,6 +757,39 @@ def measure(name, args, steps, warmup, with_kernel=True):
         rec["kernel_avg_us"] = avg * 1e3
         rec["kernel_gbps"] = wl.decode_bytes / (avg * 1e-3) / 1e9
     return wl, rec
+
+
+def measure_read_ceiling():
+    """A measured streaming-read rate on this GPU, for context next to the
+    8 TB/s peak: torch's sum (fp32 accumulation) over cold bf16 buffers of
+    32 MiB (the size of the ctx-4096 batch-8 decode) and of 1 GiB, rotating
+    over 2 GiB so that no read hits the last-level cache.  A plain library
+    reduction, so a lower bound on what a read kernel can reach."""
+    import torch
+    res = {}
+    for mib in (32, 1024):
+        nbuf = max(2, 2048 // mib)
+        bufs = [torch.empty(mib << 19, dtype=torch.bfloat16, device="cuda:0") for _ in range(nbuf)]
+        for b in bufs:
+            b.fill_(1.0)
+        out = torch.empty((), dtype=torch.float32, device="cuda:0")
+        for b in bufs[:2]:
+            torch.sum(b, dtype=torch.float32, out=out)
+        n = 2 * nbuf
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(n):
+            torch.sum(bufs[i % nbuf], dtype=torch.float32, out=out)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / n
+        res[f"read_{mib}MiB_gbps"] = round((mib << 20) / (ms * 1e-3) / 1e9, 1)
+        del bufs
+        torch.cuda.empty_cache()
+    res["probe"] = ("torch.sum over cold bf16 buffers (fp32 accumulation); a library reduction, "
+                    "so a lower bound on the streaming read ceiling")
+    return res
 
 
 def measure_block_manager(seed: int = 77):
@@ -927,6 +1020,9 @@ def main(argv=None):
           f"{bm_rec['admit_us']:.1f} us; {bm_rec['prefix_cached_tokens']} prompt tokens from the "
           "prefix cache", file=sys.stderr, flush=True)
     others["host_block_manager"] = bm_rec
+    ceiling = measure_read_ceiling()
+    print(f"[bench] measured read rate (torch.sum, cold): 32 MiB {ceiling['read_32MiB_gbps']:.0f} "
+          f"GB/s, 1 GiB {ceiling['read_1024MiB_gbps']:.0f} GB/s", file=sys.stderr, flush=True)
 
     spec = W.CONFIGS[args.workload]
     achieved = main_rec["kernel_gbps"]
@@ -960,12 +1056,15 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": "decode_split_kernel", "kernel_avg_us": round(main_rec["kernel_avg_us"], 3),
-                     "algorithmic_bytes_per_launch": main_rec["decode_bytes"]},
+                     "algorithmic_bytes_per_launch": main_rec["decode_bytes"],
+                     "frac_of_measured_read_32MiB": round(achieved / ceiling["read_32MiB_gbps"], 4)},
+        "measured_read_ceiling": ceiling,
         "workloads": others,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
+        line["cpu_baseline"]["parallel"] = cpu_baseline_parallel(spec, args.cpu_seconds / 2)
     print(json.dumps(line), flush=True)
 
 
