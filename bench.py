@@ -774,13 +774,13 @@ def measure_read_ceiling():
             b.fill_(1.0)
         out = torch.empty((), dtype=torch.float32, device="cuda:0")
         for b in bufs[:2]:
-            torch.sum(b, dtype=torch.float32, out=out)
+            torch.sum(b, dim=0, dtype=torch.float32, out=out)
         n = 2 * nbuf
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         for i in range(n):
-            torch.sum(bufs[i % nbuf], dtype=torch.float32, out=out)
+            torch.sum(bufs[i % nbuf], dim=0, dtype=torch.float32, out=out)
         e.record()
         torch.cuda.synchronize()
         ms = s.elapsed_time(e) / n
