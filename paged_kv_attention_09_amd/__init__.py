@@ -80,6 +80,8 @@ SIGNATURES = {
     "pa_bm_preempt": (_I, [_VP, _VP]),
     "pa_bm_block_tables": (_I, [_VP, _VP, _I, _VP, _VP]),
     "pa_bm_stats": (_I, [_VP, _VP, _VP, _VP, _VP]),
+    # measurement probe (include/pagedattn_probe.h)
+    "pa_read_probe": (_I, [_VP, _SZ, _VP, _I, _VP]),
 }
 
 _lib = None

@@ -18,7 +18,7 @@ OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libpagedattn.so")
 # The block manager (pa_block_manager.cpp) is host code; hipcc compiles it as C++.
 SOURCES = ["pa_api.hip", "pa_append.hip", "pa_decode.hip", "pa_prefill.hip",
-           "pa_block_manager.cpp"]
+           "pa_block_manager.cpp", "pa_probe.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of the generated code (-packed-fp32-ops).
@@ -48,7 +48,7 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source and link the shared library.  Always rebuilds."""
     os.makedirs(OUT_DIR, exist_ok=True)
     objs = [os.path.join(OUT_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
