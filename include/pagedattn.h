@@ -301,7 +301,8 @@ int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
                size_t workspace_bytes, void *stream);
 
 /* Workspace bytes pa_prefill needs for a given split count (0 when
- * num_splits <= 1).  Returns 0 for invalid arguments. */
+ * num_splits <= 1): each piece's normalised output rows, rounded to bf16,
+ * then their fp32 log-sum-exp.  Returns 0 for invalid arguments. */
 size_t pa_prefill_workspace_size(int num_seqs, int max_q_len, int num_q_heads, int head_dim,
                                  int num_splits);
 

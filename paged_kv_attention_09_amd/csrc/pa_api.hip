@@ -390,7 +390,7 @@ size_t pa_prefill_workspace_size(int num_seqs, int max_q_len, int num_q_heads, i
   if (num_seqs <= 0 || max_q_len <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
   if (num_splits <= 1 || num_splits > PA_MAX_SPLITS) return 0;
   const size_t rows = (size_t)num_seqs * max_q_len * num_q_heads * num_splits;
-  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
+  const size_t o_bytes = (rows * head_dim * sizeof(uint16_t) + 255) / 256 * 256;  // bf16 rows
   return o_bytes + (rows * sizeof(float) + 255) / 256 * 256;
 }
 
@@ -460,8 +460,8 @@ int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
                                                   a.num_splits);
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
     const size_t rows = (size_t)num_seqs * max_q_len * num_q_heads * a.num_splits;
-    a.o_part = (float *)workspace;
-    a.lse_part = (float *)((char *)workspace + (rows * head_dim * sizeof(float) + 255) / 256 * 256);
+    a.o_part = (uint16_t *)workspace;
+    a.lse_part = (float *)((char *)workspace + (rows * head_dim * sizeof(uint16_t) + 255) / 256 * 256);
   }
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = pa::launch_prefill(a, head_dim, num_q_heads / num_kv_heads, s);

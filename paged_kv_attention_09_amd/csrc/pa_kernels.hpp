@@ -45,7 +45,7 @@ struct PrefillArgs {
   const int32_t *block_tables;
   const int32_t *context_lens;
   uint16_t *out;              // [Tq, Hq, D]
-  float *o_part;              // [Tq, Hq, S, D] when the key range is split, else null
+  uint16_t *o_part;           // bf16 [Tq, Hq, S, D] when the key range is split, else null
   float *lse_part;            // [Tq, Hq, S]
   float scale_log2;
   int num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, bs_shift;

@@ -358,7 +358,8 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const f32x4 v = o[db][nb] * inv;
-        *(float4 *)(a.o_part + prow * D + 16 * db + 4 * q4) = float4{v[0], v[1], v[2], v[3]};
+        *(uint2 *)(a.o_part + prow * D + 16 * db + 4 * q4) =
+            uint2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
       }
       if (q4 == 0) a.lse_part[prow] = l != 0.f ? m[nb] + log2_fast(l) : -INFINITY;
     }
@@ -389,13 +390,28 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int r
   const int S = a.num_splits;
   const int ns = min(S, p / a.split_len + 1);
   const float *lse = a.lse_part + (size_t)r * S;
-  const float *op = a.o_part + (size_t)r * S * D + lane * PER;
+  const uint16_t *op = a.o_part + (size_t)r * S * D + lane * PER;
+  // a piece's PER bf16 values of this lane's columns, widened to fp32
+  auto load_piece = [&](int k, float (&v)[PER]) {
+    if constexpr (PER == 2) {
+      const uint32_t w = *(const uint32_t *)(op + (size_t)k * D);
+      v[0] = bf16_lo(w);
+      v[1] = bf16_hi(w);
+    } else {
+      v[0] = bf16_lo(op[(size_t)k * D]);
+    }
+  };
 
   float ov[BATCH][PER];
 #pragma unroll
-  for (int k = 0; k < BATCH; ++k)
+  for (int k = 0; k < BATCH; ++k) {
+    if (k < ns) {
+      load_piece(k, ov[k]);
+    } else {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) ov[k][e] = k < ns ? op[(size_t)k * D + e] : 0.f;
+      for (int e = 0; e < PER; ++e) ov[k][e] = 0.f;
+    }
+  }
   float x[4], mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -422,9 +438,14 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int r
     for (int e = 0; e < PER; ++e) acc[e] += w_l[wv][k] * ov[k][e];
   for (int s0 = BATCH; s0 < ns; s0 += BATCH) {
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k)
+    for (int k = 0; k < BATCH; ++k) {
+      if (s0 + k < ns) {
+        load_piece(s0 + k, ov[k]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < PER; ++e) ov[k][e] = s0 + k < ns ? op[(size_t)(s0 + k) * D + e] : 0.f;
+        for (int e = 0; e < PER; ++e) ov[k][e] = 0.f;
+      }
+    }
 #pragma unroll
     for (int k = 0; k < BATCH; ++k)
 #pragma unroll

@@ -184,7 +184,7 @@ def test_prefill_planning():
     assert L.pa_prefill_plan_splits(1, 512, 4, 16, 256, 256) == 4
     assert L.pa_prefill_plan_splits(8, 512, 8, 16, 256, 256) == 1
     rows = 1 * 512 * 28 * 4
-    want = (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    want = (rows * 128 * 2 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256   # bf16 rows
     assert L.pa_prefill_workspace_size(1, 512, 28, 128, 4) == want
     assert L.pa_prefill_workspace_size(1, 512, 28, 128, 1) == 0
 

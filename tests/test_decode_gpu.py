@@ -54,6 +54,18 @@ def test_large_batch_decode():
     assert_close(_run(case, 0), case.ref, what="c4")
 
 
+@pytest.mark.parametrize("bs,Hq,Hkv,S", [(16, 12, 2, 0), (16, 12, 2, 256), (256, 28, 4, 0),
+                                          (256, 28, 4, 3)])
+def test_long_context_decode(bs, Hq, Hkv, S):
+    """Contexts of 64K tokens (a 4096-entry table at block size 16), one
+    sequence ending mid-block, auto, maximal and odd split counts."""
+    W_ = 65536 // bs
+    spec = W.DecodeSpec(f"long-{bs}", 2, Hq, Hkv, 128, bs, 2 * W_ + 8, W_,
+                        context_lens=(65536, 40001), seed=7000 + bs)
+    case = DecodeCase(W.make_decode_inputs(spec, fill="normal"))
+    assert_close(_run(case, S), case.ref, what=f"long bs={bs} S={S}")
+
+
 def test_mixed_batch_decode_part():
     """The 64 decode sequences of the mixed batch (lengths 512..4096, group 7)."""
     case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c5d"]))
