@@ -126,7 +126,7 @@ class DecodeWorkload:
         self.NB = NB
         g = torch.Generator(device=dev)
         g.manual_seed(seed)
-        shape = (NB, bs, Hkv, D)
+        shape = (NB, Hkv, bs, D) if kv_fp8 else (NB, bs, Hkv, D)   # fp8 pools are head-major
         self.kv_fp8 = kv_fp8
         self.k_scale, self.v_scale = 0.25, 0.25
         dt = torch.uint8 if kv_fp8 else torch.bfloat16

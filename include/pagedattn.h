@@ -178,10 +178,14 @@ size_t pa_decode_multi_workspace_size(int num_seqs, int q_len, int num_q_heads, 
 
 /*
  * FP8 KV pages.  The pools hold one byte per element: k_cache, v_cache are
- * [num_blocks, block_size, num_kv_heads, head_dim] uint8 codes of the OCP
+ * [num_blocks, num_kv_heads, block_size, head_dim] uint8 codes of the OCP
  * 8-bit float format E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa
  * bits, subnormals, no infinities, 0x7F / 0xFF NaN, largest finite 448),
- * halving the pool's bytes and what a decode step reads.  K and V each carry
+ * halving the pool's bytes and what a decode step reads.  The layout is
+ * head-major, unlike the bf16 pools: the block_size rows of one kv head in
+ * one block are contiguous, so a decode workgroup reads long sequential
+ * runs; slot s is row s % block_size of block s / block_size for every kv
+ * head.  K and V each carry
  * one fp32 scale for the whole pool: a code c stands for e4m3(c) * scale.
  * Source: quantised KV cache storage, "Mini-Infer: A High-Performance LLM
  * Inference Acceleration Engine for Production Environments" (zingnex.cn

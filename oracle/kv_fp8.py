@@ -13,7 +13,9 @@ exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities, codes
 0x7F / 0xFF are NaN, largest finite value 448); one fp32 scale per tensor (K
 and V separately), the stored code being e4m3(clamp(x * (1 / scale),
 -448, 448)) rounded to nearest even, with 1 / scale and the product taken in
-fp32; the K and V a read uses are code value * scale.
+fp32; the K and V a read uses are code value * scale.  Pools are head-major,
+[num_blocks, num_kv_heads, block_size, head_dim]: slot s is row s % bs of
+block s // bs for every kv head.
 """
 from __future__ import annotations
 
@@ -74,26 +76,30 @@ def quantize(x_bf16_bits: np.ndarray, scale) -> np.ndarray:
 
 def append_fp8(new_k: np.ndarray, new_v: np.ndarray, slot_mapping: np.ndarray,
                k_cache8: np.ndarray, v_cache8: np.ndarray, k_scale, v_scale):
-    """Copies of the fp8 pools with row i of new_k / new_v (bf16 bits),
-    quantised, written to slot slot_mapping[i]; negative slots skip."""
+    """Copies of the fp8 pools [NB, Hkv, bs, D] with row i of new_k / new_v
+    ([T, Hkv, D] bf16 bits), quantised, written to slot slot_mapping[i] of
+    every kv head; negative slots skip."""
     kc, vc = k_cache8.copy(), v_cache8.copy()
-    bs = kc.shape[1]
+    bs = kc.shape[2]
     for i, s in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
         if s < 0:
             continue
-        kc[s // bs, s % bs] = quantize(new_k[i], k_scale)
-        vc[s // bs, s % bs] = quantize(new_v[i], v_scale)
+        kc[s // bs, :, s % bs] = quantize(new_k[i], k_scale)
+        vc[s // bs, :, s % bs] = quantize(new_v[i], v_scale)
     return kc, vc
 
 
 def decode_fp8(q: np.ndarray, k_cache8: np.ndarray, v_cache8: np.ndarray,
                block_tables: np.ndarray, context_lens: np.ndarray, scale, k_scale,
                v_scale) -> np.ndarray:
-    """Decode over fp8 pools: K = code value * k_scale, V = code value * v_scale
-    (scales widened from fp32), then plain attention.  q bf16 bits [B, Hq, D];
-    returns fp64 [B, Hq, D]."""
+    """Decode over fp8 pools [NB, Hkv, bs, D]: K = code value * k_scale,
+    V = code value * v_scale (scales widened from fp32), then plain attention.
+    q bf16 bits [B, Hq, D]; returns fp64 [B, Hq, D]."""
     B, Hq, D = q.shape
-    Hkv = k_cache8.shape[2]
+    Hkv = k_cache8.shape[1]
+    # token-major views [NB, bs, Hkv, D] for the shared gather
+    k_cache8 = np.transpose(k_cache8, (0, 2, 1, 3))
+    v_cache8 = np.transpose(v_cache8, (0, 2, 1, 3))
     sc = np.float64(np.float32(scale))
     ks, vs = np.float64(np.float32(k_scale)), np.float64(np.float32(v_scale))
     qf = (np.asarray(q, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32) \

@@ -137,11 +137,14 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None) -> None:
 
 
 def _pool_dims(k_cache, v_cache, dtype=torch.bfloat16):
+    """(NB, bs, Hkv, D) of a pool pair: bf16 pools are [NB, bs, Hkv, D], fp8
+    (uint8) pools head-major [NB, Hkv, bs, D]."""
     _need(k_cache, "k_cache", dtype, 4)
     _need(v_cache, "v_cache", dtype, 4, k_cache.device)
     if k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache shapes differ")
-    return tuple(int(x) for x in k_cache.shape)     # NB, bs, Hkv, D
+    NB, a, b, D = (int(x) for x in k_cache.shape)
+    return (NB, b, a, D) if dtype == torch.uint8 else (NB, a, b, D)
 
 
 def reshape_and_cache(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
@@ -155,7 +158,7 @@ def reshape_and_cache(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None
 
 def reshape_and_cache_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale: float, v_scale: float,
                           stream=None) -> None:
-    """As reshape_and_cache into fp8 pools (uint8 e4m3 codes [NB, bs, Hkv, D]):
+    """As reshape_and_cache into fp8 pools (uint8 e4m3 codes [NB, Hkv, bs, D]):
     element x is stored as e4m3(clamp(x / scale, -448, 448)), per-tensor fp32
     scales."""
     NB, bs, Hkv, D, T, dev = _append_dims(k, v, slot_mapping, k_cache, v_cache, torch.uint8)
@@ -239,7 +242,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_sp
 def decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float, k_scale: float,
                v_scale: float, num_splits: int, out, stream=None,
                workspace: Optional[torch.Tensor] = None):
-    """decode over fp8 pools (uint8 e4m3 codes [NB, bs, Hkv, D]): K and V are
+    """decode over fp8 pools (uint8 e4m3 codes [NB, Hkv, bs, D]): K and V are
     the codes' values times k_scale and v_scale."""
     NB, bs, Hkv, D, B, Hq, W, dev = _decode_dims(q, k_cache, v_cache, block_tables, context_lens,
                                                  torch.uint8)

@@ -115,6 +115,8 @@ int append_rows(const void *k, const void *v, const int64_t *slot_mapping, void 
   a.fp8 = fp8 ? 1 : 0;
   a.inv_k_scale = fp8 ? 1.0f / k_scale : 1.0f;
   a.inv_v_scale = fp8 ? 1.0f / v_scale : 1.0f;
+  a.bs_shift = log2_exact(block_size);
+  a.head_vecs = head_dim / 8;
   return pa::launch_append(a, head_dim, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

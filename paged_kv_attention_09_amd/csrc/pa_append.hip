@@ -35,8 +35,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int vec_per_r
   }
 }
 
-// fp8 pools: each lane reads 8 bf16 of K and of V (16 bytes each) and
-// writes their 8 codes (8 bytes each).  The code of x is e4m3 of
+// fp8 pools ([NB, Hkv, bs, D], head-major): each lane reads 8 bf16 of K and
+// of V (16 bytes each) and writes their 8 codes (8 bytes each) to the row of
+// its kv head.  The code of x is e4m3 of
 // clamp(x * (1 / scale), -448, 448), product in fp32, rounded to nearest
 // even; the comparisons keep a NaN product NaN.
 __device__ __forceinline__ float clamp448(float y) {
@@ -66,7 +67,11 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, int vec_p
     const int64_t e = idx - i * vec_per_row;
     const int64_t s = a.slot_mapping[i];
     if (s < 0) continue;
-    const int64_t dst = s * vec_per_row + e;
+    // head-major pool: row (block, head, offset), 8 codes per vector
+    const int64_t h = e / a.head_vecs, ve = e - h * a.head_vecs;
+    const int64_t nh = vec_per_row / a.head_vecs;
+    const int64_t blk = s >> a.bs_shift, off = s & ((1 << a.bs_shift) - 1);
+    const int64_t dst = (((blk * nh + h) << a.bs_shift) + off) * a.head_vecs + ve;
     kc[dst] = quantize8(k[idx], a.inv_k_scale);
     vc[dst] = quantize8(v[idx], a.inv_v_scale);
   }

@@ -212,9 +212,18 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   const uint32_t my_off = lds_offset(my);
   const uint32_t q_off = lds_offset(qlds);
 
-  const uint32_t RS = (uint32_t)a.num_kv_heads * RB;  // bytes between token rows
-  const char *kbase = (const char *)a.k_cache + (size_t)g * RB;
-  const char *vbase = (const char *)a.v_cache + (size_t)g * RB;
+  // bf16 pools [NB, bs, Hkv, D]: token rows of one kv head are Hkv rows
+  // apart.  fp8 pools [NB, Hkv, bs, D]: a (block, kv head) is one contiguous
+  // run of bs rows.
+  const uint32_t RS = KV8 ? (uint32_t)RB : (uint32_t)a.num_kv_heads * RB;  // between token rows
+  const size_t head_off = KV8 ? ((size_t)g * RB << bs_shift) : (size_t)g * RB;
+  const char *kbase = (const char *)a.k_cache + head_off;
+  const char *vbase = (const char *)a.v_cache + head_off;
+  // bytes from the pool start to row `off` of block `blk` (this kv head)
+  auto row_offset = [&](int blk, int off) {
+    const size_t rows = ((size_t)(uint32_t)blk << bs_shift);
+    return KV8 ? (rows * a.num_kv_heads + (size_t)off) * RB : (rows + (size_t)off) * RS;
+  };
 
   // Fused append (single query token only): the wave that owns the
   // sequence's last token writes the new K/V row of this kv head to that
@@ -251,9 +260,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 
   auto issue_chunk = [&](int ci, int stage, int blk) {
     const int tc = t0 + ci * kChunk;
-    const size_t row0 = ((size_t)(uint32_t)blk << bs_shift) + (size_t)(tc & bs_mask);
-    const char *kb = kbase + row0 * RS;
-    const char *vb = vbase + row0 * RS;
+    const size_t boff = row_offset(blk, tc & bs_mask);
+    const char *kb = kbase + boff;
+    const char *vb = vbase + boff;
     const int nvalid = t1 - tc;
     const uint32_t st = my_off + stage * STB;
 #pragma unroll

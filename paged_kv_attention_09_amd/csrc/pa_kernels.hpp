@@ -13,8 +13,10 @@ struct AppendArgs {
   void *k_cache, *v_cache;    // bf16 pools, or fp8 (e4m3) pools when fp8 is set
   int64_t num_tokens;
   int row_elems;              // num_kv_heads * head_dim
-  int fp8;
+  int fp8;                    // fp8 pools, [NB, Hkv, bs, D] (bf16 pools: [NB, bs, Hkv, D])
   float inv_k_scale, inv_v_scale;  // fp8: 1 / scale, rounded to fp32
+  int bs_shift;               // fp8: log2(block_size)
+  int head_vecs;              // fp8: head_dim / 8
 };
 
 struct DecodeArgs {

@@ -398,13 +398,13 @@ def pin_fp8_codec(kv):
 
 def pin_fp8_quantize_and_append(kv, seed=18):
     """F2: the appended codes are torch's conversion of clamp(x * (1/scale))
-    with the reciprocal and product in fp32, written at the slots (negative
-    slots skip)."""
+    with the reciprocal and product in fp32, written at the slots of the
+    head-major pools [NB, Hkv, bs, D] (negative slots skip)."""
     rng = np.random.default_rng(seed)
     Hkv, D, bs, NB = 2, 8, 4, 6
     nk = W.f32_to_bf16_bits(rng.standard_normal((5, Hkv, D), dtype=np.float32) * 300)
     nv = W.f32_to_bf16_bits(rng.standard_normal((5, Hkv, D), dtype=np.float32))
-    kc = np.full((NB, bs, Hkv, D), 0x7F, np.uint8)
+    kc = np.full((NB, Hkv, bs, D), 0x7F, np.uint8)
     vc = kc.copy()
     slots = np.array([3, -1, 9, 22, 4], np.int64)
     ks, vs = np.float32(0.37), np.float32(0.011)
@@ -415,10 +415,11 @@ def pin_fp8_quantize_and_append(kv, seed=18):
         for new, cache, sc in ((nk, k2, ks), (nv, v2, vs)):
             x = (new[i].astype(np.uint32) << np.uint32(16)).view(np.float32)
             y = np.clip(x * (np.float32(1) / sc), np.float32(-448), np.float32(448))
-            assert np.array_equal(cache[s // bs, s % bs], _torch_e4m3(y))
-    untouched = np.ones((NB, bs), bool)
+            for h in range(Hkv):
+                assert np.array_equal(cache[s // bs, h, s % bs], _torch_e4m3(y[h]))
+    untouched = np.ones((NB, Hkv, bs), bool)
     for s in slots[slots >= 0]:
-        untouched[s // bs, s % bs] = False
+        untouched[s // bs, :, s % bs] = False
     assert (k2[untouched] == 0x7F).all() and (v2[untouched] == 0x7F).all()
     assert (k2[~untouched] != 0x7F).any()
     # values beyond the range clamp to the largest finite code
@@ -429,7 +430,8 @@ def pin_fp8_quantize_and_append(kv, seed=18):
 def pin_fp8_decode_reduces_to_bf16(kv, seed=19):
     """F3: with power-of-two scales every dequantised value is exactly a bf16
     value, so decode over fp8 pools equals the (pinned) bf16 decode over the
-    dequantised pools, bit for bit."""
+    dequantised pools, bit for bit (the fp8 pools head-major
+    [NB, Hkv, bs, D], the bf16 ones [NB, bs, Hkv, D])."""
     import oracle.paged_attention as pa_oracle
     rng = np.random.default_rng(seed)
     NB, bs, Hkv, D, B, Hq = 12, 4, 2, 8, 3, 6
@@ -444,7 +446,8 @@ def pin_fp8_decode_reduces_to_bf16(kv, seed=19):
     tables = rng.permutation(NB)[:B * 4].reshape(B, 4).astype(np.int32)
     lens = np.array([1, 9, 16], np.int32)
     q = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
-    got = kv.decode_fp8(q, codes, vcodes, tables, lens, np.float32(0.3), ks, vs)
+    hm = lambda c: np.ascontiguousarray(np.transpose(c, (0, 2, 1, 3)))   # noqa: E731
+    got = kv.decode_fp8(q, hm(codes), hm(vcodes), tables, lens, np.float32(0.3), ks, vs)
     want = pa_oracle.decode(q, kbf, vbf, tables, lens, np.float32(0.3))
     assert np.array_equal(got, want)
 

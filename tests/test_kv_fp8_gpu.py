@@ -1,4 +1,5 @@
-"""FP8 KV pages on the device against the oracle (oracle/kv_fp8.py).
+"""FP8 KV pages on the device against the oracle (oracle/kv_fp8.py).  fp8
+pools are head-major, [num_blocks, num_kv_heads, block_size, head_dim].
 
 * The quantising append is compared bit for bit with the oracle's codes over
   every bf16 bit pattern, for several scales (powers of two and not).  A NaN
@@ -55,7 +56,7 @@ def test_append_fp8_every_bf16_value(k_scale, v_scale):
     rng = np.random.default_rng(5)
     slots = rng.permutation(NB * BS)[:T].astype(np.int64)
     slots[rng.choice(T, 9, replace=False)] = -1          # padding rows write nothing
-    init = rng.integers(0, 256, (NB, BS, Hkv, D), dtype=np.uint8)
+    init = rng.integers(0, 256, (NB, Hkv, BS, D), dtype=np.uint8)     # head-major pool
     kc, vc = u8_tensor(init), u8_tensor(init)
     pa.reshape_and_cache_fp8(bf16_tensor(k), bf16_tensor(v), torch.from_numpy(slots).to(DEV),
                              kc, vc, k_scale, v_scale)
@@ -68,7 +69,7 @@ def test_append_fp8_every_bf16_value(k_scale, v_scale):
         nan_slot = np.zeros(got.shape, bool)
         for i, s in enumerate(slots):
             if s >= 0:
-                nan_slot[s // BS, s % BS] = np.isnan(src_f[i])
+                nan_slot[s // BS, :, s % BS] = np.isnan(src_f[i])
         assert np.all((got[nan_slot] & 0x7F) == 0x7F), name
         diff = (got != want) & ~nan_slot
         assert not diff.any(), (name, np.argwhere(diff)[:5], got[diff][:5], want[diff][:5])
@@ -93,7 +94,7 @@ def test_append_fp8_then_decode_end_to_end():
     kb = W.f32_to_bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32) * 3)
     vb = W.f32_to_bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32))
     ks, vs = 0.011, 0.0042
-    init = np.full((NB, BS, Hkv, D), 0x7F, np.uint8)
+    init = np.full((NB, Hkv, BS, D), 0x7F, np.uint8)
     kc, vc = u8_tensor(init), u8_tensor(init)
     pa.reshape_and_cache_fp8(bf16_tensor(kb), bf16_tensor(vb), torch.from_numpy(slots).to(DEV),
                              kc, vc, ks, vs)
@@ -173,7 +174,7 @@ def test_decode_fp8_nan_code_in_context_propagates():
     inp = W.make_decode_inputs(_small_spec(128, 8, 2, 16, (40, 40), seed=41), fill="zeros")
     k8, v8 = W.fp8_codes_like(inp)
     ct = inp.pool.compact_tables(inp.block_tables, inp.poison_block)
-    v8[ct[1, 1], 3, 0, 5] = 0xFF                   # sequence 1, token 19, kv head 0
+    v8[ct[1, 1], 0, 3, 5] = 0xFF                   # sequence 1, token 19, kv head 0
     out = to_f64(_run_fp8(inp, k8, v8, 0.5, 0.5, 1))
     assert np.isnan(out[1, :4, 5]).all()           # the 4 q heads of kv head 0
     assert np.isfinite(out[0]).all() and np.isfinite(out[1, 4:]).all()
@@ -186,10 +187,12 @@ def test_decode_fp8_equals_bf16_pool_of_its_values(D, Hq, Hkv):
     inp = W.make_decode_inputs(_small_spec(D, Hq, Hkv, 16, LENS_MIX, seed=51 + D), fill="zeros")
     k8, v8 = W.fp8_codes_like(inp)
     ks, vs = 2.0 ** -3, 2.0 ** 2
-    kb = W.f32_to_bf16_bits((O8.e4m3_decode(k8) * ks).astype(np.float32))
-    vb = W.f32_to_bf16_bits((O8.e4m3_decode(v8) * vs).astype(np.float32))
-    assert np.array_equal(W.bf16_bits_to_f32(kb).astype(np.float64)[k8 != 0x7F],
-                          (O8.e4m3_decode(k8) * ks)[k8 != 0x7F])      # exact in bf16
+    tm = lambda c: np.ascontiguousarray(np.transpose(c, (0, 2, 1, 3)))   # noqa: E731
+    k8t, v8t = tm(k8), tm(v8)                       # token-major, the bf16 pool layout
+    kb = W.f32_to_bf16_bits((O8.e4m3_decode(k8t) * ks).astype(np.float32))
+    vb = W.f32_to_bf16_bits((O8.e4m3_decode(v8t) * vs).astype(np.float32))
+    assert np.array_equal(W.bf16_bits_to_f32(kb).astype(np.float64)[k8t != 0x7F],
+                          (O8.e4m3_decode(k8t) * ks)[k8t != 0x7F])      # exact in bf16
     for S in (1, 5):
         got8 = to_bits(_run_fp8(inp, k8, v8, ks, vs, S))
         pool = W.CompactPool(inp.pool.num_blocks, inp.pool.ids, kb, vb)

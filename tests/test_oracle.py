@@ -85,6 +85,9 @@ FP8_MUTANTS = {
     "v_scale_dropped": ("V = e4m3_decode(gather_sequence(v_cache8, block_tables[b], L)) * vs",
                         "V = e4m3_decode(gather_sequence(v_cache8, block_tables[b], L))"),
     "subnormal_step": ("sub = m * 2.0 ** -9", "sub = m * 2.0 ** -10"),
+    "decode_token_major": ("k_cache8 = np.transpose(k_cache8, (0, 2, 1, 3))", "pass"),
+    "append_wrong_head_axis": ("kc[s // bs, :, s % bs] = quantize(new_k[i], k_scale)",
+                               "kc[s // bs, :, s % bs] = quantize(new_k[i], k_scale)[::-1]"),
 }
 
 

@@ -382,7 +382,8 @@ def fp8_codes_like(inp: "DecodeInputs"):
     """fp8 pools for the blocks, tables and lengths of ``inp``: each referenced
     block draws its own codes (streams keyed by seed and block id), and every
     slot that ``inp``'s bf16 pool poisons holds E4M3_NAN.  Returns the K and V
-    codes, stored densely like ``inp.pool``."""
+    codes, stored densely like ``inp.pool`` but head-major, [n, Hkv, bs, D],
+    the layout of fp8 pools."""
     s = inp.spec
     shape = inp.pool.k.shape
     k = np.empty(shape, dtype=np.uint8)
@@ -392,7 +393,8 @@ def fp8_codes_like(inp: "DecodeInputs"):
         v[i] = random_e4m3_codes(s.seed, (_TAG_V8, int(p)), shape[1:])
     k[inp.pool.k == BF16_NAN] = E4M3_NAN
     v[inp.pool.v == BF16_NAN] = E4M3_NAN
-    return k, v
+    hm = lambda c: np.ascontiguousarray(np.transpose(c, (0, 2, 1, 3)))   # noqa: E731
+    return hm(k), hm(v)
 
 
 def algorithmic_decode_bytes(lens, num_q_heads, num_kv_heads, head_dim, block_size) -> int:
