@@ -70,7 +70,7 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--others", default="c2b1,c3,c4,c5d,c5p,c5mix,c2b8q2,c2b8q4,c3q4,"
-                                         "c2b8f8,c3f8,c4f8",
+                                         "c2b8f8,c3f8,c4f8,c2b8q4f8",
                    help="comma list of extra workloads measured into 'workloads' ('' = none)")
     p.add_argument("--kernel-loop", type=int, default=0,
                    help="profiling mode: launch only the split kernel this many times and exit")
@@ -199,6 +199,12 @@ class DecodeWorkload:
         self.pa.decode_fp8(self.q, self.k_cache, self.v_cache, self.tables[r], self.lens,
                            self.scale, self.k_scale, self.v_scale, self.S, self.out,
                            workspace=self.ws)
+
+    def step_multi_fp8(self, r: int):
+        """Multi-token decode over fp8 pools."""
+        self.pa.decode_multi_fp8(self.q, self.k_cache, self.v_cache, self.tables[r], self.lens,
+                                 self.scale, self.k_scale, self.v_scale, self.S, self.out,
+                                 workspace=self.ws)
 
     def step_plain(self, r: int):
         """Single-token decode without the append."""
@@ -835,7 +841,8 @@ def measure_block_manager(seed: int = 77):
             "note": "host time through the Python binding (one ctypes call per operation)"}
 
 
-MULTI_WORKLOADS = {"c2b8q2": ("c2b8", 2), "c2b8q4": ("c2b8", 4), "c3q4": ("c3", 4)}
+MULTI_WORKLOADS = {"c2b8q2": ("c2b8", 2), "c2b8q4": ("c2b8", 4), "c3q4": ("c3", 4),
+                   "c2b8q4f8": ("c2b8", 4, "fp8")}
 
 
 def measure_multi(name, args, steps, warmup):
@@ -843,17 +850,19 @@ def measure_multi(name, args, steps, warmup):
     shapes and lengths, against single-token decode of the same batch."""
     import torch
     import workloads as W
-    base, q_len = MULTI_WORKLOADS[name]
+    base, q_len = MULTI_WORKLOADS[name][:2]
+    fp8 = MULTI_WORKLOADS[name][2:] == ("fp8",)
     spec = W.CONFIGS[base]
-    wl = DecodeWorkload(spec, args.rotate_gib, args.splits, q_len=q_len)
-    ms = time_graph(wl.step_multi, wl.R, steps, warmup)
+    wl = DecodeWorkload(spec, args.rotate_gib, args.splits, q_len=q_len, kv_fp8=fp8)
+    ms = time_graph(wl.step_multi_fp8 if fp8 else wl.step_multi, wl.R, steps, warmup)
     rec = {"workload": name, "base_workload": base, "q_len": q_len,
+           "kv": "fp8 e4m3, per-tensor scales" if fp8 else "bf16",
            "us_per_call": ms * 1e3, "gbps": wl.decode_bytes / (ms * 1e-3) / 1e9,
            "decode_bytes": wl.decode_bytes, "splits": wl.S, "rotations": wl.R}
     del wl
     torch.cuda.empty_cache()
-    one = DecodeWorkload(spec, args.rotate_gib, args.splits)
-    ms1 = time_graph(one.step_plain, one.R, steps, warmup)
+    one = DecodeWorkload(spec, args.rotate_gib, args.splits, kv_fp8=fp8)
+    ms1 = time_graph(one.step_fp8 if fp8 else one.step_plain, one.R, steps, warmup)
     rec["single_token_us_per_call"] = ms1 * 1e3
     rec["ratio_to_single_token"] = ms / ms1
     return one, rec

@@ -223,6 +223,19 @@ int pa_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
                   size_t workspace_bytes, void *stream);
 
 /*
+ * pa_decode_multi over fp8 pools: q_len query tokens per sequence, causal
+ * among themselves (the speculative verify step), with K and V dequantised
+ * as for pa_decode_fp8.  q, out, workspace (pa_decode_multi_workspace_size)
+ * and limits as for pa_decode_multi; scales as for pa_decode_fp8.
+ */
+int pa_decode_multi_fp8(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_tables, const int32_t *context_lens, float scale,
+                        float k_scale, float v_scale, int num_splits, void *out, int num_seqs,
+                        int q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                        int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The two passes of pa_decode as separate calls, for callers that merge
  * pieces themselves (for example pieces of one sequence computed on
  * different devices) or time the passes apart.  Arguments mean what they mean

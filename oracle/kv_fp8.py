@@ -74,6 +74,12 @@ def quantize(x_bf16_bits: np.ndarray, scale) -> np.ndarray:
     return e4m3_encode(y)
 
 
+def token_major(pool8: np.ndarray) -> np.ndarray:
+    """View of a head-major pool [NB, Hkv, bs, D] as [NB, bs, Hkv, D], the
+    layout the shared gather reads."""
+    return np.transpose(pool8, (0, 2, 1, 3))
+
+
 def append_fp8(new_k: np.ndarray, new_v: np.ndarray, slot_mapping: np.ndarray,
                k_cache8: np.ndarray, v_cache8: np.ndarray, k_scale, v_scale):
     """Copies of the fp8 pools [NB, Hkv, bs, D] with row i of new_k / new_v
@@ -89,6 +95,14 @@ def append_fp8(new_k: np.ndarray, new_v: np.ndarray, slot_mapping: np.ndarray,
     return kc, vc
 
 
+def _sequence_kv(k_cache8, v_cache8, table, L, ks, vs):
+    """K and V of a sequence's first L tokens (token-major pool views), as
+    code value times scale, fp64 [L, Hkv, D]."""
+    K = e4m3_decode(gather_sequence(k_cache8, table, L)) * ks
+    V = e4m3_decode(gather_sequence(v_cache8, table, L)) * vs
+    return K, V
+
+
 def decode_fp8(q: np.ndarray, k_cache8: np.ndarray, v_cache8: np.ndarray,
                block_tables: np.ndarray, context_lens: np.ndarray, scale, k_scale,
                v_scale) -> np.ndarray:
@@ -97,9 +111,7 @@ def decode_fp8(q: np.ndarray, k_cache8: np.ndarray, v_cache8: np.ndarray,
     q bf16 bits [B, Hq, D]; returns fp64 [B, Hq, D]."""
     B, Hq, D = q.shape
     Hkv = k_cache8.shape[1]
-    # token-major views [NB, bs, Hkv, D] for the shared gather
-    k_cache8 = np.transpose(k_cache8, (0, 2, 1, 3))
-    v_cache8 = np.transpose(v_cache8, (0, 2, 1, 3))
+    k_cache8, v_cache8 = token_major(k_cache8), token_major(v_cache8)
     sc = np.float64(np.float32(scale))
     ks, vs = np.float64(np.float32(k_scale)), np.float64(np.float32(v_scale))
     qf = (np.asarray(q, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32) \
@@ -107,9 +119,35 @@ def decode_fp8(q: np.ndarray, k_cache8: np.ndarray, v_cache8: np.ndarray,
     out = np.zeros((B, Hq, D), dtype=np.float64)
     for b in range(B):
         L = int(context_lens[b])
-        K = e4m3_decode(gather_sequence(k_cache8, block_tables[b], L)) * ks
-        V = e4m3_decode(gather_sequence(v_cache8, block_tables[b], L)) * vs
+        K, V = _sequence_kv(k_cache8, v_cache8, block_tables[b], L, ks, vs)
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             out[b, h] = attend(qf[b, h], K[:, g, :], V[:, g, :], sc)
+    return out
+
+
+def decode_multi_fp8(q: np.ndarray, k_cache8: np.ndarray, v_cache8: np.ndarray,
+                     block_tables: np.ndarray, context_lens: np.ndarray, scale, k_scale,
+                     v_scale) -> np.ndarray:
+    """Multi-token decode over fp8 pools [NB, Hkv, bs, D]: q bf16 bits
+    [B, q_len, Hq, D]; query token j of sequence b sits at position
+    context_lens[b] - q_len + j and attends the dequantised keys up to it
+    (none when the position is negative).  Returns fp64 [B, q_len, Hq, D]."""
+    B, QL, Hq, D = q.shape
+    Hkv = k_cache8.shape[1]
+    k_cache8, v_cache8 = token_major(k_cache8), token_major(v_cache8)
+    sc = np.float64(np.float32(scale))
+    ks, vs = np.float64(np.float32(k_scale)), np.float64(np.float32(v_scale))
+    qf = (np.asarray(q, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32) \
+        .astype(np.float64)
+    out = np.zeros((B, QL, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        K, V = _sequence_kv(k_cache8, v_cache8, block_tables[b], L, ks, vs)
+        for j in range(QL):
+            p = L - QL + j
+            n_keys = p + 1 if p >= 0 else 0
+            for h in range(Hq):
+                g = kv_head_of(h, Hq, Hkv)
+                out[b, j, h] = attend(qf[b, j, h], K[:n_keys, g, :], V[:n_keys, g, :], sc)
     return out

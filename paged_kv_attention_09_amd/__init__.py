@@ -18,6 +18,7 @@ Calls (argument order as in the C ABI):
   reshape_and_cache_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream=None)
   decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
              num_splits, out, stream=None, workspace=None): fp8 (e4m3) pools
+  decode_multi_fp8(...): decode_multi over fp8 pools
   prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, out,
           max_q_len, num_splits=0, stream=None, workspace=None)
   decode_workspace_size(num_seqs, num_q_heads, head_dim, num_splits)
@@ -69,6 +70,8 @@ SIGNATURES = {
                                       _VP]),
     "pa_decode_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _F, _F, _I, _VP, _I, _I, _I, _I, _I, _I64,
                            _I, _VP, _SZ, _VP]),
+    "pa_decode_multi_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _F, _F, _I, _VP, _I, _I, _I, _I, _I,
+                                 _I, _I64, _I, _VP, _SZ, _VP]),
     # host-side block manager (include/pa_block_manager.h)
     "pa_bm_create": (_VP, [_I64, _I, _I, _I]),
     "pa_bm_destroy": (None, [_VP]),
@@ -259,6 +262,33 @@ def decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float, k_
     return out
 
 
+def decode_multi_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                     k_scale: float, v_scale: float, num_splits: int, out, stream=None,
+                     workspace: Optional[torch.Tensor] = None):
+    """decode_multi over fp8 pools (uint8 e4m3 codes [NB, Hkv, bs, D]); q, out:
+    [B, q_len, Hq, D]."""
+    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache, torch.uint8)
+    dev = k_cache.device
+    _need(q, "q", torch.bfloat16, 4, dev)
+    _need(out, "out", torch.bfloat16, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, QL, Hq, Dq = (int(x) for x in q.shape)
+    if Dq != D or tuple(out.shape) != (B, QL, Hq, D):
+        raise ValueError(f"q/out must be [{B}, {QL}, {Hq}, {D}]")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables/context_lens batch differs from q")
+    W = int(block_tables.shape[1])
+    if num_splits == 0 and B > 0:
+        num_splits = auto_splits(B, Hkv, W, bs, dev)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace, q_len=QL)
+    _check("pa_decode_multi_fp8", lib().pa_decode_multi_fp8(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), float(scale), float(k_scale), float(v_scale), int(num_splits),
+        out.data_ptr(), B, QL, Hq, Hkv, D, bs, NB, W, ws_ptr, ws_bytes, _stream_ptr(stream, dev)))
+    return out
+
+
 def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_splits: int,
                  out, stream=None, workspace: Optional[torch.Tensor] = None):
     """q, out: [B, q_len, Hq, D].  Query token j of sequence b sits at position
@@ -427,7 +457,7 @@ def prefill_auto_splits(num_seqs, max_q_len, num_kv_heads, max_blocks_per_seq, b
 __all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "decode_merge", "prefill",
            "prefill_workspace_size", "prefill_auto_splits", "decode_workspace_size", "plan_splits",
            "auto_splits", "decode_multi", "decode_multi_workspace_size", "reshape_and_cache_fp8",
-           "decode_fp8", "BlockManager", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError",
+           "decode_fp8", "decode_multi_fp8", "BlockManager", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError",
            "PA_MAX_SPLITS", "PA_MAX_QUERY_TOKENS"]
 
 

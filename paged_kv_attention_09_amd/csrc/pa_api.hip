@@ -344,6 +344,36 @@ int pa_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
                                 (hipStream_t)stream);
 }
 
+int pa_decode_multi_fp8(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_tables, const int32_t *context_lens, float scale,
+                        float k_scale, float v_scale, int num_splits, void *out, int num_seqs,
+                        int q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                        int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  if (q_len < 1 || q_len > PA_MAX_QUERY_TOKENS) return PA_ERR_SHAPE;
+  if (!(valid_kv_scale(k_scale) && valid_kv_scale(v_scale))) return PA_ERR_SHAPE;
+  pa::DecodeArgs a;
+  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, &a);
+  if (st != PA_OK) return st;
+  if ((num_q_heads / num_kv_heads) * q_len > pa::kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out) return PA_ERR_NULL;
+  a.scale_log2 = (scale * k_scale) * 1.4426950408889634f;
+  if (!std::isfinite(a.scale_log2)) return PA_ERR_SHAPE;
+  a.kv_fp8 = 1;
+  a.v_scale = v_scale;
+  a.q_len = q_len;
+  a.out = (uint16_t *)out;
+  if (a.num_splits > 1) {
+    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+  }
+  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
+                                (hipStream_t)stream);
+}
+
 int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                        const int32_t *block_tables, const int32_t *context_lens, float scale,
                        int num_splits, int num_seqs, int num_q_heads, int num_kv_heads,

@@ -143,7 +143,7 @@ static_assert(decode_merge_fits<128>(8, decode_wave_lds<128>(1, false)) &&
 // per-tensor scales fold into the score scale (K) and the output (V).
 template <int D, int G, bool MF, int NT, bool MULTI, bool KV8>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
-  static_assert(!KV8 || (MF && !MULTI), "fp8 pools: single-token matrix path");
+  static_assert(!KV8 || MF, "fp8 pools: matrix path");
   using Ge = DecodeGeom<D>;
   constexpr int NSTAGE = KV8 ? kStages8 : kStages;
   // bf16 rows, as computed on (q, the V^T reads, the merge)
@@ -156,10 +156,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   constexpr int NDMA = CHK / 1024;                 // DMA instructions per tensor per chunk
   constexpr int STB = 2 * CHK;                     // one stage: K chunk then V chunk
   constexpr int CVB = KV8 ? CHB : 0;               // bf16 V conversion buffer
-  constexpr int WAVE_LDS = KV8 ? NSTAGE * STB + CVB + (G * ROWB + 1023) / 1024 * 1024
-                               : decode_wave_lds<D>(MULTI ? 0 : G, !MF);
-  static_assert(!KV8 || decode_merge_fits<D>(G, WAVE_LDS), "merge scratch");
   constexpr int RC = MULTI ? 16 : G;   // rows per merge pass
+  constexpr int WAVE_LDS =
+      KV8 ? NSTAGE * STB + CVB + (MULTI ? 0 : (G * ROWB + 1023) / 1024 * 1024)
+          : decode_wave_lds<D>(MULTI ? 0 : G, !MF);
+  static_assert(!KV8 || decode_merge_fits<D>(RC, WAVE_LDS), "merge scratch");
   __shared__ __attribute__((aligned(1024))) char smem[kWaves * WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
@@ -777,26 +778,31 @@ hipError_t launch_split_variant(const DecodeArgs &a, int num_seqs, hipStream_t s
 // Path choice: one query token with a group of at most kMaxVectorGroup heads
 // takes the vector path, other single-token groups the matrix path with one
 // tile; several query tokens take the matrix path with one tile per 16 rows.
-// fp8 pools (one query token) always take the matrix path.
+// fp8 pools always take the matrix path.
+template <int D, int G, bool KV8>
+hipError_t launch_split_dgk(const DecodeArgs &a, int num_seqs, hipStream_t stream) {
+  if (a.q_len == 1) {
+    if constexpr (G <= kMaxVectorGroup && !KV8)
+      return launch_split_variant<D, G, false, 1, false>(a, num_seqs, stream);
+    else
+      return launch_split_variant<D, G, true, 1, false, KV8>(a, num_seqs, stream);
+  }
+  const int rows = G * a.q_len;
+  if (rows <= 16) return launch_split_variant<D, G, true, 1, true, KV8>(a, num_seqs, stream);
+  if constexpr (G * kMaxQueryTokens > 16) {
+    if (rows <= kMaxDecodeRows)
+      return launch_split_variant<D, G, true, 2, true, KV8>(a, num_seqs, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int D, int G>
 hipError_t launch_split_dg(const DecodeArgs &a, int num_seqs, hipStream_t stream) {
   if (a.kv_fp8) {
-    if (a.q_len != 1 || a.new_k != nullptr) return hipErrorInvalidValue;
-    return launch_split_variant<D, G, true, 1, false, true>(a, num_seqs, stream);
+    if (a.new_k != nullptr) return hipErrorInvalidValue;
+    return launch_split_dgk<D, G, true>(a, num_seqs, stream);
   }
-  if (a.q_len == 1) {
-    if constexpr (G <= kMaxVectorGroup)
-      return launch_split_variant<D, G, false, 1, false>(a, num_seqs, stream);
-    else
-      return launch_split_variant<D, G, true, 1, false>(a, num_seqs, stream);
-  }
-  const int rows = G * a.q_len;
-  if (rows <= 16) return launch_split_variant<D, G, true, 1, true>(a, num_seqs, stream);
-  if constexpr (G * kMaxQueryTokens > 16) {
-    if (rows <= kMaxDecodeRows)
-      return launch_split_variant<D, G, true, 2, true>(a, num_seqs, stream);
-  }
-  return hipErrorInvalidValue;
+  return launch_split_dgk<D, G, false>(a, num_seqs, stream);
 }
 
 template <int D>

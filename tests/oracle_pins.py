@@ -452,4 +452,32 @@ def pin_fp8_decode_reduces_to_bf16(kv, seed=19):
     assert np.array_equal(got, want)
 
 
-FP8_PINS = [pin_fp8_codec, pin_fp8_quantize_and_append, pin_fp8_decode_reduces_to_bf16]
+def pin_fp8_decode_multi(kv, seed=20):
+    """F4: multi-token decode over fp8 pools - with power-of-two scales it
+    equals the (pinned) bf16 multi-token decode over the dequantised pools
+    bit for bit, and with one query token it equals fp8 decode exactly."""
+    import oracle.paged_attention as pa_oracle
+    rng = np.random.default_rng(seed)
+    NB, bs, Hkv, D, B, Hq, QL = 12, 4, 2, 8, 3, 6, 3
+    codes = rng.integers(0, 256, (NB, Hkv, bs, D)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    vcodes = rng.integers(0, 256, (NB, Hkv, bs, D)).astype(np.uint8)
+    vcodes[(vcodes & 0x7F) == 0x7F] = 0x40
+    ks, vs = 2.0 ** -3, 2.0 ** 2
+    tm = lambda c: np.ascontiguousarray(np.transpose(c, (0, 2, 1, 3)))   # noqa: E731
+    kbf = W.f32_to_bf16_bits((kv.e4m3_decode(tm(codes)) * ks).astype(np.float32))
+    vbf = W.f32_to_bf16_bits((kv.e4m3_decode(tm(vcodes)) * vs).astype(np.float32))
+    tables = rng.permutation(NB)[:B * 4].reshape(B, 4).astype(np.int32)
+    lens = np.array([2, 9, 16], np.int32)                    # the first shorter than q_len
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, QL, Hq, D), dtype=np.float32))
+    got = kv.decode_multi_fp8(q, codes, vcodes, tables, lens, np.float32(0.3), ks, vs)
+    want = pa_oracle.decode_multi(q, kbf, vbf, tables, lens, np.float32(0.3))
+    assert np.array_equal(got, want)
+    assert (got[0, 0] == 0).all()                            # position -1: no keys
+    one = kv.decode_multi_fp8(q[:, :1], codes, vcodes, tables, lens, np.float32(0.3), 0.37, 0.011)
+    dec = kv.decode_fp8(q[:, 0], codes, vcodes, tables, lens, np.float32(0.3), 0.37, 0.011)
+    assert np.array_equal(one[:, 0], dec)
+
+
+FP8_PINS = [pin_fp8_codec, pin_fp8_quantize_and_append, pin_fp8_decode_reduces_to_bf16,
+            pin_fp8_decode_multi]

@@ -225,3 +225,50 @@ def test_decode_fp8_full_size_sampled(name):
     rows = sorted(set(np.random.default_rng(61).choice(spec.num_seqs, 4, replace=False).tolist()))
     ref = _oracle_fp8(inp, k8, v8, ks, vs, rows)
     assert_close(got[rows], ref, what=name)
+
+
+# ---------------------------------------------------------------------------
+# multi-token decode over fp8 pools
+# ---------------------------------------------------------------------------
+
+
+def _run_multi_fp8(inp, q, k8, v8, ks, vs, S):
+    s = inp.spec
+    kc, vc = device_pool8(inp, k8, v8)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=DEV)
+    pa.decode_multi_fp8(bf16_tensor(q), kc, vc, torch.from_numpy(inp.block_tables).to(DEV),
+                        torch.from_numpy(inp.context_lens).to(DEV), float(inp.scale), ks, vs, S,
+                        out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,QL", [(128, 12, 2, 4), (128, 28, 4, 4), (128, 16, 2, 4),
+                                         (64, 8, 2, 8), (128, 4, 4, 8), (64, 6, 2, 2)])
+@pytest.mark.parametrize("bs", [16, 256])
+def test_decode_multi_fp8(D, Hq, Hkv, QL, bs):
+    """q_len query tokens (one or two tiles of 16 rows), causal inside the
+    window, ragged lengths including sequences shorter than the window."""
+    lens = (2, 5, 17, 300, 1029)
+    inp = W.make_decode_inputs(_small_spec(D, Hq, Hkv, bs, lens, seed=900 + D + Hq + QL + bs),
+                               fill="zeros")
+    k8, v8 = W.fp8_codes_like(inp)
+    q = W.f32_to_bf16_bits(np.random.default_rng(QL + Hq).standard_normal(
+        (len(lens), QL, Hq, D), dtype=np.float32))
+    ks, vs = 0.3, 0.2
+    ct = inp.pool.compact_tables(inp.block_tables, inp.poison_block)
+    ref = O8.decode_multi_fp8(q, k8, v8, ct, inp.context_lens, inp.scale, ks, vs)
+    for S in (1, 3, 0):
+        got = to_f64(_run_multi_fp8(inp, q, k8, v8, ks, vs, S))
+        assert_close(got, ref, what=f"D={D} Hq={Hq} Hkv={Hkv} q_len={QL} bs={bs} S={S}")
+
+
+def test_decode_multi_fp8_one_token_is_decode_fp8():
+    """q_len 1 runs the single-token kernel: bit-identical to pa_decode_fp8."""
+    inp = W.make_decode_inputs(_small_spec(128, 28, 4, 16, LENS_MIX, seed=77), fill="zeros")
+    k8, v8 = W.fp8_codes_like(inp)
+    q1 = inp.q[:, None]
+    for S in (1, 5):
+        a = to_bits(_run_multi_fp8(inp, q1, k8, v8, 0.4, 0.3, S))[:, 0]
+        b = to_bits(_run_fp8(inp, k8, v8, 0.4, 0.3, S))
+        assert np.array_equal(a, b), S

@@ -80,12 +80,13 @@ FP8_MUTANTS = {
     "decode_bias_8": ("np.exp2(e.astype(np.float64) - 7.0)", "np.exp2(e.astype(np.float64) - 8.0)"),
     "no_clamp": ("y = np.clip(x * inv, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))", "y = x * inv"),
     "scale_not_inverted": ("inv = np.float32(1.0) / np.float32(scale)", "inv = np.float32(scale)"),
-    "k_scale_dropped": ("K = e4m3_decode(gather_sequence(k_cache8, block_tables[b], L)) * ks",
-                        "K = e4m3_decode(gather_sequence(k_cache8, block_tables[b], L))"),
-    "v_scale_dropped": ("V = e4m3_decode(gather_sequence(v_cache8, block_tables[b], L)) * vs",
-                        "V = e4m3_decode(gather_sequence(v_cache8, block_tables[b], L))"),
+    "k_scale_dropped": ("K = e4m3_decode(gather_sequence(k_cache8, table, L)) * ks",
+                        "K = e4m3_decode(gather_sequence(k_cache8, table, L))"),
+    "v_scale_dropped": ("V = e4m3_decode(gather_sequence(v_cache8, table, L)) * vs",
+                        "V = e4m3_decode(gather_sequence(v_cache8, table, L))"),
+    "fp8_multi_window_shifted": ("            p = L - QL + j\n            n_keys", "            p = L - QL + j - 1\n            n_keys"),
     "subnormal_step": ("sub = m * 2.0 ** -9", "sub = m * 2.0 ** -10"),
-    "decode_token_major": ("k_cache8 = np.transpose(k_cache8, (0, 2, 1, 3))", "pass"),
+    "no_token_major_view": ("return np.transpose(pool8, (0, 2, 1, 3))", "return pool8"),
     "append_wrong_head_axis": ("kc[s // bs, :, s % bs] = quantize(new_k[i], k_scale)",
                                "kc[s // bs, :, s % bs] = quantize(new_k[i], k_scale)[::-1]"),
 }
