@@ -151,3 +151,32 @@ def decode_multi_fp8(q: np.ndarray, k_cache8: np.ndarray, v_cache8: np.ndarray,
                 g = kv_head_of(h, Hq, Hkv)
                 out[b, j, h] = attend(qf[b, j, h], K[:n_keys, g, :], V[:n_keys, g, :], sc)
     return out
+
+
+def prefill_fp8(q: np.ndarray, cu_seqlens_q: np.ndarray, k_cache8: np.ndarray,
+                v_cache8: np.ndarray, block_tables: np.ndarray, context_lens: np.ndarray,
+                scale, k_scale, v_scale) -> np.ndarray:
+    """Chunked prefill over fp8 pools [NB, Hkv, bs, D]: q bf16 bits [Tq, Hq, D]
+    packed by cu_seqlens_q [B + 1]; context_lens [B] are total lengths (cached
+    prefix + chunk, the chunk's K/V already in the pool); query i of an n-row
+    chunk sits at position L - n + i and attends the dequantised keys up to it.
+    Returns fp64 [Tq, Hq, D]."""
+    Tq, Hq, D = q.shape
+    Hkv = k_cache8.shape[1]
+    k_cache8, v_cache8 = token_major(k_cache8), token_major(v_cache8)
+    sc = np.float64(np.float32(scale))
+    ks, vs = np.float64(np.float32(k_scale)), np.float64(np.float32(v_scale))
+    qf = (np.asarray(q, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32) \
+        .astype(np.float64)
+    out = np.zeros((Tq, Hq, D), dtype=np.float64)
+    for b in range(len(context_lens)):
+        L = int(context_lens[b])
+        q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        n = q1 - q0
+        K, V = _sequence_kv(k_cache8, v_cache8, block_tables[b], L, ks, vs)
+        for i in range(n):
+            p = L - n + i
+            for h in range(Hq):
+                g = kv_head_of(h, Hq, Hkv)
+                out[q0 + i, h] = attend(qf[q0 + i, h], K[:p + 1, g, :], V[:p + 1, g, :], sc)
+    return out

@@ -479,5 +479,33 @@ def pin_fp8_decode_multi(kv, seed=20):
     assert np.array_equal(one[:, 0], dec)
 
 
+def pin_fp8_prefill(kv, seed=21):
+    """F5: chunked prefill over fp8 pools - with power-of-two scales it equals
+    the (pinned) bf16 prefill over the dequantised pools bit for bit; a
+    one-row chunk equals fp8 decode exactly."""
+    import oracle.paged_attention as pa_oracle
+    rng = np.random.default_rng(seed)
+    NB, bs, Hkv, D, Hq = 12, 4, 2, 8, 6
+    codes = rng.integers(0, 256, (NB, Hkv, bs, D)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x30
+    vcodes = rng.integers(0, 256, (NB, Hkv, bs, D)).astype(np.uint8)
+    vcodes[(vcodes & 0x7F) == 0x7F] = 0x44
+    ks, vs = 2.0 ** 2, 2.0 ** -5
+    tm = lambda c: np.ascontiguousarray(np.transpose(c, (0, 2, 1, 3)))   # noqa: E731
+    kbf = W.f32_to_bf16_bits((kv.e4m3_decode(tm(codes)) * ks).astype(np.float32))
+    vbf = W.f32_to_bf16_bits((kv.e4m3_decode(tm(vcodes)) * vs).astype(np.float32))
+    tables = rng.permutation(NB)[:8].reshape(2, 4).astype(np.int32)
+    lens = np.array([13, 16], np.int32)
+    cu = np.array([0, 5, 9], np.int32)                        # chunks of 5 and 4 rows
+    q = W.f32_to_bf16_bits(rng.standard_normal((9, Hq, D), dtype=np.float32))
+    got = kv.prefill_fp8(q, cu, codes, vcodes, tables, lens, np.float32(0.2), ks, vs)
+    want = pa_oracle.prefill(q, cu, kbf, vbf, tables, lens, np.float32(0.2))
+    assert np.array_equal(got, want)
+    one = kv.prefill_fp8(q[:2], np.array([0, 1, 2], np.int32), codes, vcodes, tables, lens,
+                         np.float32(0.2), 0.7, 0.3)
+    dec = kv.decode_fp8(q[:2], codes, vcodes, tables, lens, np.float32(0.2), 0.7, 0.3)
+    assert np.array_equal(one, dec)
+
+
 FP8_PINS = [pin_fp8_codec, pin_fp8_quantize_and_append, pin_fp8_decode_reduces_to_bf16,
-            pin_fp8_decode_multi]
+            pin_fp8_decode_multi, pin_fp8_prefill]

@@ -87,6 +87,7 @@ FP8_MUTANTS = {
     "fp8_multi_window_shifted": ("            p = L - QL + j\n            n_keys", "            p = L - QL + j - 1\n            n_keys"),
     "subnormal_step": ("sub = m * 2.0 ** -9", "sub = m * 2.0 ** -10"),
     "no_token_major_view": ("return np.transpose(pool8, (0, 2, 1, 3))", "return pool8"),
+    "fp8_prefill_causal_off_by_one": ("            p = L - n + i\n", "            p = L - n + i - 1\n"),
     "append_wrong_head_axis": ("kc[s // bs, :, s % bs] = quantize(new_k[i], k_scale)",
                                "kc[s // bs, :, s % bs] = quantize(new_k[i], k_scale)[::-1]"),
 }
