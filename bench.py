@@ -70,7 +70,7 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--others", default="c2b1,c3,c4,c5d,c5p,c5mix,c2b8q2,c2b8q4,c3q4,"
-                                         "c2b8f8,c3f8,c4f8,c2b8q4f8",
+                                         "c2b8f8,c3f8,c4f8,c2b8q4f8,c5pf8,c5mixf8",
                    help="comma list of extra workloads measured into 'workloads' ('' = none)")
     p.add_argument("--kernel-loop", type=int, default=0,
                    help="profiling mode: launch only the split kernel this many times and exit")
@@ -243,7 +243,7 @@ class PrefillWorkload:
     chunk's K/V, the chunked prefill on MFMA, then the fused append + decode
     of the decode sequences."""
 
-    def __init__(self, pspec, dspec, rotate_gib: float, seed: int = 4321):
+    def __init__(self, pspec, dspec, rotate_gib: float, seed: int = 4321, kv_fp8: bool = False):
         import numpy as np
         import torch
 
@@ -251,6 +251,8 @@ class PrefillWorkload:
         import workloads as W
 
         self.pa = pa
+        self.kv_fp8 = kv_fp8
+        self.k_scale, self.v_scale = 0.25, 0.25
         dev = torch.device("cuda:0")
         self.dev = dev
         bs, Hkv, D, Hq = pspec.block_size, pspec.num_kv_heads, pspec.head_dim, pspec.num_q_heads
@@ -263,22 +265,32 @@ class PrefillWorkload:
         pblk = [-(-int(L) // bs) for L in self.plens]
         dblk = [-(-int(L) // bs) for L in self.dlens]
         per_rot = sum(pblk) + sum(dblk)
-        kv_bytes = (int(self.plens.sum()) + int(self.dlens.sum())) * Hkv * D * 2 * 2
+        elem = 1 if kv_fp8 else 2
+        kv_bytes = (int(self.plens.sum()) + int(self.dlens.sum())) * Hkv * D * elem * 2
         self.R = max(1, math.ceil(rotate_gib * 2**30 / kv_bytes))
         NB = max(pspec.num_blocks, self.R * per_rot + 1)
         g = torch.Generator(device=dev)
         g.manual_seed(seed)
-        shape = (NB, bs, Hkv, D)
-        self.k_cache = torch.empty(shape, dtype=torch.bfloat16, device=dev)
-        self.v_cache = torch.empty(shape, dtype=torch.bfloat16, device=dev)
-        step = max(1, (256 << 20) // (bs * Hkv * D * 2))
+        shape = (NB, Hkv, bs, D) if kv_fp8 else (NB, bs, Hkv, D)   # fp8 pools are head-major
+        dt = torch.uint8 if kv_fp8 else torch.bfloat16
+        self.k_cache = torch.empty(shape, dtype=dt, device=dev)
+        self.v_cache = torch.empty(shape, dtype=dt, device=dev)
+        step = max(1, (256 << 20) // (bs * Hkv * D * elem))
         for i in range(0, NB, step):
             j = min(NB, i + step)
-            self.k_cache[i:j].normal_(generator=g)
-            self.v_cache[i:j].normal_(generator=g)
+            for t in (self.k_cache, self.v_cache):
+                if kv_fp8:
+                    # fp8 codes: random sign and mantissa, exponent field 4..8
+                    sm = torch.randint(0, 256, t[i:j].shape, generator=g, device=dev,
+                                       dtype=torch.int16) & 0x87
+                    ex = torch.randint(4, 9, t[i:j].shape, generator=g, device=dev,
+                                       dtype=torch.int16) << 3
+                    t[i:j] = (sm | ex).to(torch.uint8)
+                else:
+                    t[i:j].normal_(generator=g)
         perm = torch.randperm(NB, generator=g, device=dev).cpu().numpy()
         Wp, Wd = pspec.max_blocks_per_seq, (dspec.max_blocks_per_seq if dspec else 1)
-        self.ptables, self.dtables, self.cslots = [], [], []
+        self.ptables, self.dtables, self.cslots, self.dslots = [], [], [], []
         for r in range(self.R):
             ids = perm[r * per_rot:(r + 1) * per_rot]
             tp = np.full((P, Wp), int(perm[-1]), np.int32)
@@ -296,6 +308,10 @@ class PrefillWorkload:
                     slots.append(int(tp[b, t // bs]) * bs + t % bs)
             self.ptables.append(torch.from_numpy(tp).to(dev))
             self.dtables.append(torch.from_numpy(td).to(dev))
+            if B:
+                L = self.dlens.astype(np.int64)
+                last = td[np.arange(B), (L - 1) // bs].astype(np.int64) * bs + (L - 1) % bs
+                self.dslots.append(torch.from_numpy(last).to(dev))
             self.cslots.append(torch.from_numpy(np.asarray(slots, np.int64)).to(dev))
         Tq = int(self.chunks.sum())
         self.Tq = Tq
@@ -315,7 +331,7 @@ class PrefillWorkload:
         pos = np.concatenate([np.arange(int(L - n), int(L)) for L, n in zip(self.plens, self.chunks)])
         self.flop = 4 * D * Hq * int((pos + 1).sum())
         self.append_bytes = Tq * Hkv * D * 2 * 2 * 2 + Tq * 8
-        self.prefill_bytes = (int(self.plens.sum()) * Hkv * D * 2 * 2 + 2 * Tq * Hq * D * 2)
+        self.prefill_bytes = (int(self.plens.sum()) * Hkv * D * elem * 2 + 2 * Tq * Hq * D * 2)
         if B:
             self.dlens_t = torch.from_numpy(self.dlens).to(dev)
             self.dq = torch.randn((B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
@@ -334,17 +350,35 @@ class PrefillWorkload:
         torch.cuda.synchronize()
 
     def append_chunk(self, r):
-        self.pa.reshape_and_cache(self.ck, self.cv, self.cslots[r], self.k_cache, self.v_cache)
+        if self.kv_fp8:
+            self.pa.reshape_and_cache_fp8(self.ck, self.cv, self.cslots[r], self.k_cache,
+                                          self.v_cache, self.k_scale, self.v_scale)
+        else:
+            self.pa.reshape_and_cache(self.ck, self.cv, self.cslots[r], self.k_cache,
+                                      self.v_cache)
 
     def prefill(self, r):
-        self.pa.prefill(self.q, self.cu, self.k_cache, self.v_cache, self.ptables[r],
-                        self.plens_t, self.scale, self.out, self.max_q, num_splits=self.S,
-                        workspace=self.ws)
+        if self.kv_fp8:
+            self.pa.prefill_fp8(self.q, self.cu, self.k_cache, self.v_cache, self.ptables[r],
+                                self.plens_t, self.scale, self.k_scale, self.v_scale, self.out,
+                                self.max_q, num_splits=self.S, workspace=self.ws)
+        else:
+            self.pa.prefill(self.q, self.cu, self.k_cache, self.v_cache, self.ptables[r],
+                            self.plens_t, self.scale, self.out, self.max_q, num_splits=self.S,
+                            workspace=self.ws)
 
     def decode(self, r):
-        self.pa.append_decode(self.dq, self.dk, self.dv, self.k_cache, self.v_cache,
-                              self.dtables[r], self.dlens_t, self.scale, self.dS, self.dout,
-                              workspace=self.dws)
+        if self.kv_fp8:
+            # fp8 pools: quantising append of the new rows, then decode
+            self.pa.reshape_and_cache_fp8(self.dk, self.dv, self.dslots[r], self.k_cache,
+                                          self.v_cache, self.k_scale, self.v_scale)
+            self.pa.decode_fp8(self.dq, self.k_cache, self.v_cache, self.dtables[r],
+                               self.dlens_t, self.scale, self.k_scale, self.v_scale, self.dS,
+                               self.dout, workspace=self.dws)
+        else:
+            self.pa.append_decode(self.dq, self.dk, self.dv, self.k_cache, self.v_cache,
+                                  self.dtables[r], self.dlens_t, self.scale, self.dS, self.dout,
+                                  workspace=self.dws)
 
     def step(self, r):
         self.append_chunk(r)
@@ -375,10 +409,10 @@ def time_graph(fn, R: int, steps: int, warmup: int) -> float:
     return s.elapsed_time(e) / steps
 
 
-def measure_prefill(args, steps, warmup, with_decode: bool):
+def measure_prefill(args, steps, warmup, with_decode: bool, kv_fp8: bool = False):
     import workloads as W
     wl = PrefillWorkload(W.PREFILL_CONFIGS["c5p"], W.CONFIGS["c5d"] if with_decode else None,
-                         args.rotate_gib)
+                         args.rotate_gib, kv_fp8=kv_fp8)
     ms_pf = time_graph(wl.prefill, wl.R, steps, warmup)
     rec = {"prefill_us": ms_pf * 1e3, "prefill_tflops": wl.flop / (ms_pf * 1e-3) / 1e12,
            "prefill_splits": wl.S, "prefill_gflop": wl.flop / 1e9, "query_rows": wl.Tq,
@@ -390,7 +424,11 @@ def measure_prefill(args, steps, warmup, with_decode: bool):
         rec.update({"us_per_step": ms_step * 1e3, "decode_us": ms_dec * 1e3,
                     "decode_gbps": wl.decode_bytes / (ms_dec * 1e-3) / 1e9,
                     "append_us": ms_app * 1e3, "decode_splits": wl.dS,
-                    "step": "append 512-token chunk, MFMA prefill, fused append + decode of 64"})
+                    "step": ("quantising append of the 512-token chunk, MFMA prefill over fp8 "
+                             "pools, quantising append + fp8 decode of 64") if kv_fp8 else
+                            "append 512-token chunk, MFMA prefill, fused append + decode of 64"})
+    if kv_fp8:
+        rec["kv"] = "fp8 e4m3, per-tensor scales"
     return wl, rec
 
 
@@ -1008,11 +1046,14 @@ def main(argv=None):
             msg = (f"q_len {rec['q_len']}: {rec['us_per_call']:.2f} us/call, {rec['gbps']:.1f} GB/s;"
                    f" single-token {rec['single_token_us_per_call']:.2f} us "
                    f"(x{rec['ratio_to_single_token']:.2f})")
-        elif name in ("c5p", "c5mix"):
+        elif name in ("c5p", "c5mix", "c5pf8", "c5mixf8"):
             wl, rec = measure_prefill(args, min(args.steps, 50), min(args.warmup, 5),
-                                      with_decode=(name == "c5mix"))
+                                      with_decode=name.startswith("c5mix"),
+                                      kv_fp8=name.endswith("f8"))
             msg = f"prefill {rec['prefill_us']:.2f} us ({rec['prefill_tflops']:.0f} TFLOP/s)"
-            if name == "c5mix":
+            if name.endswith("f8"):
+                msg = "fp8 pools: " + msg
+            if name.startswith("c5mix"):
                 msg += (f"; mixed step {rec['us_per_step']:.2f} us (append {rec['append_us']:.2f}, "
                         f"decode {rec['decode_us']:.2f})")
         else:

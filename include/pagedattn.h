@@ -317,6 +317,22 @@ int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
                int64_t num_blocks, int max_blocks_per_seq, void *workspace,
                size_t workspace_bytes, void *stream);
 
+/*
+ * pa_prefill over fp8 pools (head-major uint8 e4m3 codes, as for
+ * pa_decode_fp8): K and V are the codes' values times k_scale and v_scale.
+ * The codes widen exactly to bf16 inside the kernel; k_scale joins the score
+ * scale, v_scale multiplies the normalised output.  Other arguments, the
+ * workspace and the limits are those of pa_prefill; scales follow
+ * pa_reshape_and_cache_fp8's rule and scale * k_scale * log2(e) must be
+ * finite (else PA_ERR_SHAPE).
+ */
+int pa_prefill_fp8(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
+                   const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                   float scale, float k_scale, float v_scale, int num_splits, void *out,
+                   int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                   int block_size, int64_t num_blocks, int max_blocks_per_seq, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
 /* Workspace bytes pa_prefill needs for a given split count (0 when
  * num_splits <= 1): each piece's normalised output rows, rounded to bf16,
  * then their fp32 log-sum-exp.  Returns 0 for invalid arguments. */

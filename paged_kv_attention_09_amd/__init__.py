@@ -19,6 +19,8 @@ Calls (argument order as in the C ABI):
   decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
              num_splits, out, stream=None, workspace=None): fp8 (e4m3) pools
   decode_multi_fp8(...): decode_multi over fp8 pools
+  prefill_fp8(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+              v_scale, out, max_q_len, num_splits=0, stream=None, workspace=None)
   prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, out,
           max_q_len, num_splits=0, stream=None, workspace=None)
   decode_workspace_size(num_seqs, num_q_heads, head_dim, num_splits)
@@ -64,6 +66,8 @@ SIGNATURES = {
     "pa_decode_merge": (_I, [_VP, _SZ, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP]),
     "pa_prefill": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _F, _I, _VP, _I, _I, _I, _I, _I, _I, _I64,
                         _I, _VP, _SZ, _VP]),
+    "pa_prefill_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _F, _F, _F, _I, _VP, _I, _I, _I, _I, _I,
+                            _I, _I64, _I, _VP, _SZ, _VP]),
     "pa_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "pa_prefill_plan_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "pa_reshape_and_cache_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _F, _I64, _I64, _I, _I, _I,
@@ -403,7 +407,23 @@ def prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale
     context_lens[b] tokens, chunk included; query i of an n-row chunk sits at
     position context_lens[b] - n + i.  num_splits = 0 picks the key split
     automatically."""
-    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
+    return _prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                    max_q_len, num_splits, stream, workspace, None)
+
+
+def prefill_fp8(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                k_scale: float, v_scale: float, out, max_q_len: int, num_splits: int = 0,
+                stream=None, workspace: Optional[torch.Tensor] = None):
+    """prefill over fp8 pools (uint8 e4m3 codes [NB, Hkv, bs, D]): K and V are
+    the codes' values times k_scale and v_scale."""
+    return _prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                    max_q_len, num_splits, stream, workspace, (float(k_scale), float(v_scale)))
+
+
+def _prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, out,
+             max_q_len, num_splits, stream, workspace, fp8_scales):
+    NB, bs, Hkv, D = _pool_dims(k_cache, v_cache,
+                                torch.bfloat16 if fp8_scales is None else torch.uint8)
     dev = k_cache.device
     _need(q, "q", torch.bfloat16, 3, dev)
     _need(out, "out", torch.bfloat16, 3, dev)
@@ -428,13 +448,15 @@ def prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale
         if workspace.numel() * workspace.element_size() < need:
             raise ValueError(f"workspace needs {need} bytes")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check("pa_prefill", lib().pa_prefill(
-        q.data_ptr(), cu_seqlens_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), int(num_splits),
-        out.data_ptr(), B, int(max_q_len), Hq, Hkv, D, bs, NB, W, ws_ptr, ws_bytes,
-        _stream_ptr(stream, dev)))
+    ptrs = (q.data_ptr(), cu_seqlens_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), float(scale))
+    rest = (int(num_splits), out.data_ptr(), B, int(max_q_len), Hq, Hkv, D, bs, NB, W, ws_ptr,
+            ws_bytes, _stream_ptr(stream, dev))
+    if fp8_scales is None:
+        _check("pa_prefill", lib().pa_prefill(*ptrs, *rest))
+    else:
+        _check("pa_prefill_fp8", lib().pa_prefill_fp8(*ptrs, *fp8_scales, *rest))
     return out
-
 
 def prefill_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim, num_splits) -> int:
     return int(lib().pa_prefill_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim,
@@ -457,7 +479,7 @@ def prefill_auto_splits(num_seqs, max_q_len, num_kv_heads, max_blocks_per_seq, b
 __all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "decode_merge", "prefill",
            "prefill_workspace_size", "prefill_auto_splits", "decode_workspace_size", "plan_splits",
            "auto_splits", "decode_multi", "decode_multi_workspace_size", "reshape_and_cache_fp8",
-           "decode_fp8", "decode_multi_fp8", "BlockManager", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError",
+           "decode_fp8", "decode_multi_fp8", "prefill_fp8", "BlockManager", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError",
            "PA_MAX_SPLITS", "PA_MAX_QUERY_TOKENS"]
 
 

@@ -442,13 +442,16 @@ int pa_prefill_plan_splits(int num_seqs, int max_q_len, int num_kv_heads, int ma
   return n < 1 ? 1 : (n > PA_MAX_SPLITS ? PA_MAX_SPLITS : n);
 }
 
-int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
-               const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
-               float scale, int num_splits, void *out, int num_seqs, int max_q_len,
-               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-               int64_t num_blocks, int max_blocks_per_seq, void *workspace,
-               size_t workspace_bytes, void *stream) {
+namespace {
+
+int prefill_impl(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
+                 const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                 float scale, bool fp8, float k_scale, float v_scale, int num_splits, void *out,
+                 int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                 int block_size, int64_t num_blocks, int max_blocks_per_seq, void *workspace,
+                 size_t workspace_bytes, void *stream) {
   if (num_seqs < 0 || max_q_len < 0) return PA_ERR_SHAPE;
+  if (fp8 && !(valid_kv_scale(k_scale) && valid_kv_scale(v_scale))) return PA_ERR_SHAPE;
   int st = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (st != PA_OK) return st;
   st = check_pool(num_blocks, block_size, max_blocks_per_seq);
@@ -471,14 +474,18 @@ int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
   pa::PrefillArgs a;
   a.q = (const uint16_t *)q;
   a.cu_seqlens_q = cu_seqlens_q;
-  a.k_cache = (const uint16_t *)k_cache;
-  a.v_cache = (const uint16_t *)v_cache;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = (uint16_t *)out;
   a.o_part = nullptr;
   a.lse_part = nullptr;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  // fp8 pools: scores are q . (code k_scale) scale
+  a.scale_log2 = (fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
+  if (!std::isfinite(a.scale_log2)) return PA_ERR_SHAPE;
+  a.kv_fp8 = fp8 ? 1 : 0;
+  a.v_scale = fp8 ? v_scale : 1.0f;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -503,6 +510,32 @@ int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
       pa::launch_prefill_merge(a, head_dim, num_seqs * max_q_len, s) != hipSuccess)
     return PA_ERR_HIP;
   return PA_OK;
+}
+
+}  // namespace
+
+int pa_prefill(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
+               const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+               float scale, int num_splits, void *out, int num_seqs, int max_q_len,
+               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+               int64_t num_blocks, int max_blocks_per_seq, void *workspace,
+               size_t workspace_bytes, void *stream) {
+  return prefill_impl(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, false,
+                      1.0f, 1.0f, num_splits, out, num_seqs, max_q_len, num_q_heads, num_kv_heads,
+                      head_dim, block_size, num_blocks, max_blocks_per_seq, workspace,
+                      workspace_bytes, stream);
+}
+
+int pa_prefill_fp8(const void *q, const int32_t *cu_seqlens_q, const void *k_cache,
+                   const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                   float scale, float k_scale, float v_scale, int num_splits, void *out,
+                   int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                   int block_size, int64_t num_blocks, int max_blocks_per_seq, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  return prefill_impl(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, true,
+                      k_scale, v_scale, num_splits, out, num_seqs, max_q_len, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                      workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

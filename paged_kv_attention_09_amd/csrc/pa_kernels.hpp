@@ -43,7 +43,7 @@ struct DecodeArgs {
 struct PrefillArgs {
   const uint16_t *q;          // [Tq, Hq, D]
   const int32_t *cu_seqlens_q;  // [B + 1]
-  const uint16_t *k_cache, *v_cache;
+  const void *k_cache, *v_cache;  // bf16 [NB, bs, Hkv, D], or fp8 [NB, Hkv, bs, D] (kv_fp8)
   const int32_t *block_tables;
   const int32_t *context_lens;
   uint16_t *out;              // [Tq, Hq, D]
@@ -54,6 +54,8 @@ struct PrefillArgs {
   int max_q_len;
   int split_len;              // keys per piece, multiple of 64
   int num_splits;
+  int kv_fp8;                 // pools hold fp8 codes, head-major [NB, Hkv, bs, D]
+  float v_scale;              // fp8 pools: value of V = code value * v_scale
 };
 
 hipError_t launch_append(const AppendArgs &a, int head_dim, hipStream_t stream);

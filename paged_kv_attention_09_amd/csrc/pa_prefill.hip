@@ -72,11 +72,39 @@ __device__ __forceinline__ int v_pos(int c, int r) {
   return ((((c >> 1) ^ (r & (D / 16 - 1)))) << 1) | (c & 1);
 }
 
-template <int D, int G>
+// fp8 pools: stored 16-byte position of chunk c of K row r (rows of D
+// bytes): the rows that share a 256-byte bank line get distinct positions,
+// so the 8-byte K fragment reads of 16 rows hit distinct banks.
+template <int D>
+__device__ __forceinline__ int k_pos8(int c, int r) {
+  return c ^ ((r >> (D == 128 ? 1 : 2)) & (D / 16 - 1));
+}
+
+// 8 fp8 (e4m3) codes -> 8 bf16 values (exact), element order kept.
+__device__ __forceinline__ uint4 fp8x8_to_bf16_p(uint2 v) {
+  return uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, true))};
+}
+
+// KV8: the pools hold fp8 codes, head-major [NB, Hkv, bs, D].  Tiles of
+// codes stream into LDS; K fragments widen to bf16 in registers, and each
+// tile's V is widened once, by all waves, into a bf16 tile laid out as the
+// bf16 path's V tile, which the unchanged transposed reads consume.  k_scale
+// is folded into the score scale, v_scale into the output.
+template <int D, int G, bool KV8>
 __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   using Lay = PrefillLayout<D>;
-  constexpr int ROWB = Lay::ROWB, TILEB = Lay::TILEB, NDMA = Lay::NDMA, KS = Lay::KSTEPS;
-  constexpr int DB = Lay::DBLK, RPD = Lay::ROWS_PER_DMA, NCH = Lay::NCH;
+  constexpr int ROWB = Lay::ROWB, TILEB = Lay::TILEB, KS = Lay::KSTEPS;
+  constexpr int DB = Lay::DBLK;
+  // rows as stored and staged (one byte per element for fp8)
+  constexpr int RB = KV8 ? D : ROWB;
+  constexpr int NCH = RB / 16;                    // 16-byte chunks per stored row
+  constexpr int TILEK = kKeys * RB;               // bytes of one staged K (or V) tile
+  constexpr int NDMA = TILEK / 1024;              // DMA instructions per tensor per tile
+  constexpr int RPD = 1024 / RB;                  // rows per DMA instruction
+  static_assert(RPD <= 16, "a DMA instruction stays inside one 16-row group");
   // Three tile buffers: two tiles in flight while one is computed.  The DMAs
   // of a tile are issued by NI waves (a power of two), NPW instructions each,
   // so every issuing wave waits on a fixed count.
@@ -84,7 +112,9 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   constexpr int NI = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
   constexpr int NPW = 2 * NDMA / NI;
   static_assert(NPW <= 63, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) char smem[NST][2][TILEB];  // [stage][K, V]
+  __shared__ __attribute__((aligned(1024))) char smem[NST][2][TILEK];  // [stage][K, V]
+  // fp8 pools: this tile's V as bf16 (one byte when unused)
+  __shared__ __attribute__((aligned(1024))) char vconv[KV8 ? TILEB : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // q head within the group
@@ -103,9 +133,12 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   const int h = g * G + w;
   const int bs_shift = a.bs_shift, bs_mask = (1 << bs_shift) - 1;
   const auto *table = as_const(a.block_tables + (size_t)b * a.max_blocks_per_seq);
-  const uint32_t RS = (uint32_t)Hkv * ROWB;
-  const char *kbase = (const char *)a.k_cache + (size_t)g * ROWB;
-  const char *vbase = (const char *)a.v_cache + (size_t)g * ROWB;
+  // bf16 pools [NB, bs, Hkv, D]: token rows of one kv head are Hkv rows
+  // apart; fp8 pools [NB, Hkv, bs, D]: (block, kv head) runs are contiguous.
+  const uint32_t RS = KV8 ? (uint32_t)RB : (uint32_t)Hkv * RB;
+  const size_t head_off = KV8 ? ((size_t)g * RB << bs_shift) : (size_t)g * RB;
+  const char *kbase = (const char *)a.k_cache + head_off;
+  const char *vbase = (const char *)a.v_cache + head_off;
   const int c16 = lane & 15, q4 = lane >> 4;
 
   // Q^T fragments: B operand of S^T = K Q^T.  Lane: query row c16 of each
@@ -145,7 +178,9 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
     const int jj = is_v ? j - NDMA : j;
     const int row_in = jj * RPD + lane / NCH;
     const int p = lane % NCH;
-    const int c = is_v ? v_pos<D>(p, row_in) : k_pos<D>(p, row_in);
+    // fp8 V tiles stay unswizzled: they are only read by the widening pass
+    const int c = KV8 ? (is_v ? p : k_pos8<D>(p, row_in))
+                      : (is_v ? v_pos<D>(p, row_in) : k_pos<D>(p, row_in));
     dma_voff[jw] = (uint32_t)(row_in & 15) * RS + (uint32_t)c * 16;
   }
   auto issue_tile = [&](int kt0, int buf, const int (&blk)[4]) {
@@ -154,9 +189,10 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int kg = kt0 + 16 * q;
-      const size_t row0 = ((size_t)(uint32_t)blk[q] << bs_shift) + (size_t)(kg & bs_mask);
-      gk[q] = kbase + row0 * RS;
-      gv[q] = vbase + row0 * RS;
+      const size_t rows = ((size_t)(uint32_t)blk[q] << bs_shift) * (KV8 ? Hkv : 1);
+      const size_t off = (rows + (size_t)(kg & bs_mask)) * RS;
+      gk[q] = kbase + off;
+      gv[q] = vbase + off;
     }
     const bool edge_tile = kt0 + kKeys > kend;
 #pragma unroll
@@ -202,9 +238,13 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   // = chunk ^ c16; the key block adds 16 rows.  V^T fragment (head_dim block
   // db, key step kk): source row 4 q4 + c16 / 4 (+ 32 kk, + 16 for the upper
   // half), columns 16 db + 4 (c16 % 4) in the 32-byte pair db ^ (row & 7).
+  // fp8 pools: K fragment (mb, ks) is 8 bytes of row 16 mb + c16 at chunk
+  // 2 ks + q4 / 2, half q4 % 2.
   int k_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = c16 * ROWB + k_pos<D>(ks * 4 + q4, c16) * 16;
+  for (int ks = 0; ks < KS; ++ks)
+    k_off[ks] = KV8 ? c16 * RB + k_pos8<D>(2 * ks + (q4 >> 1), c16) * 16 + (q4 & 1) * 8
+                    : c16 * ROWB + k_pos<D>(ks * 4 + q4, c16) * 16;
   const int tr_row = 4 * q4 + (c16 >> 2);
   int v_off[DB];
 #pragma unroll
@@ -226,14 +266,33 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
       if (it + 3 < ntiles) tile_blocks(kt0 + 3 * kKeys, blk_a);   // consumed next iteration
     }
     const char *Kt = smem[it % NST][0];
-    const char *Vt = smem[it % NST][1];
+    const char *Vt = KV8 ? vconv : smem[it % NST][1];
+    if constexpr (KV8) {
+      // widen this tile's V to bf16, every thread a few 16-code chunks:
+      // chunk c of row r becomes bf16 chunks 2c, 2c+1, one swizzled pair
+      const char *v8 = smem[it % NST][1];
+      for (int idx = threadIdx.x; idx < kKeys * NCH; idx += 64 * G) {
+        const int r = idx / NCH, c = idx % NCH;
+        const uint4 raw = *(const uint4 *)(v8 + r * RB + c * 16);
+        char *dst = vconv + r * ROWB + v_pos<D>(2 * c, r) * 16;
+        *(uint4 *)dst = fp8x8_to_bf16_p(uint2{raw.x, raw.y});
+        *(uint4 *)(dst + 16) = fp8x8_to_bf16_p(uint2{raw.z, raw.w});
+      }
+    }
 
     // ---- S^T = K Q^T: 4 key blocks x 2 row blocks, 8 independent chains ----
     f32x4 s[4][2];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    auto kfrag = [&](int ks, int mb) __attribute__((always_inline)) {
+      const char *p = Kt + k_off[ks] + mb * 16 * RB;
+      if constexpr (KV8)
+        return fp8x8_to_bf16_p(*(const uint2 *)p);
+      else
+        return *(const uint4 *)p;
+    };
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const uint4 kf = *(const uint4 *)(Kt + k_off[0] + mb * 16 * ROWB);
+      const uint4 kf = kfrag(0, mb);
       s[mb][0] = mfma_k32(kf, qf[0][0], zero4);
       s[mb][1] = mfma_k32(kf, qf[1][0], zero4);
     }
@@ -241,7 +300,7 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
     for (int ks = 1; ks < KS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const uint4 kf = *(const uint4 *)(Kt + k_off[ks] + mb * 16 * ROWB);
+        const uint4 kf = kfrag(ks, mb);
         s[mb][0] = mfma_k32(kf, qf[0][ks], s[mb][0]);
         s[mb][1] = mfma_k32(kf, qf[1][ks], s[mb][1]);
       }
@@ -319,6 +378,8 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
       }
     }
 
+    // fp8 pools: every wave's widened V is in place
+    if constexpr (KV8) __syncthreads();
     // ---- O^T += V^T P^T, and the row sums l += ones P^T on the same unit ----
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -343,7 +404,8 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
     const int i = i0 + nb * 16 + c16;
     if (i >= n) continue;
     const size_t row = (size_t)(q0 + i) * Hq + h;
-    const float inv = l != 0.f ? 1.f / l : 0.f;
+    float inv = l != 0.f ? 1.f / l : 0.f;
+    if constexpr (KV8) inv *= a.v_scale;
     if (a.o_part == nullptr) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -463,7 +525,10 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int r
 template <int D, int G>
 hipError_t launch_prefill_dg(const PrefillArgs &a, hipStream_t stream) {
   dim3 grid((a.max_q_len + kQRows - 1) / kQRows, a.num_kv_heads * a.num_splits, a.num_seqs);
-  hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(64 * G), 0, stream, a);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL((prefill_kernel<D, G, true>), grid, dim3(64 * G), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, G, false>), grid, dim3(64 * G), 0, stream, a);
   return hipGetLastError();
 }
 

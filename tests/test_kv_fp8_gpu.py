@@ -272,3 +272,68 @@ def test_decode_multi_fp8_one_token_is_decode_fp8():
         a = to_bits(_run_multi_fp8(inp, q1, k8, v8, 0.4, 0.3, S))[:, 0]
         b = to_bits(_run_fp8(inp, k8, v8, 0.4, 0.3, S))
         assert np.array_equal(a, b), S
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill over fp8 pools
+# ---------------------------------------------------------------------------
+
+
+class PrefillCase8:
+    """A prompt chunk over an fp8 pool: the cached prefix holds random codes,
+    the chunk's own K/V rows go in through the device's quantising append
+    (and the oracle's on the host), then prefill runs."""
+
+    def __init__(self, spec, ks, vs):
+        inp = W.make_prefill_inputs(spec)
+        self.inp, self.spec, self.ks, self.vs = inp, spec, ks, vs
+        k8, v8 = W.fp8_codes_like(inp)
+        self.k_cache, self.v_cache = device_pool8(inp, k8, v8)
+        pa.reshape_and_cache_fp8(bf16_tensor(inp.new_k), bf16_tensor(inp.new_v),
+                                 torch.from_numpy(inp.slot_mapping).to(DEV), self.k_cache,
+                                 self.v_cache, ks, vs)
+        bs = spec.block_size
+        lut = {int(x): i for i, x in enumerate(inp.pool.ids)}
+        slots = np.array([lut[int(s) // bs] * bs + int(s) % bs for s in inp.slot_mapping],
+                         np.int64)
+        k8, v8 = O8.append_fp8(inp.new_k, inp.new_v, slots, k8, v8, ks, vs)
+        ct = inp.pool.compact_tables(inp.block_tables, inp.poison_block)
+        self.ref = O8.prefill_fp8(inp.q, inp.cu_seqlens_q, k8, v8, ct, inp.context_lens,
+                                  inp.scale, ks, vs)
+        self.q = bf16_tensor(inp.q)
+        self.cu = torch.from_numpy(inp.cu_seqlens_q).to(DEV)
+        self.tables = torch.from_numpy(inp.block_tables).to(DEV)
+        self.lens = torch.from_numpy(inp.context_lens).to(DEV)
+        self.max_q = int(max(spec.chunk_lens))
+
+    def run(self, S):
+        out = torch.empty_like(self.q)
+        pa.prefill_fp8(self.q, self.cu, self.k_cache, self.v_cache, self.tables, self.lens,
+                       float(self.inp.scale), self.ks, self.vs, out, self.max_q, num_splits=S)
+        torch.cuda.synchronize()
+        return to_f64(out)
+
+
+@pytest.mark.parametrize("D,G,bs,chunks,totals", [
+    (128, 7, 256, (37, 1, 64), (300, 1, 64)),       # ragged; a 1-token chunk; prefix 0
+    (128, 2, 16, (100, 33), (1000, 33)),
+    (64, 1, 16, (65, 7), (129, 520)),
+    (64, 8, 256, (31,), (2100,)),
+    (128, 5, 16, (96,), (96,)),                       # whole prompt, no prefix
+])
+def test_prefill_fp8_shapes(D, G, bs, chunks, totals):
+    W_ = -(-max(totals) // bs)
+    nb = sum(-(-t // bs) for t in totals) + 5
+    spec = W.PrefillSpec(f"p8{D}_{G}_{bs}", 2 * G, 2, D, bs, nb, W_, chunk_lens=chunks,
+                         total_lens=totals, seed=D * 10 + G + 1)
+    case = PrefillCase8(spec, 0.37, 0.029)
+    for S in (1, 2, 0):
+        assert_close(case.run(S), case.ref, what=f"fp8 prefill D{D} G{G} bs{bs} S{S}")
+
+
+@pytest.mark.parametrize("S", [0, 3])
+def test_prefill_fp8_chunk_512_of_4096(S):
+    """The 512-token chunk over a 3584-token prefix (28 q / 4 kv heads, bs 256)
+    on fp8 pools."""
+    case = PrefillCase8(W.PREFILL_CONFIGS["c5p"], 0.5, 0.25)
+    assert_close(case.run(S), case.ref, what=f"fp8 chunk512 S={S}")

@@ -378,8 +378,9 @@ def random_e4m3_codes(seed: int, tags: Sequence[int], shape) -> np.ndarray:
     return (sign | expo | mant).astype(np.uint8)
 
 
-def fp8_codes_like(inp: "DecodeInputs"):
-    """fp8 pools for the blocks, tables and lengths of ``inp``: each referenced
+def fp8_codes_like(inp):
+    """fp8 pools for the blocks, tables and lengths of ``inp`` (decode or
+    prefill inputs): each referenced
     block draws its own codes (streams keyed by seed and block id), and every
     slot that ``inp``'s bf16 pool poisons holds E4M3_NAN.  Returns the K and V
     codes, stored densely like ``inp.pool`` but head-major, [n, Hkv, bs, D],
