@@ -223,6 +223,22 @@ int pa_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
                   size_t workspace_bytes, void *stream);
 
 /*
+ * pa_append_decode over fp8 pools: for every sequence b with
+ * context_lens[b] > 0, first stores new_k[b], new_v[b] (bf16 [num_seqs,
+ * num_kv_heads, head_dim]) quantised as pa_reshape_and_cache_fp8 quantises
+ * them to the cache row of token context_lens[b] - 1, then computes what
+ * pa_decode_fp8 computes - in one launch, the workgroup that reads a
+ * sequence's last token writing it first.  Scales, pools and the other
+ * arguments as for pa_decode_fp8.
+ */
+int pa_append_decode_fp8(const void *q, const void *new_k, const void *new_v, void *k_cache,
+                         void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                         float scale, float k_scale, float v_scale, int num_splits, void *out,
+                         int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                         int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pa_decode_multi over fp8 pools: q_len query tokens per sequence, causal
  * among themselves (the speculative verify step), with K and V dequantised
  * as for pa_decode_fp8.  q, out, workspace (pa_decode_multi_workspace_size)

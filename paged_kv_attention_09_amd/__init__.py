@@ -18,6 +18,7 @@ Calls (argument order as in the C ABI):
   reshape_and_cache_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream=None)
   decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
              num_splits, out, stream=None, workspace=None): fp8 (e4m3) pools
+  append_decode_fp8(...): append_decode over fp8 pools (quantising fused append)
   decode_multi_fp8(...): decode_multi over fp8 pools
   prefill_fp8(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
               v_scale, out, max_q_len, num_splits=0, stream=None, workspace=None)
@@ -74,6 +75,8 @@ SIGNATURES = {
                                       _VP]),
     "pa_decode_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _F, _F, _I, _VP, _I, _I, _I, _I, _I, _I64,
                            _I, _VP, _SZ, _VP]),
+    "pa_append_decode_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F, _F, _F, _I, _VP, _I, _I,
+                                  _I, _I, _I, _I64, _I, _VP, _SZ, _VP]),
     "pa_decode_multi_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _F, _F, _I, _VP, _I, _I, _I, _I, _I,
                                  _I, _I64, _I, _VP, _SZ, _VP]),
     # host-side block manager (include/pa_block_manager.h)
@@ -263,6 +266,32 @@ def decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float, k_
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), float(scale), float(k_scale), float(v_scale), int(num_splits),
         out.data_ptr(), B, Hq, Hkv, D, bs, NB, W, ws_ptr, ws_bytes, _stream_ptr(stream, dev)))
+    return out
+
+
+def append_decode_fp8(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens,
+                      scale: float, k_scale: float, v_scale: float, num_splits: int, out,
+                      stream=None, workspace: Optional[torch.Tensor] = None):
+    """append_decode over fp8 pools (uint8 e4m3 codes [NB, Hkv, bs, D]): the
+    new rows (bf16 [B, Hkv, D]) are quantised into the row of token
+    context_lens[b] - 1, then decode_fp8."""
+    NB, bs, Hkv, D, B, Hq, W, dev = _decode_dims(q, k_cache, v_cache, block_tables, context_lens,
+                                                 torch.uint8)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(new_k, "new_k", torch.bfloat16, 3, dev)
+    _need(new_v, "new_v", torch.bfloat16, 3, dev)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError(f"out must be [{B}, {Hq}, {D}]")
+    if tuple(new_k.shape) != (B, Hkv, D) or tuple(new_v.shape) != (B, Hkv, D):
+        raise ValueError(f"new_k/new_v must be [{B}, {Hkv}, {D}]")
+    if num_splits == 0 and B > 0:
+        num_splits = auto_splits(B, Hkv, W, bs, dev)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace)
+    _check("pa_append_decode_fp8", lib().pa_append_decode_fp8(
+        q.data_ptr(), new_k.data_ptr(), new_v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), float(k_scale),
+        float(v_scale), int(num_splits), out.data_ptr(), B, Hq, Hkv, D, bs, NB, W, ws_ptr,
+        ws_bytes, _stream_ptr(stream, dev)))
     return out
 
 
@@ -479,7 +508,7 @@ def prefill_auto_splits(num_seqs, max_q_len, num_kv_heads, max_blocks_per_seq, b
 __all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "decode_merge", "prefill",
            "prefill_workspace_size", "prefill_auto_splits", "decode_workspace_size", "plan_splits",
            "auto_splits", "decode_multi", "decode_multi_workspace_size", "reshape_and_cache_fp8",
-           "decode_fp8", "decode_multi_fp8", "prefill_fp8", "BlockManager", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError",
+           "decode_fp8", "append_decode_fp8", "decode_multi_fp8", "prefill_fp8", "BlockManager", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError",
            "PA_MAX_SPLITS", "PA_MAX_QUERY_TOKENS"]
 
 

@@ -224,6 +224,7 @@ int resolve_decode(const void *q, const void *k_cache, const void *v_cache,
   a->q_len = 1;
   a->kv_fp8 = 0;
   a->v_scale = 1.0f;
+  a->inv_k_scale = a->inv_v_scale = 1.0f;
   return PA_OK;
 }
 
@@ -336,6 +337,36 @@ int pa_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
   a.kv_fp8 = 1;
   a.v_scale = v_scale;
   a.out = (uint16_t *)out;
+  if (a.num_splits > 1) {
+    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+  }
+  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
+                                (hipStream_t)stream);
+}
+
+int pa_append_decode_fp8(const void *q, const void *new_k, const void *new_v, void *k_cache,
+                         void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                         float scale, float k_scale, float v_scale, int num_splits, void *out,
+                         int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                         int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  if (!(valid_kv_scale(k_scale) && valid_kv_scale(v_scale))) return PA_ERR_SHAPE;
+  pa::DecodeArgs a;
+  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!out || !new_k || !new_v) return PA_ERR_NULL;
+  a.scale_log2 = (scale * k_scale) * 1.4426950408889634f;
+  if (!std::isfinite(a.scale_log2)) return PA_ERR_SHAPE;
+  a.kv_fp8 = 1;
+  a.v_scale = v_scale;
+  a.inv_k_scale = 1.0f / k_scale;
+  a.inv_v_scale = 1.0f / v_scale;
+  a.out = (uint16_t *)out;
+  a.new_k = (const uint16_t *)new_k;
+  a.new_v = (const uint16_t *)new_v;
   if (a.num_splits > 1) {
     st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
     if (st != PA_OK) return st;

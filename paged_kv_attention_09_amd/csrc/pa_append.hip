@@ -36,24 +36,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int vec_per_r
 }
 
 // fp8 pools ([NB, Hkv, bs, D], head-major): each lane reads 8 bf16 of K and
-// of V (16 bytes each) and writes their 8 codes (8 bytes each) to the row of
-// its kv head.  The code of x is e4m3 of
-// clamp(x * (1 / scale), -448, 448), product in fp32, rounded to nearest
-// even; the comparisons keep a NaN product NaN.
-__device__ __forceinline__ float clamp448(float y) {
-  return y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
-}
-
-__device__ __forceinline__ uint2 quantize8(uint4 x, float inv) {
-  auto lo = [&](uint32_t w) { return clamp448(__uint_as_float(w << 16) * inv); };
-  auto hi = [&](uint32_t w) { return clamp448(__uint_as_float(w & 0xFFFF0000u) * inv); };
-  // word_sel false fills bytes 0-1, true bytes 2-3 (keeping the others)
-  int a = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.x), hi(x.x), 0, false);
-  a = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.y), hi(x.y), a, true);
-  int b = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.z), hi(x.z), 0, false);
-  b = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.w), hi(x.w), b, true);
-  return uint2{(uint32_t)a, (uint32_t)b};
-}
+// of V (16 bytes each) and writes their 8 codes (quantize8: 8 bytes each) to
+// the row of its kv head.
 
 __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, int vec_per_row) {
   const int64_t total = a.num_tokens * vec_per_row;

@@ -85,15 +85,6 @@ __device__ __forceinline__ int row_swizzle8(int r) {
   return (r >> (D == 128 ? 1 : 2)) & (D / 16 - 1);
 }
 
-// 8 fp8 (e4m3) codes -> 8 bf16 values (exact: every e4m3 value is a bf16
-// value), element order kept.
-__device__ __forceinline__ uint4 fp8x8_to_bf16(uint2 v) {
-  return uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, true)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, true))};
-}
-
 template <int D>
 struct DecodeGeom {
   static constexpr int ROWB = D * 2;                 // bytes of one token row (one kv head)
@@ -228,20 +219,23 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 
   // Fused append (single query token only): the wave that owns the
   // sequence's last token writes the new K/V row of this kv head to that
-  // token's slot, and waits for the stores to complete before it issues any
-  // load of the chunk holding the row.  Only this wave reads that row in this
-  // launch.
-  if (!KV8 && a.new_k != nullptr && t1 == L && wave == (nck - 1) % kWaves) {
+  // token's slot (fp8 pools: quantised, 8 elements per lane), and waits for
+  // the stores to complete before it issues any load of the chunk holding
+  // the row.  Only this wave reads that row in this launch.
+  if (!MULTI && a.new_k != nullptr && t1 == L && wave == (nck - 1) % kWaves) {
     constexpr int NPOS = Ge::NPOS;
     const int tl = L - 1;
-    const size_t row = ((size_t)(uint32_t)table[tl >> bs_shift] << bs_shift) + (tl & bs_mask);
+    const size_t roff = row_offset(table[tl >> bs_shift], tl & bs_mask);
     const size_t src = ((size_t)b * a.num_kv_heads + g) * ROWB;
     if (lane < 2 * NPOS) {
       const int c = lane % NPOS;
       const bool is_v = lane >= NPOS;
-      const char *from = (const char *)(is_v ? a.new_v : a.new_k) + src + c * 16;
-      char *to = (char *)(is_v ? vbase : kbase) + row * RS + c * 16;
-      *(uint4 *)to = *(const uint4 *)from;
+      const uint4 x = *(const uint4 *)((const char *)(is_v ? a.new_v : a.new_k) + src + c * 16);
+      char *to = (char *)(is_v ? vbase : kbase) + roff;
+      if constexpr (KV8)
+        *(uint2 *)(to + c * 8) = quantize8(x, is_v ? a.inv_v_scale : a.inv_k_scale);
+      else
+        *(uint4 *)(to + c * 16) = x;
     }
     wait_vmcnt<0>();
   }
@@ -798,10 +792,8 @@ hipError_t launch_split_dgk(const DecodeArgs &a, int num_seqs, hipStream_t strea
 
 template <int D, int G>
 hipError_t launch_split_dg(const DecodeArgs &a, int num_seqs, hipStream_t stream) {
-  if (a.kv_fp8) {
-    if (a.new_k != nullptr) return hipErrorInvalidValue;
-    return launch_split_dgk<D, G, true>(a, num_seqs, stream);
-  }
+  if (a.new_k != nullptr && a.q_len != 1) return hipErrorInvalidValue;
+  if (a.kv_fp8) return launch_split_dgk<D, G, true>(a, num_seqs, stream);
   return launch_split_dgk<D, G, false>(a, num_seqs, stream);
 }
 

@@ -81,6 +81,34 @@ __device__ __forceinline__ uint2 read_tr(const char *p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// ---- fp8 (OCP e4m3) codes ----
+// 8 codes -> 8 bf16 values (exact: every e4m3 value is a bf16 value), element
+// order kept.
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint2 v) {
+  return uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, true))};
+}
+
+__device__ __forceinline__ float clamp448(float y) {
+  return y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
+}
+
+// 8 bf16 values -> their 8 codes: e4m3 of clamp(x * inv, -448, 448), the
+// product in fp32, rounded to nearest even; the comparisons keep a NaN
+// product NaN.
+__device__ __forceinline__ uint2 quantize8(uint4 x, float inv) {
+  auto lo = [&](uint32_t w) { return clamp448(__uint_as_float(w << 16) * inv); };
+  auto hi = [&](uint32_t w) { return clamp448(__uint_as_float(w & 0xFFFF0000u) * inv); };
+  // word_sel false fills bytes 0-1, true bytes 2-3 (keeping the others)
+  int a = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.x), hi(x.x), 0, false);
+  a = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.y), hi(x.y), a, true);
+  int b = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.z), hi(x.z), 0, false);
+  b = __builtin_amdgcn_cvt_pk_fp8_f32(lo(x.w), hi(x.w), b, true);
+  return uint2{(uint32_t)a, (uint32_t)b};
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 

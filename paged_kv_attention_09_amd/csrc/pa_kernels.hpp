@@ -25,7 +25,7 @@ struct DecodeArgs {
   const void *v_cache;
   const int32_t *block_tables;  // [B, W]
   const int32_t *context_lens;  // [B], including the q_len query tokens
-  const uint16_t *new_k;      // [B, Hkv, D] rows appended at token L_b - 1, or null (q_len 1)
+  const uint16_t *new_k;      // bf16 [B, Hkv, D] rows appended at token L_b - 1, or null (q_len 1)
   const uint16_t *new_v;
   uint16_t *out;              // [B, q_len, Hq, D]        (num_splits == 1)
   float *o_part;              // [B, q_len, Hq, S, D]     (num_splits > 1)
@@ -36,8 +36,9 @@ struct DecodeArgs {
   int split_len;              // tokens per split, multiple of 64
   int num_splits;
   int q_len;                  // query tokens per sequence (1 = single-token decode)
-  int kv_fp8;                 // pools hold fp8 codes (single query token, no fused append)
+  int kv_fp8;                 // pools hold fp8 codes, head-major [NB, Hkv, bs, D]
   float v_scale;              // fp8 pools: value of V = code value * v_scale
+  float inv_k_scale, inv_v_scale;  // fp8 pools, fused append: 1 / scale, rounded to fp32
 };
 
 struct PrefillArgs {

@@ -80,14 +80,6 @@ __device__ __forceinline__ int k_pos8(int c, int r) {
   return c ^ ((r >> (D == 128 ? 1 : 2)) & (D / 16 - 1));
 }
 
-// 8 fp8 (e4m3) codes -> 8 bf16 values (exact), element order kept.
-__device__ __forceinline__ uint4 fp8x8_to_bf16_p(uint2 v) {
-  return uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, true)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.f, true))};
-}
-
 // KV8: the pools hold fp8 codes, head-major [NB, Hkv, bs, D].  Tiles of
 // codes stream into LDS; K fragments widen to bf16 in registers, and each
 // tile's V is widened once, by all waves, into a bf16 tile laid out as the
@@ -275,8 +267,8 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
         const int r = idx / NCH, c = idx % NCH;
         const uint4 raw = *(const uint4 *)(v8 + r * RB + c * 16);
         char *dst = vconv + r * ROWB + v_pos<D>(2 * c, r) * 16;
-        *(uint4 *)dst = fp8x8_to_bf16_p(uint2{raw.x, raw.y});
-        *(uint4 *)(dst + 16) = fp8x8_to_bf16_p(uint2{raw.z, raw.w});
+        *(uint4 *)dst = fp8x8_to_bf16(uint2{raw.x, raw.y});
+        *(uint4 *)(dst + 16) = fp8x8_to_bf16(uint2{raw.z, raw.w});
       }
     }
 
@@ -286,7 +278,7 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
     auto kfrag = [&](int ks, int mb) __attribute__((always_inline)) {
       const char *p = Kt + k_off[ks] + mb * 16 * RB;
       if constexpr (KV8)
-        return fp8x8_to_bf16_p(*(const uint2 *)p);
+        return fp8x8_to_bf16(*(const uint2 *)p);
       else
         return *(const uint4 *)p;
     };

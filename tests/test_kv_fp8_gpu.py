@@ -337,3 +337,47 @@ def test_prefill_fp8_chunk_512_of_4096(S):
     on fp8 pools."""
     case = PrefillCase8(W.PREFILL_CONFIGS["c5p"], 0.5, 0.25)
     assert_close(case.run(S), case.ref, what=f"fp8 chunk512 S={S}")
+
+
+# ---------------------------------------------------------------------------
+# append fused into the decode launch, fp8 pools
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,bs", [(128, 28, 4, 256), (128, 12, 2, 16), (64, 8, 8, 16),
+                                         (64, 16, 2, 256)])
+def test_append_decode_fp8_equals_separate_calls(D, Hq, Hkv, bs):
+    """The fused quantising append + decode gives the pool bytes and the
+    outputs of the quantising append followed by decode, bit for bit, and the
+    oracle's values."""
+    lens = (0, 1, 16, 17, 255, 256, 700)
+    spec = _small_spec(D, Hq, Hkv, bs, lens, seed=3100 + D + Hq + bs).with_(append=True)
+    inp = W.make_decode_inputs(spec, fill="zeros")
+    k8, v8 = W.fp8_codes_like(inp)             # appended slots hold NaN codes
+    ks, vs = 0.31, 0.043
+    tables = torch.from_numpy(inp.block_tables).to(DEV)
+    lens_t = torch.from_numpy(inp.context_lens).to(DEV)
+    q = bf16_tensor(inp.q)
+    sel = np.nonzero(inp.context_lens > 0)[0]
+    nk = np.zeros((len(lens), Hkv, D), np.uint16)
+    nv = np.zeros((len(lens), Hkv, D), np.uint16)
+    nk[sel], nv[sel] = inp.new_k, inp.new_v
+    for S in (1, 0):
+        kc1, vc1 = device_pool8(inp, k8, v8)
+        out1 = torch.empty((len(lens), Hq, D), dtype=torch.bfloat16, device=DEV)
+        pa.append_decode_fp8(q, bf16_tensor(nk), bf16_tensor(nv), kc1, vc1, tables, lens_t,
+                             float(inp.scale), ks, vs, S, out1)
+        kc2, vc2 = device_pool8(inp, k8, v8)
+        out2 = torch.empty_like(out1)
+        pa.reshape_and_cache_fp8(bf16_tensor(inp.new_k), bf16_tensor(inp.new_v),
+                                 torch.from_numpy(inp.slot_mapping).to(DEV), kc2, vc2, ks, vs)
+        pa.decode_fp8(q, kc2, vc2, tables, lens_t, float(inp.scale), ks, vs, S, out2)
+        torch.cuda.synchronize()
+        assert torch.equal(kc1, kc2) and torch.equal(vc1, vc2), S
+        assert np.array_equal(to_bits(out1), to_bits(out2)), S
+    bsz = spec.block_size
+    lut = {int(x): i for i, x in enumerate(inp.pool.ids)}
+    slots = np.array([lut[int(s) // bsz] * bsz + int(s) % bsz for s in inp.slot_mapping], np.int64)
+    k8a, v8a = O8.append_fp8(inp.new_k, inp.new_v, slots, k8, v8, ks, vs)
+    ref = _oracle_fp8(inp, k8a, v8a, ks, vs)
+    assert_close(to_f64(out1), ref, what=f"fused fp8 D={D} Hq={Hq} Hkv={Hkv} bs={bs}")
