@@ -369,12 +369,10 @@ class PrefillWorkload:
 
     def decode(self, r):
         if self.kv_fp8:
-            # fp8 pools: quantising append of the new rows, then decode
-            self.pa.reshape_and_cache_fp8(self.dk, self.dv, self.dslots[r], self.k_cache,
-                                          self.v_cache, self.k_scale, self.v_scale)
-            self.pa.decode_fp8(self.dq, self.k_cache, self.v_cache, self.dtables[r],
-                               self.dlens_t, self.scale, self.k_scale, self.v_scale, self.dS,
-                               self.dout, workspace=self.dws)
+            # fp8 pools: the quantising append fused into the decode launch
+            self.pa.append_decode_fp8(self.dq, self.dk, self.dv, self.k_cache, self.v_cache,
+                                      self.dtables[r], self.dlens_t, self.scale, self.k_scale,
+                                      self.v_scale, self.dS, self.dout, workspace=self.dws)
         else:
             self.pa.append_decode(self.dq, self.dk, self.dv, self.k_cache, self.v_cache,
                                   self.dtables[r], self.dlens_t, self.scale, self.dS, self.dout,
@@ -425,7 +423,7 @@ def measure_prefill(args, steps, warmup, with_decode: bool, kv_fp8: bool = False
                     "decode_gbps": wl.decode_bytes / (ms_dec * 1e-3) / 1e9,
                     "append_us": ms_app * 1e3, "decode_splits": wl.dS,
                     "step": ("quantising append of the 512-token chunk, MFMA prefill over fp8 "
-                             "pools, quantising append + fp8 decode of 64") if kv_fp8 else
+                             "pools, fused quantising append + fp8 decode of 64") if kv_fp8 else
                             "append 512-token chunk, MFMA prefill, fused append + decode of 64"})
     if kv_fp8:
         rec["kv"] = "fp8 e4m3, per-tensor scales"
