@@ -38,6 +38,15 @@
 //      head's statistics and output column share lanes, so a rescale is
 //      lane-local.  On the vector path the loop's ALU work grows with G and
 //      at G = 6..7 it, not the memory system, set the pace.
+//  * Several query tokens per sequence (the verify step of speculative
+//    decoding): the matrix path's tile columns become (query token, head)
+//    rows, one or two tiles, with query token j masking keys past
+//    L - q_len + j; every staged chunk serves all of them.
+//  * fp8 pools (e4m3 codes, head-major [NB, Hkv, bs, D]): the chunks stage
+//    one byte per element; K fragments widen to bf16 in registers, each
+//    chunk's V widens into a per-wave bf16 buffer read by the same
+//    transposed reads; k_scale is folded into the score scale and v_scale
+//    into the output.
 //  * The 4 waves' (m, l, O) are merged through LDS; the workgroup writes
 //    either the final bf16 rows (one piece) or fp32 partials plus their
 //    base-2 log-sum-exp for the combine kernel.
@@ -54,7 +63,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kChunk = 16;     // tokens per wave step
 constexpr int kStages = 2;     // chunks in flight per wave
-constexpr int kStages8 = 2;    // the same for fp8 pools
+constexpr int kStages8 = 2;    // the same for fp8 pools (3 or 4 measured slower)
 constexpr float kSlack = 8.f;  // log2 headroom before the running max moves
 constexpr int kMaxVectorGroup = 2;
 

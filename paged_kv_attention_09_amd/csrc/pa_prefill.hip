@@ -12,9 +12,9 @@
 //    pieces handled by separate workgroups (the same split-KV scheme as
 //    decode) and merged by log-sum-exp afterwards.
 //  * Key tiles of 64 rows stream into LDS by global_load_lds_dwordx4, three
-//    stages deep (two tiles in flight while one is computed).  K rows are stored with their 16-byte chunks XOR
-//    swizzled by row, V rows with their 32-byte column pairs swizzled, so the
-//    reads below hit distinct banks.
+//    stages deep (two tiles in flight while one is computed).  K rows are
+//    stored with their 16-byte chunks XOR swizzled by row, V rows with their
+//    32-byte column pairs swizzled, so the reads below hit distinct banks.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K fragments (keys x head_dim)
 //    come from LDS, Q^T fragments sit in registers for the whole launch.
 //    The result holds one query row per lane (row = lane % 16), so softmax
@@ -31,6 +31,10 @@
 //    tiles that cross them; elsewhere the scale folds into one fma per
 //    weight.  The row sums of P come from the matrix core too (a block of
 //    ones times P^T), not from per-element adds.
+//  * With the key range in pieces, each piece writes its normalised rows in
+//    bf16 and their base-2 log-sum-exp in fp32; the merge kernel combines
+//    them.
+//  * fp8 pools (KV8): see prefill_kernel.
 #include "pa_device.hpp"
 #include "pa_kernels.hpp"
 
