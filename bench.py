@@ -806,36 +806,38 @@ def measure(name, args, steps, warmup, with_kernel=True):
     return wl, rec
 
 
-def measure_read_ceiling():
-    """The read rate this GPU delivers for a plain streaming read, for context
-    next to the 8 TB/s peak: the library's read probe (16-byte vector loads,
-    grid-stride, no writes but one word per wave) over cold buffers of 32 MiB
-    (the size of the ctx-4096 batch-8 decode) and of 1 GiB, rotating over
-    2 GiB so that no read hits the last-level cache; the best of several
-    grid sizes, timed with HIP events over back-to-back launches."""
+def read_probe_gbps(nbytes: int) -> float:
+    """Read rate of the library's streaming-read probe (16-byte vector loads,
+    no writes but one word per wave) over cold buffers of `nbytes`, rotating
+    over at least 2 GiB so that no read hits the last-level cache; the best
+    of several grid sizes, HIP events over back-to-back launches."""
     import torch
 
     import paged_kv_attention_09_amd as pa
     L = pa.lib()
-    res = {}
+    nbytes = max(16, nbytes // 16 * 16)
     sink = torch.empty(4 * 16384, dtype=torch.int32, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
-    for mib in (32, 1024):
-        nbuf = max(2, 2048 // mib)
-        bufs = [torch.ones(mib << 18, dtype=torch.int32, device="cuda:0") for _ in range(nbuf)]
-        best = 0.0
-        for wgs in (1024, 2048, 4096, 8192, 16384):
-            def launch(i):
-                st = L.pa_read_probe(bufs[i % nbuf].data_ptr(), mib << 20, sink.data_ptr(), wgs,
-                                     stream)
-                if st != 0:
-                    raise RuntimeError(f"pa_read_probe failed with status {st}")
-            n = 2 * nbuf
-            ms = time_kernel_events(launch, n, nbuf)
-            best = max(best, (mib << 20) / (ms * 1e-3) / 1e9)
-        res[f"read_{mib}MiB_gbps"] = round(best, 1)
-        del bufs
-        torch.cuda.empty_cache()
+    nbuf = max(2, -(-(2 << 30) // nbytes))
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0") for _ in range(nbuf)]
+    best = 0.0
+    for wgs in (1024, 2048, 4096, 8192, 16384):
+        def launch(i):
+            st = L.pa_read_probe(bufs[i % nbuf].data_ptr(), nbytes, sink.data_ptr(), wgs, stream)
+            if st != 0:
+                raise RuntimeError(f"pa_read_probe failed with status {st}")
+        ms = time_kernel_events(launch, max(2 * nbuf, 16), nbuf)
+        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+    del bufs
+    torch.cuda.empty_cache()
+    return best
+
+
+def measure_read_ceiling():
+    """The read rate a plain streaming read reaches on this GPU, for context
+    next to the 8 TB/s peak: cold buffers of 32 MiB (the size of the ctx-4096
+    batch-8 decode) and of 1 GiB."""
+    res = {f"read_{mib}MiB_gbps": round(read_probe_gbps(mib << 20), 1) for mib in (32, 1024)}
     res["probe"] = ("pa_read_probe: 16-byte vector loads over a cold buffer, best of 1024-16384 "
                     "workgroups, HIP events over back-to-back launches")
     return res
@@ -1076,6 +1078,12 @@ def main(argv=None):
           "prefix cache", file=sys.stderr, flush=True)
     others["host_block_manager"] = bm_rec
     ceiling = measure_read_ceiling()
+    # each decode workload's split kernel against a plain read of its own bytes
+    for name, rec in others.items():
+        if "kernel_gbps" in rec and "decode_bytes" in rec:
+            probe = read_probe_gbps(int(rec["decode_bytes"]))
+            rec["read_probe_gbps_same_bytes"] = round(probe, 1)
+            rec["kernel_frac_of_read_probe"] = round(rec["kernel_gbps"] / probe, 4)
     print(f"[bench] measured read rate (read probe, cold): 32 MiB {ceiling['read_32MiB_gbps']:.0f} "
           f"GB/s, 1 GiB {ceiling['read_1024MiB_gbps']:.0f} GB/s", file=sys.stderr, flush=True)
 
