@@ -30,7 +30,9 @@
  *     All device work is enqueued on it; no call synchronises, allocates or
  *     frees memory, or reads device memory on the host.
  *   - Supported shapes: head_dim 64 or 128; block_size 16 or 256;
- *     num_q_heads a multiple of num_kv_heads with a group of 1..8.
+ *     num_q_heads a multiple of num_kv_heads with a group of 1..8;
+ *     num_q_heads <= PA_MAX_HEADS and num_seqs <= PA_MAX_SEQS (launch grid
+ *     limits), else PA_ERR_SHAPE.
  *   - Errors are reported only through the returned status; on any status
  *     other than PA_OK from argument checking, nothing was enqueued.
  *     PA_ERR_HIP means a launch failed (hipGetLastError).  Faults inside a
@@ -65,6 +67,8 @@ enum {
 
 #define PA_MAX_SPLITS 256
 #define PA_MAX_QUERY_TOKENS 8
+#define PA_MAX_SEQS 65535
+#define PA_MAX_HEADS 4096
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
 int pa_version(void);

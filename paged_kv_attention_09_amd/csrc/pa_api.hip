@@ -26,7 +26,7 @@ int log2_exact(int v) {
 }
 
 int check_heads(int num_q_heads, int num_kv_heads, int head_dim) {
-  if (num_q_heads <= 0 || num_kv_heads <= 0) return PA_ERR_SHAPE;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads > PA_MAX_HEADS) return PA_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   const int g = num_q_heads / num_kv_heads;
@@ -187,7 +187,7 @@ int resolve_decode(const void *q, const void *k_cache, const void *v_cache,
                    const int32_t *block_tables, const int32_t *context_lens, float scale,
                    int num_splits, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                    int block_size, int64_t num_blocks, int max_blocks_per_seq, pa::DecodeArgs *a) {
-  if (num_seqs < 0) return PA_ERR_SHAPE;
+  if (num_seqs < 0 || num_seqs > PA_MAX_SEQS) return PA_ERR_SHAPE;
   int st = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (st != PA_OK) return st;
   st = check_pool(num_blocks, block_size, max_blocks_per_seq);
@@ -215,6 +215,7 @@ int resolve_decode(const void *q, const void *k_cache, const void *v_cache,
   a->o_part = nullptr;
   a->lse_part = nullptr;
   a->scale_log2 = scale * 1.4426950408889634f;
+  if (!std::isfinite(a->scale_log2)) return PA_ERR_SHAPE;
   a->num_q_heads = num_q_heads;
   a->num_kv_heads = num_kv_heads;
   a->max_blocks_per_seq = max_blocks_per_seq;
@@ -481,7 +482,7 @@ int prefill_impl(const void *q, const int32_t *cu_seqlens_q, const void *k_cache
                  int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                  int block_size, int64_t num_blocks, int max_blocks_per_seq, void *workspace,
                  size_t workspace_bytes, void *stream) {
-  if (num_seqs < 0 || max_q_len < 0) return PA_ERR_SHAPE;
+  if (num_seqs < 0 || max_q_len < 0 || num_seqs > PA_MAX_SEQS) return PA_ERR_SHAPE;
   if (fp8 && !(valid_kv_scale(k_scale) && valid_kv_scale(v_scale))) return PA_ERR_SHAPE;
   int st = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (st != PA_OK) return st;
@@ -525,6 +526,9 @@ int prefill_impl(const void *q, const int32_t *cu_seqlens_q, const void *k_cache
   a.max_q_len = max_q_len;
   a.split_len = split_len_for(max_tokens, num_splits);
   a.num_splits = num_pieces(max_tokens, a.split_len);
+  // launch grid: (kv head, piece) workgroups in y; query rows counted in int
+  if ((int64_t)num_kv_heads * a.num_splits > 65535) return PA_ERR_SHAPE;
+  if ((int64_t)num_seqs * max_q_len * num_q_heads > INT32_MAX) return PA_ERR_SHAPE;
   if (a.num_splits > 1) {
     const size_t need = pa_prefill_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim,
                                                   a.num_splits);

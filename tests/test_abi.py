@@ -55,6 +55,8 @@ def _decode(**kw):
     (dict(B=-1), SHAPE), (dict(q=None), NULL), (dict(tables=None), NULL), (dict(out=None), NULL),
     (dict(S=4), WS), (dict(S=4, ws=P, wsb=100), WS), (dict(scale=float("nan")), SHAPE),
     (dict(B=0), OK), (dict(B=0, q=None), OK),
+    (dict(scale=3e38), SHAPE),                     # scale * log2(e) overflows fp32
+    (dict(B=65536), SHAPE), (dict(Hq=8192, Hkv=1024), SHAPE),   # launch grid limits
 ])
 def test_decode_argument_checks(kw, code):
     assert _decode(**kw) == code
@@ -176,6 +178,12 @@ def test_prefill_argument_checks():
     assert f(*bad) == SPLITS
     ok0 = list(args); ok0[10] = 0
     assert f(*ok0) == OK
+    bad = list(args); bad[9] = 65536              # more sequences than the grid holds
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[11], bad[12], bad[7], bad[16] = 2048, 256, 256, 256   # 256 x 256 pieces
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[10] = 1 << 20; bad[11], bad[12] = 4096, 512   # 2^32 query rows
+    assert f(*bad) == SHAPE
 
 
 def test_prefill_planning():
