@@ -45,6 +45,8 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libpagedattn.so")
 PA_OK = 0
 PA_MAX_SPLITS = 256
 PA_MAX_QUERY_TOKENS = 8
+PA_MAX_SEQS = 65535
+PA_MAX_HEADS = 4096
 
 # Every symbol include/pagedattn.h declares, with its ctypes signature.
 _VP, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -509,7 +511,7 @@ __all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "d
            "prefill_workspace_size", "prefill_auto_splits", "decode_workspace_size", "plan_splits",
            "auto_splits", "decode_multi", "decode_multi_workspace_size", "reshape_and_cache_fp8",
            "decode_fp8", "append_decode_fp8", "decode_multi_fp8", "prefill_fp8", "BlockManager", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError",
-           "PA_MAX_SPLITS", "PA_MAX_QUERY_TOKENS"]
+           "PA_MAX_SPLITS", "PA_MAX_QUERY_TOKENS", "PA_MAX_SEQS", "PA_MAX_HEADS"]
 
 
 class BlockManager:

@@ -223,3 +223,11 @@ def test_plan_splits():
         assert s == -(-max_tokens // ((c + 63) // 64 * 64))
     assert plan(0, 2, 256, 16, 256) == SHAPE and plan(1, 2, 256, 16, 0) == SHAPE
     assert plan(1, 2, 256, 32, 256) == UNSUP
+
+
+def test_binding_constants_match_header():
+    text = open(os.path.join(INCLUDE, "pagedattn.h")).read()
+    defines = dict(re.findall(r"#define (PA_MAX_\w+) (\d+)", text))
+    assert set(defines) == {"PA_MAX_SPLITS", "PA_MAX_QUERY_TOKENS", "PA_MAX_SEQS", "PA_MAX_HEADS"}
+    for name, value in defines.items():
+        assert getattr(pa, name) == int(value), name
