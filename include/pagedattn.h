@@ -40,7 +40,9 @@
  *   - Device-resident preconditions are NOT checked (checking would need a
  *     host sync): block ids in [0, num_blocks); context_lens[b] <=
  *     max_blocks_per_seq * block_size; valid slots unique within one call.
- *     Violating them is undefined behaviour.
+ *     Violating them is undefined behaviour.  pa_check_tables,
+ *     pa_check_slots and pa_check_prefill (end of this header) check them
+ *     on host copies, for tests and debug builds.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -365,6 +367,64 @@ size_t pa_prefill_workspace_size(int num_seqs, int max_q_len, int num_q_heads, i
  * in [1, PA_MAX_SPLITS] or a negative status. */
 int pa_prefill_plan_splits(int num_seqs, int max_q_len, int num_kv_heads, int max_blocks_per_seq,
                            int block_size, int num_cus);
+
+/*
+ * Debug validation of the device-resident preconditions that the calls above
+ * leave unchecked (checking them there would need a host synchronisation).
+ * These run on the host, on HOST copies of the integer inputs: a caller (a
+ * test, or a serving loop in a debug build) copies its tables, lengths, slots
+ * or query offsets back, synchronously, and calls the check before the
+ * attention call that will read them.  Plain host code: no HIP call, no
+ * device access, nothing allocated on the device.
+ *
+ * Return value: PA_CHECK_OK when every precondition holds, else the kind of
+ * the first violation found (a positive PA_CHECK_* code), with *bad_index set
+ * (when bad_index is not NULL) to the offending sequence b or token i (-1 on
+ * success); a negative PA_ERR_* status for invalid arguments (NULL pointers,
+ * sizes out of range), with nothing checked.
+ */
+enum {
+  PA_CHECK_OK = 0,
+  PA_CHECK_LENGTH = 1,          /* context_lens[b] < 0 or > max_blocks_per_seq * block_size */
+  PA_CHECK_BLOCK_ID = 2,        /* an entry block_tables[b, j] with j < ceil(L_b / block_size)
+                                   lies outside [0, num_blocks)                              */
+  PA_CHECK_APPEND_SHARED = 3,   /* fused append: the block receiving sequence b's new row is
+                                   also read through another table entry in the same call   */
+  PA_CHECK_SLOT_RANGE = 4,      /* slot_mapping[i] >= num_blocks * block_size                 */
+  PA_CHECK_SLOT_DUPLICATE = 5,  /* slot_mapping[i] equals a valid slot of an earlier token    */
+  PA_CHECK_QUERY_OFFSETS = 6    /* cu_seqlens_q[0] != 0, decreasing, n_b > max_q_len or
+                                   n_b > context_lens[b]                                     */
+};
+
+/* Preconditions of pa_decode, pa_decode_multi, pa_decode_partials and their fp8
+ * counterparts over host copies of block_tables [num_seqs, max_blocks_per_seq]
+ * and context_lens [num_seqs]: every length in [0, max_blocks_per_seq *
+ * block_size], every table entry a sequence reads in [0, num_blocks).  With
+ * fused_append != 0 (pa_append_decode, pa_append_decode_fp8), also that the
+ * block holding each non-empty sequence's last token (the row the call
+ * writes) is read through no other table entry of the call, so no workgroup
+ * reads a row while another writes it.  Lengths and entries are checked
+ * sequence by sequence (a sequence's length before its entries); the
+ * fused-append condition only once they all hold.  Requires block_size a
+ * power of two, num_seqs >= 0, max_blocks_per_seq >= 1, num_blocks >= 1. */
+int pa_check_tables(const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                    int max_blocks_per_seq, int block_size, int64_t num_blocks,
+                    int fused_append, int64_t *bad_index);
+
+/* Preconditions of pa_reshape_and_cache(_fp8) over a host copy of
+ * slot_mapping [num_tokens]: every non-negative slot below num_blocks *
+ * block_size and no valid slot repeated.  The reported token is the first one
+ * (in token order) that is out of range or repeats an earlier valid slot. */
+int pa_check_slots(const int64_t *slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                   int block_size, int64_t *bad_index);
+
+/* Preconditions of pa_prefill(_fp8) on the query offsets, over host copies of
+ * cu_seqlens_q [num_seqs + 1] and context_lens [num_seqs]: cu_seqlens_q[0] = 0,
+ * non-decreasing, and every chunk n_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b]
+ * at most max_q_len and at most context_lens[b].  Pair it with
+ * pa_check_tables for the tables and lengths. */
+int pa_check_prefill(const int32_t *cu_seqlens_q, const int32_t *context_lens, int num_seqs,
+                     int max_q_len, int64_t *bad_index);
 
 #ifdef __cplusplus
 }

@@ -30,6 +30,10 @@ Calls (argument order as in the C ABI):
   auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, device=None)
   BlockManager(num_blocks, block_size, max_blocks_per_seq, prefix_cache): the host-side
       pool manager (admit / append / truncate / release / preempt / block_tables / stats)
+  check_tables(block_tables, context_lens, num_blocks, block_size, fused_append=False),
+  check_slots(slot_mapping, num_blocks, block_size),
+  check_prefill(cu_seqlens_q, context_lens, max_q_len): synchronous debug checks of the
+      preconditions the calls above leave unchecked (host copies; raise PreconditionError)
 """
 from __future__ import annotations
 
@@ -37,6 +41,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +97,10 @@ SIGNATURES = {
     "pa_bm_preempt": (_I, [_VP, _VP]),
     "pa_bm_block_tables": (_I, [_VP, _VP, _I, _VP, _VP]),
     "pa_bm_stats": (_I, [_VP, _VP, _VP, _VP, _VP]),
+    # host-side precondition checks (end of include/pagedattn.h)
+    "pa_check_tables": (_I, [_VP, _VP, _I, _I, _I, _I64, _I, _VP]),
+    "pa_check_slots": (_I, [_VP, _I64, _I64, _I, _VP]),
+    "pa_check_prefill": (_I, [_VP, _VP, _I, _I, _VP]),
     # measurement probe (include/pagedattn_probe.h)
     "pa_read_probe": (_I, [_VP, _SZ, _VP, _I, _VP]),
 }
@@ -507,11 +516,97 @@ def prefill_auto_splits(num_seqs, max_q_len, num_kv_heads, max_blocks_per_seq, b
     return r
 
 
+# Kinds of precondition violation reported by the pa_check_* calls.
+PA_CHECK_OK = 0
+PA_CHECK_KINDS = {
+    1: "context length outside [0, max_blocks_per_seq * block_size]",
+    2: "block table entry read by the sequence outside [0, num_blocks)",
+    3: "the block receiving the fused append is also read through another table entry",
+    4: "slot at or past num_blocks * block_size",
+    5: "valid slot repeated",
+    6: "query offsets: cu_seqlens_q[0] != 0, decreasing, or a chunk longer than max_q_len "
+       "or than its context length",
+}
+
+
+class PreconditionError(ValueError):
+    """A device-resident precondition of the attention calls does not hold."""
+
+    def __init__(self, fn: str, kind: int, index: int, what: str):
+        super().__init__(f"{fn}: {PA_CHECK_KINDS.get(kind, f'kind {kind}')} at {what} {index}")
+        self.kind = kind
+        self.index = index
+
+
+def _host_ints(x, dtype, name: str):
+    """A contiguous host numpy copy of an integer tensor or array-like
+    (device tensors are copied synchronously)."""
+    if isinstance(x, torch.Tensor):
+        want = {np.int32: torch.int32, np.int64: torch.int64}[dtype]
+        if x.dtype != want:
+            raise TypeError(f"{name} must be {want}, got {x.dtype}")
+        return np.ascontiguousarray(x.detach().cpu().numpy())
+    a = np.asarray(x)
+    out = np.ascontiguousarray(a.astype(dtype))
+    if a.size and not np.array_equal(out, a):
+        raise ValueError(f"{name} does not fit {np.dtype(dtype).name}")
+    return out
+
+
+def _raise_check(fn: str, r: int, bad, what: str) -> None:
+    if r < 0:
+        raise PagedAttnError(fn, r)
+    if r != PA_CHECK_OK:
+        raise PreconditionError(fn, r, int(bad.value), what)
+
+
+def check_tables(block_tables, context_lens, num_blocks: int, block_size: int,
+                 fused_append: bool = False) -> None:
+    """Check, on host copies, what decode / decode_multi / decode_partials (and
+    append_decode with fused_append=True) assume of their tables and lengths;
+    raise PreconditionError naming the first offending sequence."""
+    t = _host_ints(block_tables, np.int32, "block_tables")
+    lens = _host_ints(context_lens, np.int32, "context_lens")
+    if t.ndim != 2 or lens.ndim != 1 or t.shape[0] != lens.shape[0]:
+        raise ValueError("block_tables must be [B, W] and context_lens [B]")
+    bad = ctypes.c_int64(-1)
+    r = lib().pa_check_tables(t.ctypes.data, lens.ctypes.data, int(t.shape[0]), int(t.shape[1]),
+                              int(block_size), int(num_blocks), int(bool(fused_append)),
+                              ctypes.byref(bad))
+    _raise_check("pa_check_tables", r, bad, "sequence")
+
+
+def check_slots(slot_mapping, num_blocks: int, block_size: int) -> None:
+    """Check, on a host copy, what reshape_and_cache(_fp8) assumes of its slots;
+    raise PreconditionError naming the first offending token."""
+    s = _host_ints(slot_mapping, np.int64, "slot_mapping")
+    if s.ndim != 1:
+        raise ValueError("slot_mapping must be 1-D")
+    bad = ctypes.c_int64(-1)
+    r = lib().pa_check_slots(s.ctypes.data, int(s.shape[0]), int(num_blocks), int(block_size),
+                             ctypes.byref(bad))
+    _raise_check("pa_check_slots", r, bad, "token")
+
+
+def check_prefill(cu_seqlens_q, context_lens, max_q_len: int) -> None:
+    """Check, on host copies, what prefill(_fp8) assumes of its query offsets;
+    raise PreconditionError naming the first offending sequence."""
+    cu = _host_ints(cu_seqlens_q, np.int32, "cu_seqlens_q")
+    lens = _host_ints(context_lens, np.int32, "context_lens")
+    if cu.ndim != 1 or lens.ndim != 1 or cu.shape[0] != lens.shape[0] + 1:
+        raise ValueError("cu_seqlens_q must be [B + 1] and context_lens [B]")
+    bad = ctypes.c_int64(-1)
+    r = lib().pa_check_prefill(cu.ctypes.data, lens.ctypes.data, int(lens.shape[0]),
+                               int(max_q_len), ctypes.byref(bad))
+    _raise_check("pa_check_prefill", r, bad, "sequence")
+
+
 __all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "decode_merge", "prefill",
            "prefill_workspace_size", "prefill_auto_splits", "decode_workspace_size", "plan_splits",
            "auto_splits", "decode_multi", "decode_multi_workspace_size", "reshape_and_cache_fp8",
            "decode_fp8", "append_decode_fp8", "decode_multi_fp8", "prefill_fp8", "BlockManager", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError",
-           "PA_MAX_SPLITS", "PA_MAX_QUERY_TOKENS", "PA_MAX_SEQS", "PA_MAX_HEADS"]
+           "PA_MAX_SPLITS", "PA_MAX_QUERY_TOKENS", "PA_MAX_SEQS", "PA_MAX_HEADS",
+           "check_tables", "check_slots", "check_prefill", "PreconditionError", "PA_CHECK_KINDS"]
 
 
 class BlockManager:

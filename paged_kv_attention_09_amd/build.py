@@ -16,9 +16,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libpagedattn.so")
-# The block manager (pa_block_manager.cpp) is host code; hipcc compiles it as C++.
+# The block manager (pa_block_manager.cpp) and the precondition checks
+# (pa_check.cpp) are host code; hipcc compiles them as C++.
 SOURCES = ["pa_api.hip", "pa_append.hip", "pa_decode.hip", "pa_prefill.hip",
-           "pa_block_manager.cpp", "pa_probe.hip"]
+           "pa_block_manager.cpp", "pa_check.cpp", "pa_probe.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of the generated code (-packed-fp32-ops).

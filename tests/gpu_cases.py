@@ -43,8 +43,14 @@ class DecodeCase:
     """Device tensors for one decode call plus the oracle's answer."""
 
     def __init__(self, inp: W.DecodeInputs, device=DEV, with_oracle=True):
+        import paged_kv_attention_09_amd as pa
         self.inp = inp
         s = inp.spec
+        # the inputs meet the preconditions the calls leave to the caller
+        pa.check_tables(inp.block_tables, inp.context_lens, s.num_blocks, s.block_size,
+                        fused_append=inp.new_k is not None)
+        if inp.new_k is not None:
+            pa.check_slots(inp.slot_mapping, s.num_blocks, s.block_size)
         self.k_cache, self.v_cache = device_pool(inp.pool, device)
         self.q = bf16_tensor(inp.q, device)
         self.tables = torch.from_numpy(inp.block_tables).to(device)
