@@ -346,8 +346,13 @@ class PrefillWorkload:
             self.dS = pa.auto_splits(B, Hkv, Wd, bs, dev)
             self.dws = torch.zeros(max(pa.decode_workspace_size(B, Hq, D, self.dS), 256),
                                    dtype=torch.uint8, device=dev)
+            # the decode's algorithmic bytes plus the fused append of one row per
+            # sequence (bf16 rows read, written as bf16 or as fp8 codes); fp8
+            # pools move one byte per K/V element
             self.decode_bytes = W.algorithmic_decode_bytes(self.dlens, Hq, Hkv, D, bs) + \
-                B * Hkv * D * 2 * 2 * 2
+                B * Hkv * D * 2 * (2 + elem)
+            if kv_fp8:
+                self.decode_bytes -= int(self.dlens.sum()) * Hkv * D * 2
         self.B = B
         # the chunk's K/V must be in the pool before any prefill-only timing
         for r in range(self.R):
@@ -724,11 +729,23 @@ def cpu_baseline(spec, seconds: float):
             if t >= seconds:
                 break
     return {"value": round(per_call * n / t / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"fp64 numpy oracle decode of the full {spec.name} call "
                       f"({spec.num_seqs} seqs, {int(np.sum(inp.context_lens))} tokens), "
                       f"{n} calls in {t:.1f} s, 1 BLAS thread",
             "us_per_call": round(t / n * 1e6, 1)}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _oracle_sequence_worker(job):
