@@ -542,7 +542,7 @@ int prefill_impl(const void *q, const int32_t *cu_seqlens_q, const void *k_cache
   if (e == hipErrorInvalidValue) return PA_ERR_UNSUPPORTED;
   if (e != hipSuccess) return PA_ERR_HIP;
   if (a.num_splits > 1 &&
-      pa::launch_prefill_merge(a, head_dim, num_seqs * max_q_len, s) != hipSuccess)
+      pa::launch_prefill_merge(a, head_dim, s) != hipSuccess)
     return PA_ERR_HIP;
   return PA_OK;
 }

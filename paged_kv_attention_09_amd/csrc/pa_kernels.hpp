@@ -48,8 +48,8 @@ struct PrefillArgs {
   const int32_t *block_tables;
   const int32_t *context_lens;
   uint16_t *out;              // [Tq, Hq, D]
-  uint16_t *o_part;           // bf16 [Tq, Hq, S, D] when the key range is split, else null
-  float *lse_part;            // [Tq, Hq, S]
+  uint16_t *o_part;           // bf16 [B, max_q_len, Hq, S, D] when the key range is split, else null
+  float *lse_part;            // [B, max_q_len, Hq, S]
   float scale_log2;
   int num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, bs_shift;
   int max_q_len;
@@ -69,7 +69,6 @@ hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, int group, int
 hipError_t launch_decode_combine(const DecodeArgs &a, int head_dim, int num_seqs,
                                  hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, int head_dim, int group, hipStream_t stream);
-hipError_t launch_prefill_merge(const PrefillArgs &a, int head_dim, int total_q_bound,
-                                hipStream_t stream);
+hipError_t launch_prefill_merge(const PrefillArgs &a, int head_dim, hipStream_t stream);
 
 }  // namespace pa

@@ -412,7 +412,9 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
         *(uint2 *)(a.out + row * D + 16 * db + 4 * q4) = pk;
       }
     } else {
-      const size_t prow = row * a.num_splits + piece;
+      // workspace rows are [sequence, query index < max_q_len, q head, piece]
+      if (i >= a.max_q_len) continue;
+      const size_t prow = (((size_t)b * a.max_q_len + i) * Hq + h) * a.num_splits + piece;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const f32x4 v = o[db][nb] * inv;
@@ -424,98 +426,88 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-// Merge the key pieces of (query row, q head) rows: row t of sequence b sits
-// at position p = L_b - n_b + (t - cu[b]) and has floor(p / split_len) + 1
-// non-empty pieces.  One wave per row, four rows per workgroup; a row's
-// weights 2^(lse_s - M) go through LDS and all its piece loads are in flight
-// together.
+// Merge the key pieces of (query index, q head) rows.  Grid: y = sequence b,
+// x = blocks of rows j = i * Hq + h of that sequence (i < max_q_len).  A row's
+// pieces sit at workspace row (b * max_q_len + i) * Hq + h, so every load of
+// the row (its first BATCH pieces and their log-sum-exps) is issued at once,
+// together with the sequence's offsets and length, before the number of
+// non-empty pieces is known: pieces past it lie inside the workspace and are
+// dropped by a select.  Query i sits at position p = L_b - n_b + i and has
+// floor(p / split_len) + 1 non-empty pieces.  LPR lanes share a row, each
+// owning 8 columns (one 16-byte load per piece), and every lane weighs the
+// pieces itself, so the merge needs no cross-lane traffic; more than BATCH
+// pieces are folded in batches with a running maximum.
 template <int D>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int rows_bound) {
-  constexpr int PER = D / 64;      // columns per lane
-  constexpr int BATCH = 8;
-  __shared__ float w_l[4][256];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int r = blockIdx.x * 4 + wv;
-  if (r >= rows_bound) return;
-  const int Hq = a.num_q_heads;
-  const int t = r / Hq;
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
+  constexpr int LPR = D / 8;       // lanes per row
+  constexpr int RPB = 256 / LPR;   // rows per workgroup
+  constexpr int BATCH = 8;         // pieces in flight per lane
+  const int sub = threadIdx.x % LPR;
+  const int b = blockIdx.y;
+  const int Hq = a.num_q_heads, S = a.num_splits;
+  const int j = blockIdx.x * RPB + threadIdx.x / LPR;
+  const int i = j / Hq, h = j % Hq;
+  const size_t row = ((size_t)b * a.max_q_len + min(i, a.max_q_len - 1)) * Hq + h;
+  const uint4 *op = (const uint4 *)(a.o_part + row * S * D) + sub;
+  const float *lp = a.lse_part + row * S;
   const auto *cu = as_const(a.cu_seqlens_q);
-  if (t >= cu[a.num_seqs]) return;   // the grid covers num_seqs * max_q_len rows
-  int b = 0;
-  while (b + 1 < a.num_seqs && cu[b + 1] <= t) ++b;
-  const int n = cu[b + 1] - cu[b];
-  const int p = as_const(a.context_lens)[b] - n + (t - cu[b]);
-  const int S = a.num_splits;
-  const int ns = min(S, p / a.split_len + 1);
-  const float *lse = a.lse_part + (size_t)r * S;
-  const uint16_t *op = a.o_part + (size_t)r * S * D + lane * PER;
-  // a piece's PER bf16 values of this lane's columns, widened to fp32
-  auto load_piece = [&](int k, float (&v)[PER]) {
-    if constexpr (PER == 2) {
-      const uint32_t w = *(const uint32_t *)(op + (size_t)k * D);
-      v[0] = bf16_lo(w);
-      v[1] = bf16_hi(w);
-    } else {
-      v[0] = bf16_lo(op[(size_t)k * D]);
-    }
-  };
-
-  float ov[BATCH][PER];
+  const int c0 = cu[b], n = cu[b + 1] - c0;
+  const int L = as_const(a.context_lens)[b];
+  uint4 ov[BATCH];
+  float ls[BATCH];
 #pragma unroll
   for (int k = 0; k < BATCH; ++k) {
-    if (k < ns) {
-      load_piece(k, ov[k]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < PER; ++e) ov[k][e] = 0.f;
-    }
+    ov[k] = k < S ? op[(size_t)k * (D / 8)] : uint4{0u, 0u, 0u, 0u};
+    ls[k] = k < S ? lp[k] : -INFINITY;
   }
-  float x[4], mx = -INFINITY;
+  if (i >= n || i >= a.max_q_len) return;
+  const int ns = min(S, (L - n + i) / a.split_len + 1);
+
+  float M = -INFINITY, den = 0.f, acc[8];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int s = lane + 64 * k;
-    x[k] = s < ns ? lse[s] : -INFINITY;
-    mx = fmaxf(mx, x[k]);
-  }
-  const float M = wave_max(mx);
-  float den = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  // fold pieces s0 .. s0 + BATCH - 1 (those below ns) into (M, den, acc)
+  auto fold = [&](int s0) {
+    float mb = M;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int s = lane + 64 * k;
-    const float wgt = s < ns ? exp2_fast(x[k] - M) : 0.f;
-    w_l[wv][s] = wgt;
-    den += wgt;
-  }
-  den = wave_sum(den);
-  float acc[PER];
+    for (int k = 0; k < BATCH; ++k)
+      if (s0 + k < ns) mb = fmaxf(mb, ls[k]);
+    const float alpha = M == -INFINITY ? 0.f : exp2_fast(M - mb);
+    den *= alpha;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int k = 0; k < BATCH; ++k)
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w_l[wv][k] * ov[k][e];
-  for (int s0 = BATCH; s0 < ns; s0 += BATCH) {
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+    M = mb;
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
       if (s0 + k < ns) {
-        load_piece(s0 + k, ov[k]);
-      } else {
+        const float wk = exp2_fast(ls[k] - mb);
+        den += wk;
+        const uint32_t u[4] = {ov[k].x, ov[k].y, ov[k].z, ov[k].w};
 #pragma unroll
-        for (int e = 0; e < PER; ++e) ov[k][e] = 0.f;
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += wk * bf16_lo(u[e]);
+          acc[2 * e + 1] += wk * bf16_hi(u[e]);
+        }
       }
     }
+  };
+  fold(0);
+  for (int s0 = BATCH; s0 < ns; s0 += BATCH) {
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k)
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += w_l[wv][min(s0 + k, 255)] * ov[k][e];
+    for (int k = 0; k < BATCH; ++k) {
+      const int s = min(s0 + k, S - 1);
+      ov[k] = op[(size_t)s * (D / 8)];
+      ls[k] = lp[s];
+    }
+    fold(s0);
   }
   const float inv = 1.f / den;
-  uint16_t *out = a.out + (size_t)r * D + lane * PER;
-  if constexpr (PER == 2) {
-    *(uint32_t *)out = pack_bf16(acc[0] * inv, acc[1] * inv);
-  } else {
-    out[0] = (uint16_t)pack_bf16(acc[0] * inv, 0.f);
-  }
+  uint4 pk;
+  pk.x = pack_bf16(acc[0] * inv, acc[1] * inv);
+  pk.y = pack_bf16(acc[2] * inv, acc[3] * inv);
+  pk.z = pack_bf16(acc[4] * inv, acc[5] * inv);
+  pk.w = pack_bf16(acc[6] * inv, acc[7] * inv);
+  *((uint4 *)(a.out + ((size_t)(c0 + i) * Hq + h) * D) + sub) = pk;
 }
 
 template <int D, int G>
@@ -551,14 +543,14 @@ hipError_t launch_prefill(const PrefillArgs &a, int head_dim, int group, hipStre
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill_merge(const PrefillArgs &a, int head_dim, int total_q,
-                                hipStream_t stream) {
-  const int rows = total_q * a.num_q_heads;
-  dim3 grid((rows + 3) / 4);
+hipError_t launch_prefill_merge(const PrefillArgs &a, int head_dim, hipStream_t stream) {
+  const int rows = a.max_q_len * a.num_q_heads;   // per sequence
+  const int rpb = 256 / (head_dim / 8);
+  dim3 grid((rows + rpb - 1) / rpb, a.num_seqs);
   if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, dim3(256), 0, stream, a, rows);
+    hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, dim3(256), 0, stream, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_merge_kernel<64>, grid, dim3(256), 0, stream, a, rows);
+    hipLaunchKernelGGL(prefill_merge_kernel<64>, grid, dim3(256), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
