@@ -660,7 +660,8 @@ def ingest_sq(directory: str, kernel: str, out_name: str, command: str, flop_per
     for r in rows:
         durs[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     med["dispatch_ns"] = statistics.median(durs.values())
-    lines = [f"# SQ counters: {out_name}", "", f"Kernel `{kernel}`; per-dispatch medians over "
+    title = "SQ counters" if all(c.startswith(("SQ_", "GRBM_")) for c in per) else "Counters"
+    lines = [f"# {title}: {out_name}", "", f"Kernel `{kernel}`; per-dispatch medians over "
              f"{len(next(iter(per.values())))} dispatches.", "", "Command (run from /tmp with "
              "TMPDIR=/tmp):", "", "```", command, "```", "", "| counter | value |", "|---|---|"]
     lines += [f"| {c}{' (per XCD)' if c.startswith('GRBM_') else ''} | {v:.0f} |"
@@ -682,6 +683,10 @@ def ingest_sq(directory: str, kernel: str, out_name: str, command: str, flop_per
             lines.append(f"| executed / algorithmic | {ex / flop_per_call:.3f} |")
             lines.append(f"| algorithmic rate over the dispatch | "
                          f"{flop_per_call / med['dispatch_ns'] / 1e3:.0f} TFLOP/s |")
+    if "TCC_HIT_sum" in med and "TCC_MISS_sum" in med:
+        h, m = med["TCC_HIT_sum"], med["TCC_MISS_sum"]
+        rec["l2_hit_rate"] = h / max(h + m, 1.0)
+        lines.append(f"| L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS) | {100 * h / max(h + m, 1.0):.1f} % |")
     if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med:
         c, a = med["SQ_LDS_BANK_CONFLICT"], med["SQ_LDS_IDX_ACTIVE"]
         rec["lds_bank_conflict_rate"] = c / max(a - c, 1.0)
