@@ -11,8 +11,9 @@
 //    tile staged in LDS serves all G heads.  Long key ranges are cut into
 //    pieces handled by separate workgroups (the same split-KV scheme as
 //    decode) and merged by log-sum-exp afterwards.
-//  * Key tiles of 64 rows stream into LDS by global_load_lds_dwordx4, three
-//    stages deep (two tiles in flight while one is computed).  K rows are
+//  * Key tiles of 64 rows stream into LDS by global_load_lds_dwordx4, four
+//    stages deep (three tiles in flight while one is computed; three stages
+//    for the one shape whose DMA count would overflow the wait counter).  K rows are
 //    stored with their 16-byte chunks XOR swizzled by row, V rows with their
 //    32-byte column pairs swizzled, so the reads below hit distinct banks.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K fragments (keys x head_dim)
@@ -101,13 +102,14 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   constexpr int NDMA = TILEK / 1024;              // DMA instructions per tensor per tile
   constexpr int RPD = 1024 / RB;                  // rows per DMA instruction
   static_assert(RPD <= 16, "a DMA instruction stays inside one 16-row group");
-  // Three tile buffers: two tiles in flight while one is computed.  The DMAs
-  // of a tile are issued by NI waves (a power of two), NPW instructions each,
-  // so every issuing wave waits on a fixed count.
-  constexpr int NST = 3;
+  // NST tile buffers: NST - 1 tiles in flight while one is computed.  The
+  // DMAs of a tile are issued by NI waves (a power of two), NPW instructions
+  // each, so every issuing wave waits on a fixed count per tile.
   constexpr int NI = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
   constexpr int NPW = 2 * NDMA / NI;
-  static_assert(NPW <= 63, "vmcnt range");
+  // four stages where the DMA count of two tiles fits the vmcnt field
+  constexpr int NST = 2 * NPW <= 63 ? 4 : 3;
+  static_assert((NST - 2) * NPW <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[NST][2][TILEK];  // [stage][K, V]
   // fp8 pools: this tile's V as bf16 (one byte when unused)
   __shared__ __attribute__((aligned(1024))) char vconv[KV8 ? TILEB : 1];
@@ -213,14 +215,15 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   };
 
   const int ntiles = (kend - kbeg + kKeys - 1) / kKeys;
-  int blk_a[4], blk_b[4];
-  tile_blocks(kbeg, blk_a);
-  issue_tile(kbeg, 0, blk_a);
-  if (ntiles > 1) {
-    tile_blocks(kbeg + kKeys, blk_b);
-    issue_tile(kbeg + kKeys, 1, blk_b);
+  int blk[4];
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t) {
+    if (t < ntiles) {
+      tile_blocks(kbeg + t * kKeys, blk);
+      issue_tile(kbeg + t * kKeys, t, blk);
+    }
   }
-  if (ntiles > 2) tile_blocks(kbeg + 2 * kKeys, blk_a);   // for tile 2
+  if (ntiles > NST - 1) tile_blocks(kbeg + (NST - 1) * kKeys, blk);   // for tile NST - 1
 
   float m[2] = {-INFINITY, -INFINITY};
   f32x4 o[DB][2];
@@ -248,18 +251,16 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
     v_off[db] = tr_row * ROWB + v_pos<D>(2 * db + ((c16 & 3) >> 1), tr_row) * 16 + (c16 & 1) * 8;
 
   for (int it = 0; it < ntiles; ++it) {
-    // this wave's DMAs of tile it are done when at most those of tile it+1
-    // are outstanding; the barrier then publishes everyone's tile it and
-    // retires all reads of the stage tile it+2 is about to overwrite.
-    if (it + 1 < ntiles)
-      wait_vmcnt<NPW>();
-    else
-      wait_vmcnt<0>();
+    // this wave's DMAs of tile it are done when at most those of the tiles
+    // issued after it (up to NST - 2) are outstanding; the barrier then
+    // publishes everyone's tile it and retires all reads of the stage that
+    // tile it + NST - 1 is about to overwrite (it held tile it - 1).
+    wait_vmcnt_steps<NPW, NST - 2>(min(NST - 2, ntiles - 1 - it));
     __syncthreads();
     const int kt0 = kbeg + it * kKeys;
-    if (it + 2 < ntiles) {
-      issue_tile(kt0 + 2 * kKeys, (it + 2) % NST, blk_a);
-      if (it + 3 < ntiles) tile_blocks(kt0 + 3 * kKeys, blk_a);   // consumed next iteration
+    if (it + NST - 1 < ntiles) {
+      issue_tile(kt0 + (NST - 1) * kKeys, (it + NST - 1) % NST, blk);
+      if (it + NST < ntiles) tile_blocks(kt0 + NST * kKeys, blk);   // consumed next iteration
     }
     const char *Kt = smem[it % NST][0];
     const char *Vt = KV8 ? vconv : smem[it % NST][1];
