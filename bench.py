@@ -825,7 +825,37 @@ def measure(name, args, steps, warmup, with_kernel=True):
         avg = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
         rec["kernel_avg_us"] = avg * 1e3
         rec["kernel_gbps"] = wl.decode_bytes / (avg * 1e-3) / 1e9
+    if spec.len_range is not None:
+        rec.update(measure_longest_first(wl, steps, warmup))
     return wl, rec
+
+
+def measure_longest_first(wl, steps, warmup):
+    """The same batch launched longest sequence first, in the order the
+    library's block manager gives (pa_bm_order_longest_first): the sequences'
+    rows of q, tables and lengths permuted, the work unchanged."""
+    import numpy as np
+    import torch
+    spec = wl.spec
+    B, bs = spec.num_seqs, spec.block_size
+    need = int(((wl.lens_np.astype(np.int64) + bs - 1) // bs).sum())
+    bm = wl.pa.BlockManager(max(spec.num_blocks, need + 1), bs, spec.max_blocks_per_seq,
+                            prefix_cache=False)
+    for b, L in enumerate(wl.lens_np):
+        bm.admit(b, 0, np.zeros(int(L), np.int32))
+    order = bm.order_longest_first(np.arange(B))
+    del bm
+    perm = torch.from_numpy(order).to(wl.dev)
+    saved = wl.tables, wl.lens
+    wl.tables = [t[perm].contiguous() for t in saved[0]]
+    wl.lens = saved[1][perm].contiguous()
+    ms_step, _ = time_steps_graph(wl, steps, warmup)
+    avg = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
+    wl.tables, wl.lens = saved
+    return {"longest_first_us_per_call": ms_step * 1e3,
+            "longest_first_gbps": (wl.decode_bytes + wl.append_bytes) / (ms_step * 1e-3) / 1e9,
+            "longest_first_kernel_us": avg * 1e3,
+            "longest_first_kernel_gbps": wl.decode_bytes / (avg * 1e-3) / 1e9}
 
 
 def read_probe_gbps(nbytes: int) -> float:
@@ -1089,6 +1119,10 @@ def main(argv=None):
                    f"kernel {rec['kernel_avg_us']:.2f} us ({rec['kernel_gbps']:.0f} GB/s); "
                    f"eager {rec['eager_us_per_step']:.2f} us (graph saves "
                    f"{100 * rec['graph_saving']:.0f}%)")
+            if "longest_first_us_per_call" in rec:
+                msg += (f"; longest first {rec['longest_first_us_per_call']:.2f} us/step, kernel "
+                        f"{rec['longest_first_kernel_us']:.2f} us "
+                        f"({rec['longest_first_kernel_gbps']:.0f} GB/s)")
         others[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rec.items()
                         if k not in ("wall_s",)}
         print(f"[bench] {name}: {msg}", file=sys.stderr, flush=True)

@@ -110,6 +110,17 @@ int pa_bm_preempt(pa_block_manager *bm, int64_t *victim);
 int pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seq_ids, int n_seqs,
                        int32_t *tables_out, int32_t *lens_out);
 
+/* Launch order for a decode batch: writes to order_out the n_seqs ids of
+ * seq_ids sorted by context length, longest first (equal lengths keep their
+ * order in seq_ids).  A decode launch dispatches its workgroups in batch
+ * order; when a batch has more (sequence, kv head) units than the GPU holds
+ * at once, starting the longest sequences first keeps the last workgroups
+ * short (longest-processing-time-first scheduling).  Pass order_out to
+ * pa_bm_block_tables to build the rows in that order.  PA_ERR_STATE for an
+ * unknown id (nothing is written); order_out must not overlap seq_ids. */
+int pa_bm_order_longest_first(const pa_block_manager *bm, const int64_t *seq_ids, int n_seqs,
+                              int64_t *order_out);
+
 /* Pool accounting: blocks never used or released unshared (free), released
  * shareable blocks (cached, reusable until evicted), blocks held by running
  * sequences (used); free + cached + used = num_blocks.  *running receives the

@@ -97,6 +97,7 @@ SIGNATURES = {
     "pa_bm_preempt": (_I, [_VP, _VP]),
     "pa_bm_block_tables": (_I, [_VP, _VP, _I, _VP, _VP]),
     "pa_bm_stats": (_I, [_VP, _VP, _VP, _VP, _VP]),
+    "pa_bm_order_longest_first": (_I, [_VP, _VP, _I, _VP]),
     # host-side precondition checks (end of include/pagedattn.h)
     "pa_check_tables": (_I, [_VP, _VP, _I, _I, _I, _I64, _I, _VP]),
     "pa_check_slots": (_I, [_VP, _I64, _I64, _I, _VP]),
@@ -689,6 +690,17 @@ class BlockManager:
             self._h, ids.ctypes.data_as(ctypes.c_void_p), n,
             tables.ctypes.data_as(ctypes.c_void_p), lens.ctypes.data_as(ctypes.c_void_p)))
         return tables, lens
+
+    def order_longest_first(self, seq_ids):
+        """The ids of seq_ids sorted by context length, longest first (ties keep
+        their order): the launch order that keeps a large decode batch's last
+        workgroups short."""
+        ids = self._np.ascontiguousarray(seq_ids, dtype=self._np.int64)
+        out = self._np.empty(len(ids), dtype=self._np.int64)
+        _check("pa_bm_order_longest_first", lib().pa_bm_order_longest_first(
+            self._h, ids.ctypes.data_as(ctypes.c_void_p), len(ids),
+            out.ctypes.data_as(ctypes.c_void_p)))
+        return out
 
     def stats(self):
         """(free, cached, used) blocks and the number of running sequences."""

@@ -363,6 +363,26 @@ int pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seq_ids, int n
   return PA_OK;
 }
 
+int pa_bm_order_longest_first(const pa_block_manager *bm, const int64_t *seq_ids, int n_seqs,
+                              int64_t *order_out) {
+  if (!bm) return PA_ERR_NULL;
+  if (n_seqs < 0) return PA_ERR_SHAPE;
+  if (n_seqs == 0) return PA_OK;
+  if (!seq_ids || !order_out) return PA_ERR_NULL;
+  std::vector<std::pair<int64_t, int>> keyed((size_t)n_seqs);  // (length, position)
+  for (int i = 0; i < n_seqs; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return PA_ERR_STATE;
+    keyed[(size_t)i] = {it->second.len, i};
+  }
+  std::stable_sort(keyed.begin(), keyed.end(),
+                   [](const std::pair<int64_t, int> &x, const std::pair<int64_t, int> &y) {
+                     return x.first > y.first;
+                   });
+  for (int i = 0; i < n_seqs; ++i) order_out[i] = seq_ids[keyed[(size_t)i].second];
+  return PA_OK;
+}
+
 int pa_bm_stats(const pa_block_manager *bm, int64_t *free_blocks, int64_t *cached_blocks,
                 int64_t *used_blocks, int64_t *running) {
   if (!bm) return PA_ERR_NULL;

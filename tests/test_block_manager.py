@@ -325,6 +325,28 @@ def test_native_equals_model(seed, num_blocks, bs, prefix):
         assert counts["refused"] > 0
 
 
+def test_order_longest_first():
+    """Launch order of a batch: ids sorted by context length, longest first,
+    ties in the given order; an unknown id is refused and writes nothing."""
+    rng = np.random.default_rng(5)
+    bm = pa.BlockManager(512, 16, 16)
+    lens = {}
+    for sid in range(40):
+        n = int(rng.choice([3, 17, 17, 64, 100, 200]))
+        bm.admit(sid, 0, list(range(n)))
+        lens[sid] = n
+    for _ in range(5):
+        pick = [int(x) for x in rng.permutation(40)[:int(rng.integers(1, 41))]]
+        got = bm.order_longest_first(pick).tolist()
+        assert got == sorted(pick, key=lambda i: -lens[i])     # Python's sort is stable
+        t, l = bm.block_tables(got)
+        assert (np.diff(l) <= 0).all()
+    with pytest.raises(pa.PagedAttnError) as e:
+        bm.order_longest_first([1, 99])
+    assert e.value.status == STATE
+    assert bm.order_longest_first([]).tolist() == []
+
+
 def test_native_argument_errors():
     with pytest.raises(ValueError):
         pa.BlockManager(0, 16, 4)
