@@ -830,10 +830,9 @@ def measure(name, args, steps, warmup, with_kernel=True):
     return wl, rec
 
 
-def measure_longest_first(wl, steps, warmup):
-    """The same batch launched longest sequence first, in the order the
-    library's block manager gives (pa_bm_order_longest_first): the sequences'
-    rows of q, tables and lengths permuted, the work unchanged."""
+def longest_first_order(wl):
+    """Device permutation of a workload's sequences, longest first, as the
+    library's block manager gives it (pa_bm_order_longest_first)."""
     import numpy as np
     import torch
     spec = wl.spec
@@ -845,7 +844,14 @@ def measure_longest_first(wl, steps, warmup):
         bm.admit(b, 0, np.zeros(int(L), np.int32))
     order = bm.order_longest_first(np.arange(B))
     del bm
-    perm = torch.from_numpy(order).to(wl.dev)
+    return torch.from_numpy(order).to(wl.dev)
+
+
+def measure_longest_first(wl, steps, warmup):
+    """The same batch launched longest sequence first, in the order the
+    library's block manager gives (pa_bm_order_longest_first): the sequences'
+    rows of tables and lengths permuted, the work unchanged."""
+    perm = longest_first_order(wl)
     saved = wl.tables, wl.lens
     wl.tables = [t[perm].contiguous() for t in saved[0]]
     wl.lens = saved[1][perm].contiguous()
@@ -978,6 +984,13 @@ def measure_fp8(name, args, steps, warmup):
     rec = {"workload": name, "base_workload": base, "kv": "fp8 e4m3, per-tensor scales",
            "us_per_call": ms * 1e3, "gbps": wl.decode_bytes / (ms * 1e-3) / 1e9,
            "decode_bytes": wl.decode_bytes, "splits": wl.S, "rotations": wl.R}
+    if spec.len_range is not None:
+        perm = longest_first_order(wl)
+        wl.tables = [t[perm].contiguous() for t in wl.tables]
+        wl.lens = wl.lens[perm].contiguous()
+        ms_lf = time_graph(wl.step_fp8, wl.R, steps, warmup)
+        rec["longest_first_us_per_call"] = ms_lf * 1e3
+        rec["longest_first_gbps"] = wl.decode_bytes / (ms_lf * 1e-3) / 1e9
     del wl
     torch.cuda.empty_cache()
     one = DecodeWorkload(spec, args.rotate_gib, args.splits)
@@ -1098,6 +1111,8 @@ def main(argv=None):
             wl, rec = measure_fp8(name, args, min(args.steps, 100), min(args.warmup, 10))
             msg = (f"fp8 pools: {rec['us_per_call']:.2f} us/call, {rec['gbps']:.1f} GB/s; bf16 "
                    f"{rec['bf16_us_per_call']:.2f} us (x{rec['speedup_over_bf16']:.2f})")
+            if "longest_first_us_per_call" in rec:
+                msg += f"; longest first {rec['longest_first_us_per_call']:.2f} us"
         elif name in MULTI_WORKLOADS:
             wl, rec = measure_multi(name, args, min(args.steps, 100), min(args.warmup, 10))
             msg = (f"q_len {rec['q_len']}: {rec['us_per_call']:.2f} us/call, {rec['gbps']:.1f} GB/s;"

@@ -256,7 +256,8 @@ def test_nonzero_stream_and_no_host_sync():
     assert_close(to_f64(case.out), case.ref, what="side stream")
 
 
-@pytest.mark.parametrize("name,S", [("c3", 0), ("c3", 1), ("c5d", 0), ("c2b8", 7), ("empty", 4)])
+@pytest.mark.parametrize("name,S", [("c3", 0), ("c3", 1), ("c5d", 0), ("c2b8", 7), ("c2b8", 0),
+                                    ("c2b1", 0), ("empty", 4)])
 def test_fused_append_decode(name, S):
     """append_decode == reshape_and_cache at each sequence's last token followed
     by decode: pools bit-exact against the oracle append, output within
