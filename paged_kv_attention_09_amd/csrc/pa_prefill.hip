@@ -45,6 +45,9 @@ namespace {
 
 constexpr int kQRows = 32;   // query positions per workgroup (two 16-row MFMA blocks)
 constexpr int kKeys = 64;    // keys per LDS tile
+constexpr int KG = kKeys / 16;   // 16-key groups (MFMA key blocks) per tile
+constexpr int KK = kKeys / 32;   // 32-key reduction steps of the P.V product per tile
+constexpr int kTileLds = 128 * 1024;  // LDS for the K/V stages
 constexpr float kSlackP = 8.f;
 
 // v_max3_f32 without the input canonicalisation the compiler adds for fmaxf
@@ -107,9 +110,13 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   // each, so every issuing wave waits on a fixed count per tile.
   constexpr int NI = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
   constexpr int NPW = 2 * NDMA / NI;
-  // four stages where the DMA count of two tiles fits the vmcnt field
-  constexpr int NST = 2 * NPW <= 63 ? 4 : 3;
-  static_assert((NST - 2) * NPW <= 63, "vmcnt range");
+  // as many stages (up to four) as kTileLds holds, fewer where the DMA
+  // count of the tiles in flight behind the one waited for would overflow
+  // the vmcnt field
+  constexpr int STL = (kTileLds - (KV8 ? TILEB : 0)) / (2 * TILEK);
+  constexpr int NSTL = STL < 4 ? STL : 4;
+  constexpr int NST = (NSTL - 2) * NPW <= 63 ? NSTL : 3;
+  static_assert(NST >= 2 && (NST - 2) * NPW <= 63, "stages and vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[NST][2][TILEK];  // [stage][K, V]
   // fp8 pools: this tile's V as bf16 (one byte when unused)
   __shared__ __attribute__((aligned(1024))) char vconv[KV8 ? TILEB : 1];
@@ -157,9 +164,9 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   // block for block_size 256), clamped into the table.  Loaded one tile ahead
   // of their use so the scalar-load latency hides behind a tile of compute.
   const int Wm1 = a.max_blocks_per_seq - 1;
-  auto tile_blocks = [&](int kt0, int (&blk)[4]) {
+  auto tile_blocks = [&](int kt0, int (&blk)[KG]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) blk[q] = table[min((kt0 + 16 * q) >> bs_shift, Wm1)];
+    for (int q = 0; q < KG; ++q) blk[q] = table[min((kt0 + 16 * q) >> bs_shift, Wm1)];
   };
 
   // Tile DMA: the 2 * NDMA instructions of a tile are issued by NI waves,
@@ -181,11 +188,11 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
                       : (is_v ? v_pos<D>(p, row_in) : k_pos<D>(p, row_in));
     dma_voff[jw] = (uint32_t)(row_in & 15) * RS + (uint32_t)c * 16;
   }
-  auto issue_tile = [&](int kt0, int buf, const int (&blk)[4]) {
+  auto issue_tile = [&](int kt0, int buf, const int (&blk)[KG]) {
     if (w >= NI) return;
-    const char *gk[4], *gv[4];
+    const char *gk[KG], *gv[KG];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < KG; ++q) {
       const int kg = kt0 + 16 * q;
       const size_t rows = ((size_t)(uint32_t)blk[q] << bs_shift) * (KV8 ? Hkv : 1);
       const size_t off = (rows + (size_t)(kg & bs_mask)) * RS;
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   };
 
   const int ntiles = (kend - kbeg + kKeys - 1) / kKeys;
-  int blk[4];
+  int blk[KG];
 #pragma unroll
   for (int t = 0; t < NST - 1; ++t) {
     if (t < ntiles) {
@@ -277,8 +284,8 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // ---- S^T = K Q^T: 4 key blocks x 2 row blocks, 8 independent chains ----
-    f32x4 s[4][2];
+    // ---- S^T = K Q^T: KG key blocks x 2 row blocks, 2 KG independent chains ----
+    f32x4 s[KG][2];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     auto kfrag = [&](int ks, int mb) __attribute__((always_inline)) {
       const char *p = Kt + k_off[ks] + mb * 16 * RB;
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
         return *(const uint4 *)p;
     };
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < KG; ++mb) {
       const uint4 kf = kfrag(0, mb);
       s[mb][0] = mfma_k32(kf, qf[0][0], zero4);
       s[mb][1] = mfma_k32(kf, qf[1][0], zero4);
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int ks = 1; ks < KS; ++ks) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < KG; ++mb) {
         const uint4 kf = kfrag(ks, mb);
         s[mb][0] = mfma_k32(kf, qf[0][ks], s[mb][0]);
         s[mb][1] = mfma_k32(kf, qf[1][ks], s[mb][1]);
@@ -317,11 +324,14 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
         float t = max3(s[0][nb][0], s[0][nb][1], s[0][nb][2]);
         t = max3(t, s[0][nb][3], s[1][nb][0]);
         t = max3(t, s[1][nb][1], s[1][nb][2]);
-        t = max3(t, s[1][nb][3], s[2][nb][0]);
-        t = max3(t, s[2][nb][1], s[2][nb][2]);
-        t = max3(t, s[2][nb][3], s[3][nb][0]);
-        t = max3(t, s[3][nb][1], s[3][nb][2]);
-        t = max3(t, s[3][nb][3], t);
+        t = max3(t, s[1][nb][3], t);
+#pragma unroll
+        for (int mb = 2; mb < KG; mb += 2) {
+          t = max3(t, s[mb][nb][0], s[mb][nb][1]);
+          t = max3(t, s[mb][nb][2], s[mb][nb][3]);
+          t = max3(t, s[mb + 1][nb][0], s[mb + 1][nb][1]);
+          t = max3(t, s[mb + 1][nb][2], s[mb + 1][nb][3]);
+        }
         mxs[nb] = t * a.scale_log2;
       }
     } else {
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
         const int prow = pos0 + nb * 16 + c16;
         float t = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < KG; ++mb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int key = kt0 + mb * 16 + q4 * 4 + e;
@@ -357,13 +367,13 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
     }
     // P^T fragments (B operand of O^T = V^T P^T), one per (row block, 32-key
     // step): lane holds keys 16 (2 kk) + 4 q4 + e and 16 (2 kk + 1) + 4 q4 + e.
-    uint4 pf[2][2];
+    uint4 pf[2][KK];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const float mm = m[nb] == -INFINITY ? 0.f : m[nb];
       const float c = plain ? a.scale_log2 : 1.f;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < KK; ++kk) {
         uint32_t pk[4];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -379,7 +389,7 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
     if constexpr (KV8) __syncthreads();
     // ---- O^T += V^T P^T, and the row sums l += ones P^T on the same unit ----
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const char *vp = Vt + v_off[db] + kk * 32 * ROWB;
