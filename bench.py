@@ -687,6 +687,16 @@ def ingest_sq(directory: str, kernel: str, out_name: str, command: str, flop_per
         h, m = med["TCC_HIT_sum"], med["TCC_MISS_sum"]
         rec["l2_hit_rate"] = h / max(h + m, 1.0)
         lines.append(f"| L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS) | {100 * h / max(h + m, 1.0):.1f} % |")
+    if "TCC_EA0_RDREQ_LEVEL_sum" in med and "TCC_EA0_RDREQ_sum" in med:
+        # Little's law over the L2 -> memory read queue: the per-cycle sum of
+        # outstanding reads over the requests gives their mean latency
+        lat = med["TCC_EA0_RDREQ_LEVEL_sum"] / max(med["TCC_EA0_RDREQ_sum"], 1.0)
+        rec["l2_read_latency_cycles"] = lat
+        lines.append(f"| mean L2 -> memory read latency = RDREQ_LEVEL / RDREQ | {lat:.0f} cycles |")
+        if "GRBM_GUI_ACTIVE" in med:
+            inflight = med["TCC_EA0_RDREQ_LEVEL_sum"] / max(med["GRBM_GUI_ACTIVE"], 1.0)
+            rec["l2_reads_in_flight"] = inflight
+            lines.append(f"| mean L2 -> memory reads in flight, all L2 channels | {inflight:.0f} |")
     if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med:
         c, a = med["SQ_LDS_BANK_CONFLICT"], med["SQ_LDS_IDX_ACTIVE"]
         rec["lds_bank_conflict_rate"] = c / max(a - c, 1.0)
