@@ -43,9 +43,10 @@ class PrefillCase:
         return oracle.prefill(self.inp.q, self.inp.cu_seqlens_q, kc, vc, ct,
                               self.inp.context_lens, self.inp.scale)
 
-    def run(self, S=0):
+    def run(self, S=0, max_q=None):
         pa.prefill(self.q, self.cu, self.k_cache, self.v_cache, self.tables, self.lens,
-                   float(self.inp.scale), self.out, self.max_q, num_splits=S)
+                   float(self.inp.scale), self.out, self.max_q if max_q is None else max_q,
+                   num_splits=S)
         torch.cuda.synchronize()
         return to_f64(self.out)
 
@@ -78,6 +79,27 @@ def test_prefill_shapes(D, G, bs, chunks, totals):
     case = PrefillCase(spec)
     for S in (1, 2, 0):
         assert_close(case.run(S), case.ref, what=f"D{D} G{G} bs{bs} S{S}")
+
+
+def test_many_ragged_sequences():
+    """40 sequences in one call: chunks of 0..100 tokens (empty chunks and
+    empty sequences included) over prefixes of 0..500 tokens, bs 16, a
+    max_q_len above every chunk, several split counts: every row of every
+    sequence reaches the oracle, through one merge grid row per sequence."""
+    rng = np.random.default_rng(40)
+    chunks = [int(x) for x in rng.choice([0, 1, 5, 31, 32, 33, 64, 100], size=40)]
+    totals = [c + int(rng.integers(0, 501)) * (i % 3 != 0) for i, c in enumerate(chunks)]
+    chunks[7], totals[7] = 0, 0                        # an empty sequence
+    bs = 16
+    W_ = -(-max(totals) // bs)
+    nb = sum(-(-t // bs) for t in totals) + 5
+    spec = W.PrefillSpec("many", 12, 4, 128, bs, nb, W_, chunk_lens=tuple(chunks),
+                         total_lens=tuple(totals), seed=41)
+    case = PrefillCase(spec)
+    pa.check_prefill(case.inp.cu_seqlens_q, case.inp.context_lens, max(chunks) + 7)
+    pa.check_tables(case.inp.block_tables, case.inp.context_lens, nb, bs)
+    for S in (1, 3, 0, 16):
+        assert_close(case.run(S, max_q=max(chunks) + 7), case.ref, what=f"many S={S}")
 
 
 def test_one_token_chunk_equals_decode():
