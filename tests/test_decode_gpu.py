@@ -91,14 +91,27 @@ def test_split_sweep(name):
                                     (128, 2, 16), (128, 5, 16), (128, 8, 256)])
 def test_shape_matrix(D, G, bs):
     """Every supported head_dim and group size, both block sizes, ragged lengths.
-    Small split counts give a grid of at most one workgroup per compute unit
-    (the 4-deep DMA pipeline); 64 pieces of 64 tokens give 640 workgroups
-    (the 2-deep pipeline, two workgroups per compute unit)."""
+    Small split counts give a grid of at most one workgroup per compute unit;
+    64 pieces of 64 tokens give 640 workgroups, two per compute unit at a
+    time."""
     spec = W.DecodeSpec(f"m{D}_{G}_{bs}", 5, 2 * G, 2, D, bs, 200, 4096 // bs,
                         context_lens=(1, 15, 16, 17, 700 if bs == 16 else 2049), seed=D + G + bs)
     case = DecodeCase(W.make_decode_inputs(spec))
     for S in (1, 5, 64, 0):
         assert_close(_run(case, S), case.ref, what=f"D{D} G{G} bs{bs} S{S}")
+
+
+@pytest.mark.parametrize("G", [2, 7])
+@pytest.mark.parametrize("scale", [0.0, -0.0883883461356163, 0.5])
+def test_scale_sign_and_size(G, scale):
+    """A zero scale (uniform weights), a negative one (the scores' order
+    reversed) and a large one (sharp weights), on the vector (group 2) and the
+    matrix (group 7) path, one piece and several."""
+    spec = W.DecodeSpec(f"scale{G}", 4, 2 * G, 2, 128, 16, 400, 256,
+                        context_lens=(1, 33, 700, 4096), scale=scale, seed=61 + G)
+    case = DecodeCase(W.make_decode_inputs(spec))
+    for S in (1, 16):
+        assert_close(_run(case, S), case.ref, what=f"G{G} scale {scale} S{S}")
 
 
 def test_empty_sequences_give_zeros():

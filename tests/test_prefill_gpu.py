@@ -102,6 +102,17 @@ def test_many_ragged_sequences():
         assert_close(case.run(S, max_q=max(chunks) + 7), case.ref, what=f"many S={S}")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.0883883461356163])
+def test_prefill_scale_sign(scale):
+    """Zero and negative scales take the explicitly scaled (non-folded)
+    softmax path on every tile."""
+    spec = W.PrefillSpec("pscale", 14, 2, 128, 16, 60, 48, chunk_lens=(70, 3),
+                         total_lens=(700, 40), scale=scale, seed=71)
+    case = PrefillCase(spec)
+    for S in (1, 3):
+        assert_close(case.run(S), case.ref, what=f"prefill scale {scale} S{S}")
+
+
 def test_one_token_chunk_equals_decode():
     """A chunk of one query is a decode step."""
     spec = W.PrefillSpec("one", 28, 4, 128, 256, 40, 16, chunk_lens=(1, 1, 1),
