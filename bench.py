@@ -751,6 +751,59 @@ def cpu_baseline(spec, seconds: float):
             "us_per_call": round(t / n * 1e6, 1)}
 
 
+def parity_record(spec):
+    """The benchmarked call (fused append + decode at the automatic split
+    count) on host-drawn inputs of the same workload, against the oracle:
+    error statistics for the JSON line.  Part of the oracle leg."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import paged_kv_attention_09_amd as pa
+    import workloads as W
+
+    s = spec.with_(append=True)
+    inp = W.make_decode_inputs(s)
+    dev = torch.device("cuda:0")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+
+    shape = (s.num_blocks,) + inp.pool.k.shape[1:]
+    kc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = torch.full_like(kc, float("nan"))
+    ids = torch.from_numpy(inp.pool.ids).to(dev)
+    kc.index_copy_(0, ids, bf16(inp.pool.k))
+    vc.index_copy_(0, ids, bf16(inp.pool.v))
+    B, Hkv, D, bs = s.num_seqs, s.num_kv_heads, s.head_dim, s.block_size
+    sel = np.nonzero(inp.context_lens > 0)[0]
+    nk = np.zeros((B, Hkv, D), np.uint16)
+    nv = np.zeros_like(nk)
+    nk[sel], nv[sel] = inp.new_k, inp.new_v
+    q = bf16(inp.q)
+    out = torch.empty_like(q)
+    tables = torch.from_numpy(inp.block_tables).to(dev)
+    lens = torch.from_numpy(inp.context_lens).to(dev)
+    S = pa.auto_splits(B, Hkv, s.max_blocks_per_seq, bs, dev)
+    pa.append_decode(q, bf16(nk), bf16(nv), kc, vc, tables, lens, float(inp.scale), S, out)
+    torch.cuda.synchronize()
+    lut = {int(x): i for i, x in enumerate(inp.pool.ids)}
+    slots = np.array([lut[int(t) // bs] * bs + int(t) % bs for t in inp.slot_mapping], np.int64)
+    k2, v2 = oracle.append(inp.new_k, inp.new_v, slots, inp.pool.k, inp.pool.v)
+    ct = inp.pool.compact_tables(inp.block_tables, inp.poison_block)
+    ref = oracle.decode(inp.q, k2, v2, ct, inp.context_lens, inp.scale)
+    got = oracle.bf16_bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    err = np.abs(got - ref)
+    ratio = err / (1e-2 + 1e-2 * np.abs(ref))
+    return {"call": "pa_append_decode", "splits": S, "outputs": int(ref.size),
+            "max_abs_err": float(err.max()), "rms_err": float(np.sqrt((err ** 2).mean())),
+            "max_err_over_tolerance": float(ratio.max()), "tolerance": "1e-2 + 1e-2 |oracle|",
+            "within_tolerance": bool(np.isfinite(got).all() and (ratio <= 1.0).all()),
+            "inputs": "the workload drawn on the host (workloads module), K/V bf16 N(0,1), "
+                      "unreferenced pool NaN-poisoned; fp64 oracle"}
+
+
 def cpu_model() -> str:
     """The host CPU's model name, from /proc/cpuinfo."""
     try:
@@ -1209,6 +1262,12 @@ def main(argv=None):
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
         line["cpu_baseline"]["parallel"] = cpu_baseline_parallel(spec, args.cpu_seconds / 2)
+        # the same oracle leg checks the benchmarked call's results on host-drawn inputs
+        par = parity_record(spec)
+        line["cpu_baseline"]["parity_of_benchmarked_call"] = par
+        print(f"[bench] parity against the oracle: max abs err {par['max_abs_err']:.2e}, "
+              f"rms {par['rms_err']:.2e}, within tolerance: {par['within_tolerance']}",
+              file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
 
 
