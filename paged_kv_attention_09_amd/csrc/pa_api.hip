@@ -251,24 +251,71 @@ int launch_split_and_merge(const pa::DecodeArgs &a, int head_dim, int group, int
 
 }  // namespace
 
-int pa_decode(const void *q, const void *k_cache, const void *v_cache,
-              const int32_t *block_tables, const int32_t *context_lens, float scale,
-              int num_splits, void *out, int num_seqs, int num_q_heads, int num_kv_heads,
-              int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
-              void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+// What distinguishes the decode entry points: query tokens per sequence, fp8
+// pools with their scales, and the fused append of each sequence's new row.
+struct DecodeVariant {
+  int q_len = 1;
+  bool fp8 = false;
+  float k_scale = 1.0f, v_scale = 1.0f;
+  bool append = false;
+  const void *new_k = nullptr, *new_v = nullptr;
+};
+
+// The decode entry points' shared body: argument checks in a fixed order
+// (query tokens, fp8 scales, shapes, rows per workgroup, pointers, the fp8
+// score scale), then the split pass and, with more than one piece, the merge.
+int decode_entry(const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *block_tables, const int32_t *context_lens, float scale,
+                 int num_splits, void *out, int num_seqs, int num_q_heads, int num_kv_heads,
+                 int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                 void *workspace, size_t workspace_bytes, void *stream, const DecodeVariant &v) {
+  if (v.q_len < 1 || v.q_len > PA_MAX_QUERY_TOKENS) return PA_ERR_SHAPE;
+  if (v.fp8 && !(valid_kv_scale(v.k_scale) && valid_kv_scale(v.v_scale))) return PA_ERR_SHAPE;
   pa::DecodeArgs a;
   int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
                           num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                           max_blocks_per_seq, &a);
-  if (st != PA_OK || num_seqs == 0) return st;
-  if (!out) return PA_ERR_NULL;
+  if (st != PA_OK) return st;
+  if ((num_q_heads / num_kv_heads) * v.q_len > pa::kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || (v.append && (!v.new_k || !v.new_v))) return PA_ERR_NULL;
+  if (v.fp8) {
+    // scores are q . (code k_scale) scale: k_scale joins the score scale
+    a.scale_log2 = (scale * v.k_scale) * 1.4426950408889634f;
+    if (!std::isfinite(a.scale_log2)) return PA_ERR_SHAPE;
+    a.kv_fp8 = 1;
+    a.v_scale = v.v_scale;
+    if (v.append) {
+      a.inv_k_scale = 1.0f / v.k_scale;
+      a.inv_v_scale = 1.0f / v.v_scale;
+    }
+  }
+  a.q_len = v.q_len;
   a.out = (uint16_t *)out;
+  if (v.append) {
+    a.new_k = (const uint16_t *)v.new_k;
+    a.new_v = (const uint16_t *)v.new_v;
+  }
   if (a.num_splits > 1) {
     st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
     if (st != PA_OK) return st;
   }
   return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
                                 (hipStream_t)stream);
+}
+
+}  // namespace
+
+int pa_decode(const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, const int32_t *context_lens, float scale,
+              int num_splits, void *out, int num_seqs, int num_q_heads, int num_kv_heads,
+              int head_dim, int block_size, int64_t num_blocks, int max_blocks_per_seq,
+              void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_entry(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
+                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, workspace, workspace_bytes, stream, DecodeVariant{});
 }
 
 int pa_append_decode(const void *q, const void *new_k, const void *new_v, void *k_cache,
@@ -277,21 +324,13 @@ int pa_append_decode(const void *q, const void *new_k, const void *new_v, void *
                      int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                      int max_blocks_per_seq, void *workspace, size_t workspace_bytes,
                      void *stream) {
-  pa::DecodeArgs a;
-  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
-                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                          max_blocks_per_seq, &a);
-  if (st != PA_OK || num_seqs == 0) return st;
-  if (!out || !new_k || !new_v) return PA_ERR_NULL;
-  a.out = (uint16_t *)out;
-  a.new_k = (const uint16_t *)new_k;
-  a.new_v = (const uint16_t *)new_v;
-  if (a.num_splits > 1) {
-    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
-    if (st != PA_OK) return st;
-  }
-  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
-                                (hipStream_t)stream);
+  DecodeVariant v;
+  v.append = true;
+  v.new_k = new_k;
+  v.new_v = new_v;
+  return decode_entry(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
+                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, workspace, workspace_bytes, stream, v);
 }
 
 int pa_decode_multi(const void *q, const void *k_cache, const void *v_cache,
@@ -300,23 +339,11 @@ int pa_decode_multi(const void *q, const void *k_cache, const void *v_cache,
                     int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                     int max_blocks_per_seq, void *workspace, size_t workspace_bytes,
                     void *stream) {
-  if (q_len < 1 || q_len > PA_MAX_QUERY_TOKENS) return PA_ERR_SHAPE;
-  pa::DecodeArgs a;
-  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
-                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                          max_blocks_per_seq, &a);
-  if (st != PA_OK) return st;
-  if ((num_q_heads / num_kv_heads) * q_len > pa::kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
-  if (!out) return PA_ERR_NULL;
-  a.q_len = q_len;
-  a.out = (uint16_t *)out;
-  if (a.num_splits > 1) {
-    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
-    if (st != PA_OK) return st;
-  }
-  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
-                                (hipStream_t)stream);
+  DecodeVariant v;
+  v.q_len = q_len;
+  return decode_entry(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
+                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, workspace, workspace_bytes, stream, v);
 }
 
 int pa_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
@@ -325,25 +352,13 @@ int pa_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
                   int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                   int64_t num_blocks, int max_blocks_per_seq, void *workspace,
                   size_t workspace_bytes, void *stream) {
-  if (!(valid_kv_scale(k_scale) && valid_kv_scale(v_scale))) return PA_ERR_SHAPE;
-  pa::DecodeArgs a;
-  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
-                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                          max_blocks_per_seq, &a);
-  if (st != PA_OK || num_seqs == 0) return st;
-  if (!out) return PA_ERR_NULL;
-  // scores are q . (code k_scale) scale: k_scale joins the score scale
-  a.scale_log2 = (scale * k_scale) * 1.4426950408889634f;
-  if (!std::isfinite(a.scale_log2)) return PA_ERR_SHAPE;
-  a.kv_fp8 = 1;
-  a.v_scale = v_scale;
-  a.out = (uint16_t *)out;
-  if (a.num_splits > 1) {
-    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
-    if (st != PA_OK) return st;
-  }
-  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
-                                (hipStream_t)stream);
+  DecodeVariant v;
+  v.fp8 = true;
+  v.k_scale = k_scale;
+  v.v_scale = v_scale;
+  return decode_entry(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
+                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, workspace, workspace_bytes, stream, v);
 }
 
 int pa_append_decode_fp8(const void *q, const void *new_k, const void *new_v, void *k_cache,
@@ -352,28 +367,16 @@ int pa_append_decode_fp8(const void *q, const void *new_k, const void *new_v, vo
                          int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                          int block_size, int64_t num_blocks, int max_blocks_per_seq,
                          void *workspace, size_t workspace_bytes, void *stream) {
-  if (!(valid_kv_scale(k_scale) && valid_kv_scale(v_scale))) return PA_ERR_SHAPE;
-  pa::DecodeArgs a;
-  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
-                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                          max_blocks_per_seq, &a);
-  if (st != PA_OK || num_seqs == 0) return st;
-  if (!out || !new_k || !new_v) return PA_ERR_NULL;
-  a.scale_log2 = (scale * k_scale) * 1.4426950408889634f;
-  if (!std::isfinite(a.scale_log2)) return PA_ERR_SHAPE;
-  a.kv_fp8 = 1;
-  a.v_scale = v_scale;
-  a.inv_k_scale = 1.0f / k_scale;
-  a.inv_v_scale = 1.0f / v_scale;
-  a.out = (uint16_t *)out;
-  a.new_k = (const uint16_t *)new_k;
-  a.new_v = (const uint16_t *)new_v;
-  if (a.num_splits > 1) {
-    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
-    if (st != PA_OK) return st;
-  }
-  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
-                                (hipStream_t)stream);
+  DecodeVariant v;
+  v.fp8 = true;
+  v.k_scale = k_scale;
+  v.v_scale = v_scale;
+  v.append = true;
+  v.new_k = new_k;
+  v.new_v = new_v;
+  return decode_entry(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
+                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, workspace, workspace_bytes, stream, v);
 }
 
 int pa_decode_multi_fp8(const void *q, const void *k_cache, const void *v_cache,
@@ -382,28 +385,14 @@ int pa_decode_multi_fp8(const void *q, const void *k_cache, const void *v_cache,
                         int q_len, int num_q_heads, int num_kv_heads, int head_dim,
                         int block_size, int64_t num_blocks, int max_blocks_per_seq,
                         void *workspace, size_t workspace_bytes, void *stream) {
-  if (q_len < 1 || q_len > PA_MAX_QUERY_TOKENS) return PA_ERR_SHAPE;
-  if (!(valid_kv_scale(k_scale) && valid_kv_scale(v_scale))) return PA_ERR_SHAPE;
-  pa::DecodeArgs a;
-  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
-                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                          max_blocks_per_seq, &a);
-  if (st != PA_OK) return st;
-  if ((num_q_heads / num_kv_heads) * q_len > pa::kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
-  if (!out) return PA_ERR_NULL;
-  a.scale_log2 = (scale * k_scale) * 1.4426950408889634f;
-  if (!std::isfinite(a.scale_log2)) return PA_ERR_SHAPE;
-  a.kv_fp8 = 1;
-  a.v_scale = v_scale;
-  a.q_len = q_len;
-  a.out = (uint16_t *)out;
-  if (a.num_splits > 1) {
-    st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
-    if (st != PA_OK) return st;
-  }
-  return launch_split_and_merge(a, head_dim, num_q_heads / num_kv_heads, num_seqs,
-                                (hipStream_t)stream);
+  DecodeVariant v;
+  v.q_len = q_len;
+  v.fp8 = true;
+  v.k_scale = k_scale;
+  v.v_scale = v_scale;
+  return decode_entry(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
+                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, workspace, workspace_bytes, stream, v);
 }
 
 int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
