@@ -422,7 +422,9 @@ def measure_prefill(args, steps, warmup, with_decode: bool, kv_fp8: bool = False
     wl = PrefillWorkload(W.PREFILL_CONFIGS["c5p"], W.CONFIGS["c5d"] if with_decode else None,
                          args.rotate_gib, kv_fp8=kv_fp8)
     ms_pf = time_graph(wl.prefill, wl.R, steps, warmup)
-    rec = {"prefill_us": ms_pf * 1e3, "prefill_tflops": wl.flop / (ms_pf * 1e-3) / 1e12,
+    name = W.PREFILL_CONFIGS["c5p"].name + (" with " + W.CONFIGS["c5d"].name if with_decode else "")
+    rec = {"workload": name + (", fp8 pools" if kv_fp8 else ""),
+           "prefill_us": ms_pf * 1e3, "prefill_tflops": wl.flop / (ms_pf * 1e-3) / 1e12,
            "prefill_splits": wl.S, "prefill_gflop": wl.flop / 1e9, "query_rows": wl.Tq,
            "rotations": wl.R}
     if with_decode:
@@ -873,7 +875,7 @@ def measure(name, args, steps, warmup, with_kernel=True):
     wl = DecodeWorkload(spec, args.rotate_gib, args.splits)
     ms_step, wall = time_steps_graph(wl, steps, warmup)
     bytes_step = wl.decode_bytes + wl.append_bytes
-    rec = {"workload": name, "ms_per_step": ms_step, "wall_s": wall,
+    rec = {"workload": spec.name, "key": name, "ms_per_step": ms_step, "wall_s": wall,
            "gbps": bytes_step / (ms_step * 1e-3) / 1e9,
            "us_per_call": ms_step * 1e3, "splits": wl.S, "rotations": wl.R,
            "decode_bytes": wl.decode_bytes, "append_bytes": wl.append_bytes,
@@ -1019,7 +1021,9 @@ def measure_multi(name, args, steps, warmup):
     spec = W.CONFIGS[base]
     wl = DecodeWorkload(spec, args.rotate_gib, args.splits, q_len=q_len, kv_fp8=fp8)
     ms = time_graph(wl.step_multi_fp8 if fp8 else wl.step_multi, wl.R, steps, warmup)
-    rec = {"workload": name, "base_workload": base, "q_len": q_len,
+    rec = {"workload": f"{spec.name}, {q_len} query tokens" + (", fp8 pools" if fp8 else ""),
+           "key": name, "base_workload": base,
+           "q_len": q_len,
            "kv": "fp8 e4m3, per-tensor scales" if fp8 else "bf16",
            "us_per_call": ms * 1e3, "gbps": wl.decode_bytes / (ms * 1e-3) / 1e9,
            "decode_bytes": wl.decode_bytes, "splits": wl.S, "rotations": wl.R}
@@ -1044,7 +1048,8 @@ def measure_fp8(name, args, steps, warmup):
     spec = W.CONFIGS[base]
     wl = DecodeWorkload(spec, args.rotate_gib, args.splits, kv_fp8=True)
     ms = time_graph(wl.step_fp8, wl.R, steps, warmup)
-    rec = {"workload": name, "base_workload": base, "kv": "fp8 e4m3, per-tensor scales",
+    rec = {"workload": f"{spec.name}, fp8 pools", "key": name, "base_workload": base,
+           "kv": "fp8 e4m3, per-tensor scales",
            "us_per_call": ms * 1e3, "gbps": wl.decode_bytes / (ms * 1e-3) / 1e9,
            "decode_bytes": wl.decode_bytes, "splits": wl.S, "rotations": wl.R}
     if spec.len_range is not None:
