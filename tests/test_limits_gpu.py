@@ -5,6 +5,7 @@
   fused append + decode, over ragged lengths that include empty sequences.
 * PA_MAX_HEADS q heads: group 8 (matrix path), group 1 (vector path) and the
   multi-token decode, whose merge grid spans q_len * PA_MAX_HEADS rows.
+* Both limits over fp8 pools too.
 
 Tolerance as for every attention output here: |gpu - oracle| <= 1e-2 +
 1e-2 |oracle| elementwise, and the append bit-exact over the whole pools.
@@ -19,6 +20,7 @@ import paged_kv_attention_09_amd as pa
 import workloads as W
 from gpu_cases import DEV, DecodeCase, assert_close, bf16_tensor, to_bits, to_f64
 from test_decode_multi_gpu import MultiCase
+from test_kv_fp8_gpu import _oracle_fp8, _run_fp8
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +106,36 @@ def test_max_heads_multi_token_decode():
         case.run(S)
         torch.cuda.synchronize()
         assert_close(to_f64(case.out), case.ref, what=f"multi Hq={case.Hq} S={S}")
+
+
+@pytest.fixture(scope="module")
+def max_seq_fp8():
+    inp = W.make_decode_inputs(_max_seq_spec(), fill="zeros")
+    k8, v8 = W.fp8_codes_like(inp)
+    return inp, k8, v8, _oracle_fp8(inp, k8, v8, 0.3, 0.7)
+
+
+@pytest.mark.parametrize("S", [1, 2])
+def test_max_num_seqs_decode_fp8(max_seq_fp8, S):
+    """PA_MAX_SEQS sequences over fp8 pools (head-major codes, per-pool scales)."""
+    inp, k8, v8, ref = max_seq_fp8
+    print(f"decode_fp8 B={inp.spec.num_seqs} S={S}", flush=True)
+    got = to_f64(_run_fp8(inp, k8, v8, 0.3, 0.7, S))
+    assert_close(got, ref, what=f"fp8 B={inp.spec.num_seqs} S={S}")
+
+
+def test_max_heads_decode_fp8():
+    """PA_MAX_HEADS q heads at group 8 over fp8 pools, S = 1, 2 and automatic."""
+    lens = (1, 40, 100)
+    nb = sum(-(-L // 16) for L in lens) + 4
+    spec = W.DecodeSpec("max-heads-fp8", len(lens), pa.PA_MAX_HEADS, 512, 64, 16, nb, 8,
+                        context_lens=lens, seed=9400)
+    inp = W.make_decode_inputs(spec, fill="zeros")
+    k8, v8 = W.fp8_codes_like(inp)
+    ref = _oracle_fp8(inp, k8, v8, 0.5, 0.25)
+    for S in (1, 2, 0):
+        print(f"decode_fp8 Hq={spec.num_q_heads} S={S}", flush=True)
+        assert_close(to_f64(_run_fp8(inp, k8, v8, 0.5, 0.25, S)), ref, what=f"fp8 heads S={S}")
 
 
 def test_one_past_each_limit_is_refused(max_seq_case):
