@@ -5,7 +5,7 @@
   fused append + decode, over ragged lengths that include empty sequences.
 * PA_MAX_HEADS q heads: group 8 (matrix path), group 1 (vector path) and the
   multi-token decode, whose merge grid spans q_len * PA_MAX_HEADS rows.
-* Both limits over fp8 pools too.
+* Both limits over fp8 pools too, and PA_MAX_SEQS prompt chunks in one prefill.
 
 Tolerance as for every attention output here: |gpu - oracle| <= 1e-2 +
 1e-2 |oracle| elementwise, and the append bit-exact over the whole pools.
@@ -136,6 +136,58 @@ def test_max_heads_decode_fp8():
     for S in (1, 2, 0):
         print(f"decode_fp8 Hq={spec.num_q_heads} S={S}", flush=True)
         assert_close(to_f64(_run_fp8(inp, k8, v8, 0.5, 0.25, S)), ref, what=f"fp8 heads S={S}")
+
+
+def test_max_num_seqs_prefill():
+    """PA_MAX_SEQS prompt chunks in one prefill call (the merge grid's sequence
+    dimension at its limit): chunks of 0..3 tokens, most sequences 0..16
+    tokens long and every 1000th 65..80 (two key pieces at S = 2), every
+    cached token already in the pool.  Inputs are drawn here in bulk (one
+    normal draw for the whole pool) since the pool has 66k blocks."""
+    B, Hq, Hkv, D, bs, Wt = pa.PA_MAX_SEQS, 2, 1, 64, 16, 5
+    rng = np.random.default_rng(9500)
+    totals = rng.integers(0, 17, B)
+    long = np.arange(B) % 1000 == 7
+    totals[long] = rng.integers(65, 81, int(long.sum()))
+    chunks = np.minimum(totals, rng.integers(0, 4, B))
+    nblk = (totals + bs - 1) // bs
+    NB = int(nblk.sum()) + 1
+    poison = NB - 1
+    ids = rng.permutation(NB - 1)
+    tables = np.full((B, Wt), poison, np.int32)
+    off = 0
+    for b in np.nonzero(nblk)[0]:
+        tables[b, :nblk[b]] = ids[off:off + nblk[b]]
+        off += int(nblk[b])
+    pools = []
+    for _ in range(2):
+        pool = np.empty((NB, bs, Hkv, D), np.uint16)
+        for i in range(0, NB, 8192):
+            j = min(NB, i + 8192)
+            pool[i:j] = W.f32_to_bf16_bits(rng.standard_normal((j - i, bs, Hkv, D), np.float32))
+        pool[poison] = W.BF16_NAN
+        tail = np.nonzero(totals % bs)[0]       # slots past each sequence's length: NaN
+        for b in tail:
+            pool[tables[b, totals[b] // bs], totals[b] % bs:] = W.BF16_NAN
+        pools.append(pool)
+    kc, vc = pools
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum(chunks)
+    q = W.f32_to_bf16_bits(rng.standard_normal((int(cu[-1]), Hq, D), np.float32))
+    lens = totals.astype(np.int32)
+    scale = np.float32(0.125)
+    pa.check_tables(tables, lens, NB, bs)
+    pa.check_prefill(cu, lens, 3)
+    ref = oracle.prefill(q, cu, kc, vc, tables, lens, scale)
+    dk, dv = bf16_tensor(kc), bf16_tensor(vc)
+    dq = bf16_tensor(q)
+    out = torch.empty_like(dq)
+    for S in (1, 2):
+        print(f"prefill B={B} S={S}", flush=True)
+        pa.prefill(dq, torch.from_numpy(cu).to(DEV), dk, dv, torch.from_numpy(tables).to(DEV),
+                   torch.from_numpy(lens).to(DEV), float(scale), out, 3, num_splits=S)
+        torch.cuda.synchronize()
+        assert_close(to_f64(out), ref, what=f"prefill B={B} S={S}")
 
 
 def test_one_past_each_limit_is_refused(max_seq_case):
