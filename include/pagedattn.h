@@ -118,6 +118,8 @@ int pa_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mappi
  *                 pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, S)
  *                 bytes for the S actually used (may be NULL when that is 0).
  *                 Calls that run concurrently must not share a workspace.
+ *                 Its contents need no initialisation: the merge reads only
+ *                 the pieces the split pass of the same call wrote.
  * Arithmetic: fp32 scores and accumulators from bf16 inputs; softmax weights
  * are rounded to bf16 before the weighted sum of V.
  */

@@ -237,8 +237,9 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_sp
     """out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over the first
     context_lens[b] tokens of sequence b, read through block_tables.
     num_splits = 0 picks the split count automatically.  The split workspace
-    comes zero-filled from torch's caching allocator unless `workspace` (uint8,
-    on the device, zero-filled before its first use) is given."""
+    comes from torch's caching allocator unless `workspace` (uint8, on the
+    device, of at least decode_workspace_size bytes) is given; its contents
+    need no initialisation."""
     NB, bs, Hkv, D = _pool_dims(k_cache, v_cache)
     dev = k_cache.device
     _need(q, "q", torch.bfloat16, 3, dev)
@@ -390,7 +391,8 @@ def _workspace(B, Hq, D, num_splits, dev, workspace, q_len=1):
     if not need:
         return None, 0, workspace
     if workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+        # no fill: the merge reads only the pieces the split pass wrote
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace.device != dev or workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace needs {need} bytes on {dev}")
     return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace

@@ -310,6 +310,23 @@ def test_workspace_reused_across_calls():
         assert_close(to_f64(c.out), c.ref, what="reuse")
 
 
+def test_workspace_needs_no_initialisation():
+    """A workspace full of NaN bytes before the call: pieces past a sequence's
+    end are never written and must never be read (ragged lengths, empty
+    sequences, S well above the pieces most sequences have)."""
+    import paged_kv_attention_09_amd as pa
+    spec = W.CONFIGS["c3"].with_(context_lens=(0, 1, 130, 4096, 700, 0, 2049, 17), len_range=None,
+                                 append=False)
+    case = DecodeCase(W.make_decode_inputs(spec))
+    for S in (3, 16, 64):
+        ws = torch.full((pa.decode_workspace_size(8, 28, 128, S),), 0xFF, dtype=torch.uint8,
+                        device=DEV)
+        pa.decode(case.q, case.k_cache, case.v_cache, case.tables, case.lens, case.scale, S,
+                  case.out, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(to_f64(case.out), case.ref, what=f"NaN workspace S={S}")
+
+
 def test_partials_then_merge_matches_decode():
     """The two passes as separate calls reach the oracle and agree with the
     single-launch decode up to rounding (the merges sum in different orders,

@@ -113,6 +113,22 @@ def test_prefill_scale_sign(scale):
         assert_close(case.run(S), case.ref, what=f"prefill scale {scale} S{S}")
 
 
+def test_prefill_workspace_needs_no_initialisation():
+    """A prefill workspace full of NaN bytes: rows past each chunk and pieces
+    past each row's causal end are never written and never read."""
+    spec = W.PrefillSpec("wsnan", 14, 2, 128, 16, 200, 160, chunk_lens=(70, 0, 3, 33),
+                         total_lens=(2500, 9, 40, 33), seed=81)
+    case = PrefillCase(spec)
+    max_q = 80
+    for S in (2, 5):
+        n = pa.prefill_workspace_size(4, max_q, 14, 128, S)
+        ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=DEV)
+        pa.prefill(case.q, case.cu, case.k_cache, case.v_cache, case.tables, case.lens,
+                   float(case.inp.scale), case.out, max_q, num_splits=S, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(to_f64(case.out), case.ref, what=f"prefill NaN workspace S={S}")
+
+
 def test_one_token_chunk_equals_decode():
     """A chunk of one query is a decode step."""
     spec = W.PrefillSpec("one", 28, 4, 128, 256, 40, 16, chunk_lens=(1, 1, 1),
