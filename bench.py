@@ -30,7 +30,12 @@ Method
   * roofline.achieved = algorithmic decode bytes per launch / average
     split-kernel duration; peak = 8000 GB/s (MI355X HBM3E).
   * cpu_baseline: the fp64 numpy oracle on host copies of the same workload,
-    one BLAS thread, repeated for about --cpu-seconds.
+    one worker process per host core (at most 16), one BLAS thread each,
+    for about --cpu-seconds; the whole call in one thread is nested.  The
+    same leg checks the benchmarked calls' results against the oracle (the
+    fused decode step and the mixed prefill + decode step).
+  * split_kv_gain: the ctx-4096 batches at the automatic split count against
+    one piece per (sequence, kv head).
 
 Prints ONE JSON line.
 """
@@ -560,13 +565,16 @@ def ingest_trace(directory: str, out_name: str, command: str):
     for r in _read_csv(directory, "kernel_trace.csv"):
         k = _short_kernel(r["Kernel_Name"])
         durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    srcs = PREFILL_SOURCES if "prefill" in out_name else KERNEL_SOURCES
+    src_hash = kernel_source_hash(srcs)
     lines = [f"# Kernel durations: {out_name}", "", "Command (run from /tmp with TMPDIR=/tmp):", "",
              "```", command, "```", "",
              "| kernel | calls | avg us | median us | p90 us | min us | max us | % of GPU time |",
              "|---|---|---|---|---|---|---|---|"]
+    rec = {"command": command, "kernel_source_sha256_16": src_hash, "kernels": {}}
     for r in rows:
         k = _short_kernel(r["Name"])
-        if not k.startswith(("decode", "append", "prefill")):
+        if not k.startswith(("decode", "append", "prefill", "read_probe")):
             continue
         d = sorted(durs.get(k, [float("nan")]))
         p90 = d[min(len(d) - 1, int(0.9 * len(d)))]
@@ -574,10 +582,33 @@ def ingest_trace(directory: str, out_name: str, command: str):
                      f"{statistics.median(d):.2f} | {p90:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
+        rec["kernels"][k] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                             "median_us": statistics.median(d), "p90_us": p90}
+    lines += ["", f"Kernel sources ({', '.join(os.path.basename(x) for x in srcs)}) "
+                  f"sha256[:16], comments excluded: {src_hash}"]
     path = os.path.join(PROFILES, out_name + ".md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
+    with open(os.path.join(PROFILES, out_name + ".json"), "w") as f:
+        json.dump(rec, f, indent=1)
     print(path)
+
+
+def load_trace(out_name: str, kernel_prefix: str):
+    """(average, median) microseconds of the first kernel whose name starts
+    with kernel_prefix in a committed trace summary, if its kernel sources
+    match the current ones; else None."""
+    path = os.path.join(PROFILES, out_name + ".json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    for k, v in rec["kernels"].items():
+        if k.startswith(kernel_prefix):
+            return v["avg_us"], v["median_us"], k
+    return None
 
 
 def ingest_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib: int,
@@ -654,7 +685,7 @@ def ingest_sq(directory: str, kernel: str, out_name: str, command: str, flop_per
     # GRBM counters have one instance per XCD and rocprofv3's own formulas
     # take their maximum, i.e. about the sum over the XCD count.
     gpu = [a for a in _read_csv(directory, "agent_info.csv") if a.get("Agent_Type") == "GPU"][0]
-    nxcc, simds = int(gpu["Num_Xcc"]), int(gpu["Simd_Count"])
+    nxcc, simds, cus = int(gpu["Num_Xcc"]), int(gpu["Simd_Count"]), int(gpu["Cu_Count"])
     for c in list(med):
         if c.startswith("GRBM_"):
             med[c] = med[c] / nxcc
@@ -673,6 +704,12 @@ def ingest_sq(directory: str, kernel: str, out_name: str, command: str, flop_per
         util = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * simds)
         rec["mfma_util"] = util
         lines.append(f"| MfmaUtil = MFMA busy / (GUI active x {simds} SIMDs) | {100 * util:.1f} % |")
+    if "SQ_BUSY_CU_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
+        # SQ_BUSY_CU_CYCLES counts quad-cycles per busy CU, summed over the CUs
+        frac = 4 * med["SQ_BUSY_CU_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * cus)
+        rec["active_cu_frac"] = frac
+        lines.append(f"| active-CU fraction = 4 x SQ_BUSY_CU_CYCLES / (GUI active x {cus} CUs) | "
+                     f"{100 * frac:.1f} % |")
     if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
         ex = med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
         rec["mfma_flop_executed"] = ex
@@ -724,8 +761,9 @@ def load_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(spec, seconds: float):
-    """The oracle, as it stands, on host copies of the workload, one thread."""
+def cpu_baseline_single(spec, seconds: float):
+    """The oracle, as it stands, on host copies of the whole workload call,
+    in this process with one BLAS thread."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -746,7 +784,6 @@ def cpu_baseline(spec, seconds: float):
             if t >= seconds:
                 break
     return {"value": round(per_call * n / t / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"fp64 numpy oracle decode of the full {spec.name} call "
                       f"({spec.num_seqs} seqs, {int(np.sum(inp.context_lens))} tokens), "
                       f"{n} calls in {t:.1f} s, 1 BLAS thread",
@@ -806,22 +843,100 @@ def parity_record(spec):
                       "unreferenced pool NaN-poisoned; fp64 oracle"}
 
 
+def mixed_parity_record(kv_fp8: bool):
+    """The benchmarked mixed step (PrefillWorkload.step: append of the 512-row
+    chunk, prefill, fused append + decode of the 64 sequences, one pool, one
+    stream), run once outside any timed region on the benchmark's own
+    device-drawn inputs (one rotation), against the oracle on host copies of
+    those inputs: the referenced blocks of both pools bit for bit, the prefill
+    and decode rows within 1e-2 + 1e-2 |oracle|.  Part of the oracle leg."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import oracle.kv_fp8 as O8
+    import workloads as W
+
+    wl = PrefillWorkload(W.PREFILL_CONFIGS["c5p"], W.CONFIGS["c5d"], 0.0, kv_fp8=kv_fp8)
+    bs = int(wl.k_cache.shape[2] if kv_fp8 else wl.k_cache.shape[1])
+    host = lambda t: t.detach().cpu().numpy()                            # noqa: E731
+    bits = lambda t: host(t.view(torch.int16)).view(np.uint16)           # noqa: E731
+    ptab, dtab = host(wl.ptables[0]), host(wl.dtables[0])
+    used = [int(x) for b, L in enumerate(wl.plens) for x in ptab[b, :-(-int(L) // bs)]]
+    used += [int(x) for b, L in enumerate(wl.dlens) for x in dtab[b, :-(-int(L) // bs)]]
+    ids = np.asarray(sorted(set(used)), np.int64)
+    lut = np.full(int(wl.k_cache.shape[0]), 0, np.int64)
+    lut[ids] = np.arange(len(ids))
+    ids_t = torch.from_numpy(ids).to(wl.dev)
+    pool = (lambda t: host(t[ids_t])) if kv_fp8 else (lambda t: bits(t[ids_t]))
+    k0, v0 = pool(wl.k_cache), pool(wl.v_cache)
+    wl.out.fill_(float("nan"))
+    wl.dout.fill_(float("nan"))
+    wl.step(0)
+    torch.cuda.synchronize()
+    k1, v1 = pool(wl.k_cache), pool(wl.v_cache)
+    slots = np.concatenate([host(wl.cslots[0]), host(wl.dslots[0])])
+    cslots = lut[slots // bs] * bs + slots % bs
+    nk = np.concatenate([bits(wl.ck), bits(wl.dk)])
+    nv = np.concatenate([bits(wl.cv), bits(wl.dv)])
+    pct, dct = lut[ptab].astype(np.int32), lut[dtab].astype(np.int32)
+    if kv_fp8:
+        ka, va = O8.append_fp8(nk, nv, cslots, k0, v0, wl.k_scale, wl.v_scale)
+        ref_p = O8.prefill_fp8(bits(wl.q), host(wl.cu), ka, va, pct, wl.plens, wl.scale,
+                               wl.k_scale, wl.v_scale)
+        ref_d = O8.decode_fp8(bits(wl.dq), ka, va, dct, wl.dlens, wl.scale, wl.k_scale,
+                              wl.v_scale)
+    else:
+        ka, va = oracle.append(nk, nv, cslots, k0, v0)
+        ref_p = oracle.prefill(bits(wl.q), host(wl.cu), ka, va, pct, wl.plens, wl.scale)
+        ref_d = oracle.decode(bits(wl.dq), ka, va, dct, wl.dlens, wl.scale)
+    rec = {"call": "append chunk, prefill, fused append + decode (one pool, one stream)",
+           "kv": "fp8 e4m3" if kv_fp8 else "bf16",
+           "pools_bit_exact": bool(np.array_equal(k1, ka) and np.array_equal(v1, va)),
+           "tolerance": "1e-2 + 1e-2 |oracle|"}
+    ok = rec["pools_bit_exact"]
+    for part, got_t, ref in (("prefill", wl.out, ref_p), ("decode", wl.dout, ref_d)):
+        got = oracle.bf16_bits_to_f64(bits(got_t))
+        err = np.abs(got - ref)
+        ratio = err / (1e-2 + 1e-2 * np.abs(ref))
+        fin = bool(np.isfinite(got).all())
+        rec[part] = {"outputs": int(ref.size), "max_abs_err": float(np.nanmax(err)),
+                     "rms_err": float(np.sqrt(np.nanmean(err ** 2))),
+                     "max_err_over_tolerance": float(np.nanmax(ratio)), "finite": fin}
+        ok = ok and fin and bool((ratio <= 1.0).all())
+    rec["within_tolerance"] = ok
+    rec["inputs"] = ("the benchmark's own device-drawn mixed-step inputs (one rotation), copied "
+                     "to the host before the step; fp64 oracle")
+    del wl
+    torch.cuda.empty_cache()
+    return rec
+
+
 def cpu_model() -> str:
-    """The host CPU's model name, from /proc/cpuinfo."""
+    """The host CPU's model string and its family/model/stepping, from
+    /proc/cpuinfo."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = (x.strip() for x in line.split(":", 1))
+                    fields.setdefault(k, v)
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    extra = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping")
+                      if k in fields)
+    return f"{name} ({extra})" if extra else name
 
 
-def _oracle_sequence_worker(job):
-    """One sequence of a workload through the oracle, repeatedly, for about
-    `seconds`, in a fresh process with one BLAS thread.  Returns (bytes, s)."""
-    name, b, seconds = job
+def oracle_job(name: str, pairs, seconds: float):
+    """Worker body of the parallel CPU baseline, run in its own process: the
+    oracle over each (sequence, kv head) sub-call in `pairs` of workload
+    `name`, round robin, for about `seconds`.  A sub-call is the oracle's
+    decode of one sequence restricted to one kv head and its group of q heads
+    (the oracle itself, unchanged, on a slice of the inputs).  Prints one JSON
+    line: the sub-calls' algorithmic bytes processed and the seconds taken."""
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -829,39 +944,62 @@ def _oracle_sequence_worker(job):
     spec = W.CONFIGS[name]
     inp = W.make_decode_inputs(spec)
     ct = inp.pool.compact_tables(inp.block_tables, inp.poison_block)
-    lens = inp.context_lens[b:b + 1]
-    per_call = W.algorithmic_decode_bytes(lens, spec.num_q_heads, spec.num_kv_heads,
-                                          spec.head_dim, spec.block_size)
-    n = 0
+    G = spec.group
+    subs = []
+    for b, g in pairs:
+        lens = inp.context_lens[b:b + 1]
+        subs.append((inp.q[b:b + 1, g * G:(g + 1) * G], inp.pool.k[:, :, g:g + 1],
+                     inp.pool.v[:, :, g:g + 1], ct[b:b + 1], lens,
+                     W.algorithmic_decode_bytes(lens, G, 1, spec.head_dim, spec.block_size)))
+    done, n = 0, 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while True:
-            oracle.decode(inp.q[b:b + 1], inp.pool.k, inp.pool.v, ct[b:b + 1], lens, inp.scale)
+            q, k, v, tab, lens, nbytes = subs[n % len(subs)]
+            oracle.decode(q, k, v, tab, lens, inp.scale)
+            done += nbytes
             n += 1
             t = time.perf_counter() - t0
-            if t >= seconds:
+            if t >= seconds and n >= len(subs):
                 break
-    return per_call * n, t
+    print(json.dumps({"bytes": done, "seconds": t, "subcalls": n}), flush=True)
 
 
-def cpu_baseline_parallel(spec, seconds: float):
-    """The same oracle over the workload's sequences in parallel worker
-    processes (started fresh, not forked from this GPU process), one sequence
-    and one BLAS thread each."""
-    import multiprocessing as mp
-    workers = min(spec.num_seqs, len(os.sched_getaffinity(0)), 16)
-    jobs = [(_config_key(spec), b, seconds) for b in range(spec.num_seqs)]
-    with mp.get_context("spawn").Pool(workers) as pool:
-        res = pool.map(_oracle_sequence_worker, jobs, chunksize=1)
-    total = sum(r[0] for r in res)
-    # sequences beyond the worker count run in later rounds; the wall time is
-    # the sum over rounds of the slowest worker of each round
-    rounds = [max(r[1] for r in res[i:i + workers]) for i in range(0, len(res), workers)]
-    wall = sum(rounds)
-    return {"value": round(total / wall / 1e9, 4), "unit": "GB/s", "cores": workers,
-            "kind": "oracle",
-            "sample": f"the same oracle, {spec.num_seqs} sequences over {workers} worker processes "
-                      f"(one BLAS thread each), about {seconds:.0f} s per sequence"}
+def cpu_baseline(spec, seconds: float):
+    """The oracle timed on the host's cores: one worker process per core (at
+    most 16, the CPU share of a one-GPU machine), each with one BLAS thread,
+    sharing the workload's (sequence, kv head) sub-calls; value = their
+    algorithmic bytes over the slowest worker's time.  The same oracle on the
+    whole call in one thread is nested as `single_thread`."""
+    import subprocess
+    name = _config_key(spec)
+    pairs = [(b, g) for b in range(spec.num_seqs) for g in range(spec.num_kv_heads)]
+    visible = len(os.sched_getaffinity(0))
+    workers = max(1, min(visible, 16, len(pairs)))
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    procs = []
+    for w in range(workers):
+        mine = pairs[w::workers]
+        code = (f"import bench; bench.oracle_job({name!r}, {mine!r}, {seconds!r})")
+        procs.append(subprocess.Popen([sys.executable, "-c", code], cwd=ROOT, env=env,
+                                      stdout=subprocess.PIPE, text=True))
+    res = []
+    for p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            raise RuntimeError(f"oracle worker failed with status {p.returncode}")
+        res.append(json.loads(out.strip().splitlines()[-1]))
+    total = sum(r["bytes"] for r in res)
+    wall = max(r["seconds"] for r in res)
+    rec = {"value": round(total / wall / 1e9, 4), "unit": "GB/s", "cores": workers,
+           "kind": "oracle", "cpu_model": cpu_model(), "host_cores_visible": visible,
+           "sample": f"fp64 numpy oracle over the {len(pairs)} (sequence, kv head) sub-calls of "
+                     f"the {spec.name} call, {workers} worker processes with one BLAS thread "
+                     f"each, about {seconds:.0f} s each ({sum(r['subcalls'] for r in res)} "
+                     f"sub-calls); input generation not timed",
+           "us_per_call": round(wall / (sum(r["subcalls"] for r in res) / len(pairs)) * 1e6, 1)}
+    rec["single_thread"] = cpu_baseline_single(spec, seconds / 2)
+    return rec
 
 
 def _config_key(spec):
@@ -893,6 +1031,54 @@ def measure(name, args, steps, warmup, with_kernel=True):
     if spec.len_range is not None:
         rec.update(measure_longest_first(wl, steps, warmup))
     return wl, rec
+
+
+def load_sq(out_name: str, key: str):
+    """A derived value of a committed counter summary whose kernel sources
+    match the current ones, else None."""
+    path = os.path.join(PROFILES, out_name + ".json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get(key)
+
+
+def measure_split_gain(args, steps, warmup):
+    """What split-KV buys at ctx 4096: the same batch at the automatic split
+    count and at one piece per (sequence, kv head) (S = 1, no merge), the
+    split kernel alone (HIP events) and the whole graph-replayed step; the
+    active-CU fraction of each from committed counter summaries
+    (profiles/split_gain_<workload>_s<S>_cu_counters) when they match the
+    current kernels."""
+    import torch
+    import workloads as W
+    res = {}
+    for name in ("c2b1", "c2b8"):
+        wl = DecodeWorkload(W.CONFIGS[name], args.rotate_gib, 0)
+        auto = wl.S
+        row = {"workload": W.CONFIGS[name].name, "auto_splits": auto}
+        for label, S in (("auto", auto), ("s1", 1)):
+            wl.set_splits(S)
+            ms_step, _ = time_steps_graph(wl, steps, warmup)
+            ms_k = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
+            row[f"{label}_step_us"] = round(ms_step * 1e3, 3)
+            row[f"{label}_kernel_us"] = round(ms_k * 1e3, 3)
+            cu = load_sq(f"split_gain_{name}_{'s1' if S == 1 else 'auto'}_cu_counters",
+                         "active_cu_frac")
+            if cu is not None:
+                row[f"{label}_active_cu_frac"] = round(cu, 4)
+        row["step_speedup"] = round(row["s1_step_us"] / row["auto_step_us"], 3)
+        row["kernel_speedup"] = round(row["s1_kernel_us"] / row["auto_kernel_us"], 3)
+        res[name] = row
+        print(f"[bench] split-KV gain {name}: step S=1 {row['s1_step_us']:.2f} us vs S={auto} "
+              f"{row['auto_step_us']:.2f} us (x{row['step_speedup']:.2f})", file=sys.stderr,
+              flush=True)
+        del wl
+        torch.cuda.empty_cache()
+    return res
 
 
 def longest_first_order(wl):
@@ -929,28 +1115,43 @@ def measure_longest_first(wl, steps, warmup):
             "longest_first_kernel_gbps": wl.decode_bytes / (avg * 1e-3) / 1e9}
 
 
-def read_probe_gbps(nbytes: int) -> float:
-    """Read rate of the library's streaming-read probe (16-byte vector loads,
-    no writes but one word per wave) over cold buffers of `nbytes`, rotating
-    over at least 2 GiB so that no read hits the last-level cache; the best
-    of several grid sizes, HIP events over back-to-back launches."""
-    import torch
+def _read_probe_fn():
+    """pa_bench_read_probe from the benchmark's own probe library
+    (libpa_readprobe.so, built beside the attention library)."""
+    import ctypes
 
     import paged_kv_attention_09_amd as pa
-    L = pa.lib()
+    f = ctypes.CDLL(os.path.join(os.path.dirname(pa.LIB_PATH), "libpa_readprobe.so")) \
+        .pa_bench_read_probe
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    return f
+
+
+def read_probe_gbps(nbytes: int):
+    """Fastest plain read of `nbytes` the probe finds on this GPU: each
+    workgroup reads one contiguous slice with 4, 8 or 16 independent 16-byte
+    loads in flight per thread, over grids of 512 to 16384 workgroups; cold
+    buffers (rotating over at least 2 GiB, so no read hits the last-level
+    cache); HIP events over back-to-back launches.  Returns (GB/s, grid,
+    unroll) of the best setting."""
+    import torch
+    f = _read_probe_fn()
     nbytes = max(16, nbytes // 16 * 16)
     sink = torch.empty(4 * 16384, dtype=torch.int32, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     nbuf = max(2, -(-(2 << 30) // nbytes))
     bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0") for _ in range(nbuf)]
-    best = 0.0
-    for wgs in (1024, 2048, 4096, 8192, 16384):
-        def launch(i):
-            st = L.pa_read_probe(bufs[i % nbuf].data_ptr(), nbytes, sink.data_ptr(), wgs, stream)
-            if st != 0:
-                raise RuntimeError(f"pa_read_probe failed with status {st}")
-        ms = time_kernel_events(launch, max(2 * nbuf, 16), nbuf)
-        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+    best = (0.0, 0, 0)
+    for wgs in (512, 1024, 2048, 4096, 8192, 16384):
+        for unroll in (4, 8, 16):
+            def launch(i):
+                st = f(bufs[i % nbuf].data_ptr(), nbytes, sink.data_ptr(), wgs, unroll, stream)
+                if st != 0:
+                    raise RuntimeError(f"pa_bench_read_probe failed with status {st}")
+            ms = time_kernel_events(launch, max(2 * nbuf, 32), nbuf)
+            best = max(best, (nbytes / (ms * 1e-3) / 1e9, wgs, unroll))
     del bufs
     torch.cuda.empty_cache()
     return best
@@ -960,9 +1161,14 @@ def measure_read_ceiling():
     """The read rate a plain streaming read reaches on this GPU, for context
     next to the 8 TB/s peak: cold buffers of 32 MiB (the size of the ctx-4096
     batch-8 decode) and of 1 GiB."""
-    res = {f"read_{mib}MiB_gbps": round(read_probe_gbps(mib << 20), 1) for mib in (32, 1024)}
-    res["probe"] = ("pa_read_probe: 16-byte vector loads over a cold buffer, best of 1024-16384 "
-                    "workgroups, HIP events over back-to-back launches")
+    res = {}
+    for mib in (32, 1024):
+        gbps, wgs, unroll = read_probe_gbps(mib << 20)
+        res[f"read_{mib}MiB_gbps"] = round(gbps, 1)
+        res[f"read_{mib}MiB_best_setting"] = {"workgroups": wgs, "loads_in_flight": unroll}
+    res["probe"] = ("pa_bench_read_probe (libpa_readprobe.so): contiguous slice per workgroup, "
+                    "16-byte loads, best of 512-16384 workgroups x 4/8/16 loads in flight, cold "
+                    "buffers, HIP events over back-to-back launches")
     return res
 
 
@@ -1210,6 +1416,7 @@ def main(argv=None):
                         if k not in ("wall_s",)}
         print(f"[bench] {name}: {msg}", file=sys.stderr, flush=True)
 
+    split_gain = measure_split_gain(args, min(args.steps, 100), min(args.warmup, 10))
     bm_rec = measure_block_manager()
     print(f"[bench] block manager: decode step {bm_rec['decode_step_us_256_seqs']:.1f} us, "
           f"tables {bm_rec['block_tables_us_256_seqs']:.1f} us for 256 sequences; admit "
@@ -1220,7 +1427,7 @@ def main(argv=None):
     # each decode workload's split kernel against a plain read of its own bytes
     for name, rec in others.items():
         if "kernel_gbps" in rec and "decode_bytes" in rec:
-            probe = read_probe_gbps(int(rec["decode_bytes"]))
+            probe = read_probe_gbps(int(rec["decode_bytes"]))[0]
             rec["read_probe_gbps_same_bytes"] = round(probe, 1)
             rec["kernel_frac_of_read_probe"] = round(rec["kernel_gbps"] / probe, 4)
     print(f"[bench] measured read rate (read probe, cold): 32 MiB {ceiling['read_32MiB_gbps']:.0f} "
@@ -1229,6 +1436,7 @@ def main(argv=None):
     spec = W.CONFIGS[args.workload]
     achieved = main_rec["kernel_gbps"]
     traffic = load_traffic(args.workload)
+    trace = load_trace(f"decode_{args.workload}_kernel_trace", "decode_split_kernel")
     line = {
         "metric": "paged-decode achieved HBM GB/s (% of peak) and us/call at ctx 4096",
         "value": round(main_rec["gbps"], 2),
@@ -1259,17 +1467,34 @@ def main(argv=None):
                      "traffic": traffic,
                      "kernel": "decode_split_kernel", "kernel_avg_us": round(main_rec["kernel_avg_us"], 3),
                      "algorithmic_bytes_per_launch": main_rec["decode_bytes"],
+                     "headline": "frac: split-kernel average from HIP events in this run",
                      "frac_of_measured_read_32MiB": round(achieved / ceiling["read_32MiB_gbps"], 4)},
         "measured_read_ceiling": ceiling,
+        "split_kv_gain": split_gain,
         "workloads": others,
     }
+    if trace is not None:
+        avg_us, med_us, kname = trace
+        line["roofline"]["trace"] = {
+            "summary": f"profiles/decode_{args.workload}_kernel_trace.md", "kernel": kname,
+            "avg_us": round(avg_us, 3), "median_us": round(med_us, 3),
+            "frac_from_avg": round(main_rec["decode_bytes"] / (avg_us * 1e-6) / 1e9
+                                   / HBM_PEAK_GBS, 4),
+            "events_over_trace_avg": round(main_rec["kernel_avg_us"] / avg_us, 4)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
-        line["cpu_baseline"]["parallel"] = cpu_baseline_parallel(spec, args.cpu_seconds / 2)
         # the same oracle leg checks the benchmarked call's results on host-drawn inputs
         par = parity_record(spec)
         line["cpu_baseline"]["parity_of_benchmarked_call"] = par
+        mixed_par = {}
+        for name in ("c5mix", "c5mixf8"):
+            if name in others:
+                mixed_par[name] = mixed_parity_record(name.endswith("f8"))
+                others[name]["parity"] = mixed_par[name]
+                print(f"[bench] {name} parity against the oracle: pools bit-exact "
+                      f"{mixed_par[name]['pools_bit_exact']}, within tolerance "
+                      f"{mixed_par[name]['within_tolerance']}", file=sys.stderr, flush=True)
         print(f"[bench] parity against the oracle: max abs err {par['max_abs_err']:.2e}, "
               f"rms {par['rms_err']:.2e}, within tolerance: {par['within_tolerance']}",
               file=sys.stderr, flush=True)

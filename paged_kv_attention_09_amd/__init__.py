@@ -102,8 +102,6 @@ SIGNATURES = {
     "pa_check_tables": (_I, [_VP, _VP, _I, _I, _I, _I64, _I, _VP]),
     "pa_check_slots": (_I, [_VP, _I64, _I64, _I, _VP]),
     "pa_check_prefill": (_I, [_VP, _VP, _I, _I, _VP]),
-    # measurement probe (include/pagedattn_probe.h)
-    "pa_read_probe": (_I, [_VP, _SZ, _VP, _I, _VP]),
 }
 
 _lib = None
@@ -222,6 +220,8 @@ def plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus)
 
 
 def auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, device=None) -> int:
+    if isinstance(device, str):
+        device = torch.device(device)
     if device is None:
         device = torch.cuda.current_device()
     elif isinstance(device, torch.device):
@@ -254,7 +254,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_sp
     W = int(block_tables.shape[1])
     if num_splits == 0 and B > 0:
         num_splits = auto_splits(B, Hkv, W, bs, dev)
-    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace, stream=stream)
     _check("pa_decode", lib().pa_decode(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), float(scale), int(num_splits), out.data_ptr(), B, Hq, Hkv, D,
@@ -274,7 +274,7 @@ def decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float, k_
         raise ValueError(f"out must be [{B}, {Hq}, {D}]")
     if num_splits == 0 and B > 0:
         num_splits = auto_splits(B, Hkv, W, bs, dev)
-    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace, stream=stream)
     _check("pa_decode_fp8", lib().pa_decode_fp8(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), float(scale), float(k_scale), float(v_scale), int(num_splits),
@@ -299,7 +299,7 @@ def append_decode_fp8(q, new_k, new_v, k_cache, v_cache, block_tables, context_l
         raise ValueError(f"new_k/new_v must be [{B}, {Hkv}, {D}]")
     if num_splits == 0 and B > 0:
         num_splits = auto_splits(B, Hkv, W, bs, dev)
-    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace, stream=stream)
     _check("pa_append_decode_fp8", lib().pa_append_decode_fp8(
         q.data_ptr(), new_k.data_ptr(), new_v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), float(scale), float(k_scale),
@@ -327,7 +327,8 @@ def decode_multi_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: flo
     W = int(block_tables.shape[1])
     if num_splits == 0 and B > 0:
         num_splits = auto_splits(B, Hkv, W, bs, dev)
-    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace, q_len=QL)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace, q_len=QL,
+                                             stream=stream)
     _check("pa_decode_multi_fp8", lib().pa_decode_multi_fp8(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), float(scale), float(k_scale), float(v_scale), int(num_splits),
@@ -355,7 +356,8 @@ def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale: float, 
     W = int(block_tables.shape[1])
     if num_splits == 0 and B > 0:
         num_splits = auto_splits(B, Hkv, W, bs, dev)
-    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace, q_len=QL)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace, q_len=QL,
+                                             stream=stream)
     _check("pa_decode_multi", lib().pa_decode_multi(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), float(scale), int(num_splits), out.data_ptr(), B, QL, Hq, Hkv,
@@ -378,7 +380,7 @@ def append_decode(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens,
         raise ValueError(f"new_k/new_v must be [{B}, {Hkv}, {D}]")
     if num_splits == 0 and B > 0:
         num_splits = auto_splits(B, Hkv, W, bs, dev)
-    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace)
+    ws_ptr, ws_bytes, workspace = _workspace(B, Hq, D, num_splits, dev, workspace, stream=stream)
     _check("pa_append_decode", lib().pa_append_decode(
         q.data_ptr(), new_k.data_ptr(), new_v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), float(scale), int(num_splits),
@@ -386,13 +388,24 @@ def append_decode(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
-def _workspace(B, Hq, D, num_splits, dev, workspace, q_len=1):
+def _scratch(nbytes: int, dev, stream) -> torch.Tensor:
+    """A workspace from torch's caching allocator, allocated on the stream the
+    call is enqueued on (not necessarily the current one): the allocator then
+    hands the block to later work only in that stream's order, so freeing it
+    when the call returns cannot let other streams overwrite it while the
+    kernels still use it.  No fill: the kernels read only what they wrote."""
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+def _workspace(B, Hq, D, num_splits, dev, workspace, q_len=1, stream=None):
     need = decode_multi_workspace_size(B, q_len, Hq, D, num_splits) if B > 0 else 0
     if not need:
         return None, 0, workspace
     if workspace is None:
-        # no fill: the merge reads only the pieces the split pass wrote
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream)
     if workspace.device != dev or workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace needs {need} bytes on {dev}")
     return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
@@ -487,7 +500,7 @@ def _prefill(q, cu_seqlens_q, k_cache, v_cache, block_tables, context_lens, scal
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            workspace = _scratch(need, dev, stream)
         if workspace.numel() * workspace.element_size() < need:
             raise ValueError(f"workspace needs {need} bytes")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -508,6 +521,8 @@ def prefill_workspace_size(num_seqs, max_q_len, num_q_heads, head_dim, num_split
 
 def prefill_auto_splits(num_seqs, max_q_len, num_kv_heads, max_blocks_per_seq, block_size,
                         device=None) -> int:
+    if isinstance(device, str):
+        device = torch.device(device)
     if device is None:
         device = torch.cuda.current_device()
     elif isinstance(device, torch.device):

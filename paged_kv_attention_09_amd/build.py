@@ -19,7 +19,11 @@ LIB = os.path.join(OUT_DIR, "libpagedattn.so")
 # The block manager (pa_block_manager.cpp) and the precondition checks
 # (pa_check.cpp) are host code; hipcc compiles them as C++.
 SOURCES = ["pa_api.hip", "pa_append.hip", "pa_decode.hip", "pa_prefill.hip",
-           "pa_block_manager.cpp", "pa_check.cpp", "pa_probe.hip"]
+           "pa_block_manager.cpp", "pa_check.cpp"]
+# The benchmark's streaming-read probe is a library of its own, outside the
+# attention library's ABI.
+PROBE_SOURCES = ["bench/read_probe.hip"]
+PROBE_LIB = os.path.join(OUT_DIR, "libpa_readprobe.so")
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of the generated code (-packed-fp32-ops).
@@ -45,22 +49,29 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print(r.stderr, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library.  Always rebuilds."""
-    os.makedirs(OUT_DIR, exist_ok=True)
-    objs = [os.path.join(OUT_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     for o in objs:
         os.remove(o)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link the attention library and the
+    benchmark's read probe.  Always rebuilds."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    obj = lambda s: os.path.join(OUT_DIR, os.path.basename(os.path.splitext(s)[0]) + ".o")  # noqa
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(7, len(srcs))) as ex:
+        list(ex.map(lambda s: _compile(s, obj(s), verbose), srcs))
+    _link([obj(s) for s in SOURCES], LIB, verbose)
+    _link([obj(s) for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

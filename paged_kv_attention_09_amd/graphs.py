@@ -108,6 +108,10 @@ class PaddedDecodeGraphs:
         P = self.size_for(B)
         b = self._buf[P]
         self.stream.wait_stream(torch.cuda.current_stream(self.stream.device))
+        # the copies run on the graphs' stream: the caller's tensors must not be
+        # recycled by the allocator before that stream has read them
+        for t in (q, new_k, new_v, block_tables, context_lens):
+            t.record_stream(self.stream)
         with torch.cuda.stream(self.stream):
             b["q"][:B].copy_(q)
             b["new_k"][:B].copy_(new_k)

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(HEADERS) == 3 and len(names) == 35, names
+    assert len(HEADERS) == 2 and len(names) == 34, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -118,13 +118,6 @@ def test_append_argument_checks():
     assert f(P, P, P, P, P, 1, 10, 16, 1, 80, None) == UNSUP
     assert f(None, None, None, P, P, 0, 10, 16, 1, 64, None) == OK
     assert f(None, P, P, P, P, 3, 10, 16, 1, 64, None) == NULL
-
-
-def test_read_probe_argument_checks():
-    f = pa.lib().pa_read_probe
-    assert f(None, 16, P, 1, None) == NULL and f(P, 16, None, 1, None) == NULL
-    assert f(P, 0, P, 1, None) == SHAPE and f(P, 24, P, 1, None) == SHAPE
-    assert f(P, 16, P, 0, None) == SHAPE
 
 
 def test_append_fp8_argument_checks():

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import paged_kv_attention_09_amd as pa
 import workloads as W
 from gpu_cases import DEV, DecodeCase, assert_close, bf16_tensor, to_bits, to_f64
 
@@ -267,6 +268,37 @@ def test_nonzero_stream_and_no_host_sync():
         case.run(num_splits=0, stream=s)
     s.synchronize()
     assert_close(to_f64(case.out), case.ref, what="side stream")
+
+
+def test_binding_workspace_lives_on_the_call_stream(monkeypatch):
+    """Without a caller workspace the binding allocates one on the stream the
+    call is enqueued on, even when that stream is not the current one, so the
+    caching allocator cannot hand the freed block to other streams while the
+    split and merge kernels still use it; the results match the oracle."""
+    case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c3"]))
+    s = torch.cuda.Stream()
+    seen = []
+    real_empty = torch.empty
+
+    def spy(*args, **kw):
+        if kw.get("dtype") == torch.uint8:
+            seen.append(torch.cuda.current_stream().cuda_stream)
+        return real_empty(*args, **kw)
+
+    s.wait_stream(torch.cuda.current_stream())
+    # the workload's new rows first (their slots hold poison until appended)
+    pa.reshape_and_cache(case.new_k, case.new_v, case.slots, case.k_cache, case.v_cache, stream=s)
+    monkeypatch.setattr(torch, "empty", spy)
+    pa.decode(case.q, case.k_cache, case.v_cache, case.tables, case.lens, case.scale, 4,
+              case.out, stream=s)
+    monkeypatch.setattr(torch, "empty", real_empty)
+    assert seen == [s.cuda_stream], seen
+    # the current stream allocates and writes while s may still run
+    junk = torch.full((4 << 20,), 3, dtype=torch.uint8, device=DEV)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert_close(to_f64(case.out), case.ref, what="workspace on a non-current stream")
+    del junk
 
 
 @pytest.mark.parametrize("name,S", [("c3", 0), ("c3", 1), ("c5d", 0), ("c2b8", 7), ("c2b8", 0),

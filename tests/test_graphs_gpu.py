@@ -71,3 +71,28 @@ def test_batch_over_the_largest_size_is_refused(setup):
     _, _, graphs = setup
     with pytest.raises(ValueError):
         graphs.size_for(9)
+
+
+def test_prepare_holds_caller_tensors_until_its_stream_read_them(setup):
+    """prepare() copies on the graphs' stream.  With that stream still busy,
+    the caller frees its tensors and fills fresh allocations of the same
+    sizes on its own stream: the static buffers must still receive the
+    original rows (the allocator may not recycle memory the graphs' stream
+    has yet to read)."""
+    case, ref, graphs = setup
+    idx = np.array([4, 1, 10])
+    sel = torch.from_numpy(idx).to(DEV)
+    srcs = [t[sel].clone() for t in (case.q, case.new_k, case.new_v, case.tables, case.lens)]
+    want = [t.clone() for t in srcs]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(graphs.stream):
+        torch.cuda._sleep(20_000_000)            # keeps the copies waiting
+    P = graphs.prepare(*srcs)
+    shapes = [(t.shape, t.dtype) for t in srcs]
+    del srcs
+    junk = [torch.full(s, 7, dtype=dt, device=DEV) for s, dt in shapes]
+    torch.cuda.synchronize()
+    b = graphs.buffers(P)
+    for name, w in zip(("q", "new_k", "new_v", "tables", "lens"), want):
+        assert torch.equal(b[name][:3], w), f"{name} was overwritten before the copy read it"
+    del junk

@@ -169,3 +169,30 @@ def test_poison_not_read_and_finite(chunk512):
     """Pool blocks no sequence references, and slots past the context, hold
     NaN: the output stays finite."""
     assert np.isfinite(chunk512.run(0)).all()
+
+
+def test_prefill_workspace_lives_on_the_call_stream(chunk512, monkeypatch):
+    """As for decode: the binding's own prefill workspace is allocated on the
+    call's stream when that stream is not the current one."""
+    s = torch.cuda.Stream()
+    seen = []
+    real_empty = torch.empty
+
+    def spy(*args, **kw):
+        if kw.get("dtype") == torch.uint8:
+            seen.append(torch.cuda.current_stream().cuda_stream)
+        return real_empty(*args, **kw)
+
+    s.wait_stream(torch.cuda.current_stream())
+    out = torch.empty_like(chunk512.q)
+    monkeypatch.setattr(torch, "empty", spy)
+    pa.prefill(chunk512.q, chunk512.cu, chunk512.k_cache, chunk512.v_cache, chunk512.tables,
+               chunk512.lens, float(chunk512.inp.scale), out, chunk512.max_q, num_splits=4,
+               stream=s)
+    monkeypatch.setattr(torch, "empty", real_empty)
+    assert seen == [s.cuda_stream], seen
+    junk = torch.full((8 << 20,), 3, dtype=torch.uint8, device=DEV)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert_close(to_f64(out), chunk512.ref, what="prefill workspace on a non-current stream")
+    del junk

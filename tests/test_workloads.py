@@ -103,3 +103,43 @@ def test_algorithmic_bytes_c2():
     # 8 x 4096 tokens x 2 kv heads x 128 x 2 B x (K, V) + q + out + 2048 table entries + lens
     assert W.algorithmic_decode_bytes([4096] * 8, 12, 2, 128, 16) == \
         8 * 4096 * 2 * 128 * 2 * 2 + 2 * 8 * 12 * 128 * 2 + 2048 * 4 + 8 * 4
+
+
+def test_mixed_inputs_share_one_pool():
+    """The mixed-batch step's prompt chunk and decode sequences take disjoint
+    blocks of one pool; every row the step appends lands on a poisoned slot
+    of the right sequence and position."""
+    pspec = W.PREFILL_CONFIGS["c5p"].with_(total_lens=(700,), chunk_lens=(200,), num_blocks=64,
+                                          max_blocks_per_seq=4)
+    dspec = W.CONFIGS["c5d"].with_(num_seqs=5, len_range=(1, 900), num_blocks=32,
+                                   max_blocks_per_seq=4)
+    m = W.make_mixed_inputs(pspec, dspec)
+    p, d = m.prefill, m.decode
+    assert p.pool is m.pool and d.pool is m.pool and m.pool.num_blocks == 64
+    assert d.spec.num_blocks == 64 and d.spec.append
+    bs = 256
+    used = []
+    for tab, lens in ((p.block_tables, p.context_lens), (d.block_tables, d.context_lens)):
+        for b, L in enumerate(lens):
+            n = -(-int(L) // bs)
+            used += [int(x) for x in tab[b, :n]]
+            assert (tab[b, n:] == p.poison_block).all()
+    assert len(set(used)) == len(used) and sorted(used) == sorted(int(i) for i in m.pool.ids)
+    idx = {int(x): i for i, x in enumerate(m.pool.ids)}
+    # the chunk's slots are its last 200 positions, the decode slots each last token
+    assert [int(s) for s in p.slot_mapping] == [
+        int(p.block_tables[0, t // bs]) * bs + t % bs for t in range(500, 700)]
+    assert [int(s) for s in d.slot_mapping] == [
+        int(d.block_tables[b, (L - 1) // bs]) * bs + (int(L) - 1) % bs
+        for b, L in enumerate(d.context_lens)]
+    k, v, slots = m.all_rows()
+    assert k.shape == (205, 4, 128) and v.shape == k.shape and len(slots) == 205
+    assert len(set(int(s) for s in slots)) == 205
+    for s in slots:
+        assert (m.pool.k[idx[int(s) // bs], int(s) % bs] == W.BF16_NAN).all()
+        assert (m.pool.v[idx[int(s) // bs], int(s) % bs] == W.BF16_NAN).all()
+    # the cached prefix is data, not poison; the two sides draw different q
+    assert not (m.pool.k[idx[int(p.block_tables[0, 0])], :100] == W.BF16_NAN).any()
+    assert not np.array_equal(p.q[:5], d.q)
+    again = W.make_mixed_inputs(pspec, dspec)
+    assert np.array_equal(again.pool.k, m.pool.k) and np.array_equal(again.decode.q, d.q)

@@ -367,6 +367,75 @@ def make_prefill_inputs(spec: PrefillSpec, *, fill: str = "normal") -> PrefillIn
     return PrefillInputs(spec, q, cu, pool, tables, lens, poison, spec.scale_f32, nk, nv, slots)
 
 
+@dataclasses.dataclass
+class MixedInputs:
+    """One mixed-batch step over one shared pool: the prompt chunk(s) of
+    ``prefill`` and the decode sequences of ``decode`` reference disjoint
+    blocks of the same ``pool`` (both input objects hold that same pool).
+    The chunk's rows and each decode sequence's new row arrive by slot and
+    their slots hold poison until then."""
+    prefill: PrefillInputs
+    decode: DecodeInputs
+    pool: CompactPool
+
+    def all_rows(self):
+        """Every row the step appends, chunk rows first: (new_k, new_v, slots)."""
+        p, d = self.prefill, self.decode
+        return (np.concatenate([p.new_k, d.new_k]), np.concatenate([p.new_v, d.new_v]),
+                np.concatenate([p.slot_mapping, d.slot_mapping]))
+
+
+def make_mixed_inputs(pspec: PrefillSpec, dspec: DecodeSpec) -> MixedInputs:
+    """Inputs of the chunked-prefill mixed batch: prompt chunks (``pspec``)
+    interleaved with active decodes (``dspec``, one new token each), in one
+    pool of max(num_blocks) blocks.  One seeded permutation of that pool
+    (seed ``pspec.seed``) hands the prompt sequences their blocks first, then
+    the decode sequences.  The prompt side draws q and its chunk rows from
+    ``pspec.seed``, the decode side from ``dspec.seed``."""
+    key = lambda s: (s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size)   # noqa: E731
+    assert key(pspec) == key(dspec), "prompt and decode sides must share the pool's shape"
+    bs, Hkv, D, Hq = dspec.block_size, dspec.num_kv_heads, dspec.head_dim, dspec.num_q_heads
+    plens = np.asarray(pspec.total_lens, dtype=np.int32)
+    chunks = np.asarray(pspec.chunk_lens, dtype=np.int32)
+    assert (chunks <= plens).all() and (chunks >= 0).all()
+    dlens = draw_context_lens(dspec)
+    assert (dlens > 0).all(), "every decode sequence appends one token"
+    NB = max(pspec.num_blocks, dspec.num_blocks)
+    W = max(pspec.max_blocks_per_seq, dspec.max_blocks_per_seq)
+    lens = np.concatenate([plens, dlens])
+    tables, ids, poison = assign_blocks(pspec.seed, NB, lens, bs, W)
+    k, v = fill_blocks(pspec.seed, ids, bs, Hkv, D)
+    pool = CompactPool(NB, ids, k, v)
+    poison_tails(pool, tables, lens, bs)
+    P = len(plens)
+    ptab = np.ascontiguousarray(tables[:P, :pspec.max_blocks_per_seq])
+    dtab = np.ascontiguousarray(tables[P:, :dspec.max_blocks_per_seq])
+    cu = np.zeros(P + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(chunks)
+    pslots = np.asarray([int(ptab[b, t // bs]) * bs + t % bs
+                         for b, (L, n) in enumerate(zip(plens, chunks))
+                         for t in range(int(L) - int(n), int(L))], dtype=np.int64)
+    dslots = np.asarray([int(dtab[b, (L - 1) // bs]) * bs + int((L - 1) % bs)
+                         for b, L in enumerate(dlens)], dtype=np.int64)
+    idx = {int(p): i for i, p in enumerate(ids)}
+    for s in np.concatenate([pslots, dslots]):
+        i = idx[int(s) // bs]
+        pool.k[i, int(s) % bs] = BF16_NAN
+        pool.v[i, int(s) % bs] = BF16_NAN
+    tq = int(cu[-1])
+    pre = PrefillInputs(
+        pspec, normal_bf16(pspec.seed, (_TAG_Q,), (tq, Hq, D)), cu, pool, ptab, plens, poison,
+        pspec.scale_f32, normal_bf16(pspec.seed, (_TAG_NEWK,), (tq, Hkv, D)),
+        normal_bf16(pspec.seed, (_TAG_NEWV,), (tq, Hkv, D)), pslots)
+    B = len(dlens)
+    dec = DecodeInputs(
+        dspec.with_(append=True, num_blocks=NB), normal_bf16(dspec.seed, (_TAG_Q,), (B, Hq, D)),
+        pool, dtab, dlens, poison, dspec.scale_f32,
+        normal_bf16(dspec.seed, (_TAG_NEWK,), (B, Hkv, D)),
+        normal_bf16(dspec.seed, (_TAG_NEWV,), (B, Hkv, D)), dslots)
+    return MixedInputs(pre, dec, pool)
+
+
 def random_e4m3_codes(seed: int, tags: Sequence[int], shape) -> np.ndarray:
     """Random fp8 codes: sign, exponent field uniform in 4..8 and mantissa
     field uniform in 0..7, so magnitudes lie in [2^-3, 3.75] and no code is
