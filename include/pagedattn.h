@@ -63,14 +63,18 @@ enum {
   PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required      */
   PA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed      */
   PA_ERR_NO_BLOCKS = -7,   /* block manager: the pool cannot supply the blocks */
-  PA_ERR_STATE = -8        /* block manager: unknown/duplicate sequence, or a
+  PA_ERR_STATE = -8,       /* block manager: unknown/duplicate sequence, or a
                               forbidden state change                          */
+  PA_ERR_SCRATCH = -9      /* pa_decode_noalloc: the call needs more than the
+                              library's static scratch                        */
 };
 
 #define PA_MAX_SPLITS 256
 #define PA_MAX_QUERY_TOKENS 8
 #define PA_MAX_SEQS 65535
 #define PA_MAX_HEADS 4096
+/* Bytes of the static device scratch of pa_decode_noalloc (per device). */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
 int pa_version(void);
@@ -294,6 +298,31 @@ int pa_decode_merge(const void *workspace, size_t workspace_bytes, const int32_t
 /* Workspace bytes pa_decode needs for a given split count (0 when
  * num_splits <= 1).  Returns 0 for invalid arguments. */
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int num_splits);
+
+/*
+ * pa_decode for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, computation and results as pa_decode (the same
+ * kernels, bit for bit at the same split count), minus the workspace: the
+ * split partials go to a static device array of PA_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per device, held until the process ends.  Nothing
+ * is allocated or freed, and the scratch needs no initialisation (the merge
+ * reads only what the split pass of the same call wrote).
+ *   - Every call on one device shares that device's scratch: calls that may
+ *     run concurrently on one device (different streams, overlapping
+ *     graphs) race and must be serialised by the caller.
+ *   - A call whose split count needs more than PA_NOALLOC_SCRATCH_BYTES
+ *     (pa_decode_workspace_size) returns PA_ERR_SCRATCH and enqueues
+ *     nothing; pass a smaller num_splits, or use pa_decode.
+ *   - The scratch's device address is looked up once per device, on the
+ *     first call made with that device current (PA_ERR_HIP if the lookup
+ *     fails).
+ */
+int pa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      int num_splits, void *out, int num_seqs, int num_q_heads,
+                      int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                      int max_blocks_per_seq, void *stream);
 
 /* Split count that pa_decode uses for num_splits = 0 on a device with
  * num_cus compute units.  Pure host arithmetic on the shapes (context

@@ -52,6 +52,8 @@ PA_MAX_SPLITS = 256
 PA_MAX_QUERY_TOKENS = 8
 PA_MAX_SEQS = 65535
 PA_MAX_HEADS = 4096
+PA_ERR_SCRATCH = -9
+PA_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 # Every symbol include/pagedattn.h declares, with its ctypes signature.
 _VP, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -64,6 +66,8 @@ SIGNATURES = {
     "pa_append_decode": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F, _I, _VP, _I, _I, _I, _I, _I,
                               _I64, _I, _VP, _SZ, _VP]),
     "pa_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "pa_decode_noalloc": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _I, _VP, _I, _I, _I, _I, _I, _I64, _I,
+                               _VP]),
     "pa_decode_multi": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _I, _VP, _I, _I, _I, _I, _I, _I, _I64, _I,
                              _VP, _SZ, _VP]),
     "pa_decode_multi_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
@@ -259,6 +263,24 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_sp
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         context_lens.data_ptr(), float(scale), int(num_splits), out.data_ptr(), B, Hq, Hkv, D,
         bs, NB, W, ws_ptr, ws_bytes, _stream_ptr(stream, dev)))
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                   num_splits: int, out, stream=None):
+    """decode without a workspace and without any allocation: the split
+    partials go to the library's static per-device scratch
+    (PA_NOALLOC_SCRATCH_BYTES).  Calls that may overlap on one device race on
+    that scratch.  A split count whose partials do not fit raises
+    PagedAttnError with status PA_ERR_SCRATCH."""
+    NB, bs, Hkv, D, B, Hq, W, dev = _decode_dims(q, k_cache, v_cache, block_tables, context_lens)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError(f"out must be [{B}, {Hq}, {D}]")
+    _check("pa_decode_noalloc", lib().pa_decode_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), float(scale), int(num_splits), out.data_ptr(), B, Hq, Hkv, D,
+        bs, NB, W, _stream_ptr(stream, dev)))
     return out
 
 

@@ -69,11 +69,32 @@ int cu_count(int device) {
   return g_cu_count[device];
 }
 
+// Split partials of pa_decode_noalloc: a static device array, one copy per
+// device (each device that loads the library holds its own until the process
+// ends).  Host code never passes this name to a kernel: on the host it is only
+// a stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_addr[kMaxDevices];
+
+// Device address of `device`'s copy of the scratch, or NULL; `device` must be
+// the current device.
+void *scratch_address(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[device], [device] {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) ptr = nullptr;
+    g_scratch_addr[device] = ptr;
+  });
+  return g_scratch_addr[device];
+}
+
 }  // namespace
 
 extern "C" {
 
-int pa_version(void) { return 100; }
+int pa_version(void) { return 101; }
 
 const char *pa_status_string(int status) {
   switch (status) {
@@ -87,6 +108,9 @@ const char *pa_status_string(int status) {
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP call or kernel launch failed";
     case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: the KV pool cannot supply the blocks";
     case PA_ERR_STATE: return "PA_ERR_STATE: unknown or duplicate sequence, or forbidden change";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: the split partials exceed PA_NOALLOC_SCRATCH_BYTES; use fewer "
+             "splits or pa_decode with a workspace";
     default: return "unknown pagedattn status";
   }
 }
@@ -316,6 +340,35 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
   return decode_entry(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                       max_blocks_per_seq, workspace, workspace_bytes, stream, DecodeVariant{});
+}
+
+int pa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      int num_splits, void *out, int num_seqs, int num_q_heads,
+                      int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                      int max_blocks_per_seq, void *stream) {
+  // argument checks and the split count first: a refused call touches no device
+  pa::DecodeArgs a;
+  int st = resolve_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!out) return PA_ERR_NULL;
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  if (a.num_splits > 1) {
+    if (pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, a.num_splits) >
+        PA_NOALLOC_SCRATCH_BYTES)
+      return PA_ERR_SCRATCH;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+    ws = scratch_address(dev);
+    if (ws == nullptr) return PA_ERR_HIP;
+    ws_bytes = PA_NOALLOC_SCRATCH_BYTES;
+  }
+  return decode_entry(q, k_cache, v_cache, block_tables, context_lens, scale, num_splits, out,
+                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, ws, ws_bytes, stream, DecodeVariant{});
 }
 
 int pa_append_decode(const void *q, const void *new_k, const void *new_v, void *k_cache,

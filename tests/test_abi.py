@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(HEADERS) == 2 and len(names) == 34, names
+    assert len(HEADERS) == 2 and len(names) == 35, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
