@@ -510,6 +510,86 @@ def time_steps_eager(wl, steps: int, warmup: int) -> float:
     return s.elapsed_time(e) / steps, host * 1e3 / steps
 
 
+def measure_multilayer(args, layers: int = 28, steps: int = 20, warmup: int = 3):
+    """A whole decode step's attention, as a model runs it: `layers` fused
+    append + decode calls back to back, layer l over its own K/V (block set
+    l of the workload's rotations).  Timed three ways: issued from Python
+    through the binding (what an engine loop does), issued through the raw C
+    function with prebuilt arguments (the least host work possible), and
+    replayed from one captured graph.  Milliseconds come from HIP events
+    around `steps` steps; host issue time from the host clock."""
+    import ctypes
+    import torch
+    import workloads as W
+    res = {}
+    for name in ("c2b1", "c2b8"):
+        wl = DecodeWorkload(W.CONFIGS[name], args.rotate_gib, 0)
+        rots = [l % wl.R for l in range(layers)]
+        f = wl.pa.lib().pa_append_decode
+        sp = torch.cuda.current_stream().cuda_stream
+        B, Hq, D = (int(x) for x in wl.q.shape)
+        NB, bs, Hkv, _ = (int(x) for x in wl.k_cache.shape)
+        W_ = int(wl.tables[0].shape[1])
+        raw = [(wl.q.data_ptr(), wl.new_k.data_ptr(), wl.new_v.data_ptr(),
+                wl.k_cache.data_ptr(), wl.v_cache.data_ptr(), wl.tables[r].data_ptr(),
+                wl.lens.data_ptr(), ctypes.c_float(wl.scale), wl.S, wl.out.data_ptr(), B, Hq,
+                Hkv, D, bs, NB, W_, wl.ws.data_ptr(), wl.ws.numel(), sp) for r in rots]
+
+        def step_binding():
+            for r in rots:
+                wl.step(r)
+
+        def step_raw():
+            for a in raw:
+                f(*a)
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            host = time.perf_counter() - t0
+            e.record()
+            torch.cuda.synchronize()
+            return s.elapsed_time(e) * 1e3 / steps, host * 1e6 / steps
+
+        eager_b, host_b = timed(step_binding)
+        eager_r, host_r = timed(step_raw)
+        step_binding()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step_binding()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        graph_us = s.elapsed_time(e) * 1e3 / steps
+        res[name] = {"workload": W.CONFIGS[name].name, "layers": layers, "splits": wl.S,
+                     "eager_binding_us_per_step": round(eager_b, 2),
+                     "eager_binding_host_us_per_step": round(host_b, 2),
+                     "eager_raw_us_per_step": round(eager_r, 2),
+                     "eager_raw_host_us_per_step": round(host_r, 2),
+                     "graph_us_per_step": round(graph_us, 2),
+                     "graph_saving_vs_binding": round(1 - graph_us / eager_b, 4),
+                     "graph_saving_vs_raw": round(1 - graph_us / eager_r, 4)}
+        print(f"[bench] {layers}-layer step {name}: graph {graph_us:.1f} us, eager through the "
+              f"binding {eager_b:.1f} us (host {host_b:.1f}), raw C calls {eager_r:.1f} us",
+              file=sys.stderr, flush=True)
+        del g, wl
+        torch.cuda.empty_cache()
+    return res
+
+
 def time_steps_graph(wl, steps: int, warmup: int, fused: bool = True):
     """Warm up eagerly, capture `steps` steps in one graph, replay it between events."""
     import torch
@@ -704,11 +784,16 @@ def ingest_sq(directory: str, kernel: str, out_name: str, command: str, flop_per
         util = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * simds)
         rec["mfma_util"] = util
         lines.append(f"| MfmaUtil = MFMA busy / (GUI active x {simds} SIMDs) | {100 * util:.1f} % |")
-    if "SQ_BUSY_CU_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
-        # SQ_BUSY_CU_CYCLES counts quad-cycles per busy CU, summed over the CUs
-        frac = 4 * med["SQ_BUSY_CU_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * cus)
+    if "SQ_BUSY_CU_CYCLES" in med:
+        # SQ_BUSY_CU_CYCLES, summed over the CUs, counts the shader clocks each
+        # CU has waves resident (a long kernel filling every CU reads ~0.9 x
+        # CUs x its clocks).  GRBM_GUI_ACTIVE spans more than a short dispatch
+        # under counter collection, so the fraction uses the dispatch's own
+        # duration at the nominal 2.4 GHz shader clock.
+        frac = med["SQ_BUSY_CU_CYCLES"] / (med["dispatch_ns"] * 2.4 * cus)
         rec["active_cu_frac"] = frac
-        lines.append(f"| active-CU fraction = 4 x SQ_BUSY_CU_CYCLES / (GUI active x {cus} CUs) | "
+        rec["cu_busy_cycles_per_ns"] = med["SQ_BUSY_CU_CYCLES"] / med["dispatch_ns"]
+        lines.append(f"| active-CU fraction = SQ_BUSY_CU_CYCLES / (dispatch ns x 2.4 GHz x {cus} CUs) | "
                      f"{100 * frac:.1f} % |")
     if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
         ex = med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
@@ -1417,6 +1502,7 @@ def main(argv=None):
         print(f"[bench] {name}: {msg}", file=sys.stderr, flush=True)
 
     split_gain = measure_split_gain(args, min(args.steps, 100), min(args.warmup, 10))
+    multilayer = measure_multilayer(args)
     bm_rec = measure_block_manager()
     print(f"[bench] block manager: decode step {bm_rec['decode_step_us_256_seqs']:.1f} us, "
           f"tables {bm_rec['block_tables_us_256_seqs']:.1f} us for 256 sequences; admit "
@@ -1471,6 +1557,7 @@ def main(argv=None):
                      "frac_of_measured_read_32MiB": round(achieved / ceiling["read_32MiB_gbps"], 4)},
         "measured_read_ceiling": ceiling,
         "split_kv_gain": split_gain,
+        "multilayer_graph": multilayer,
         "workloads": others,
     }
     if trace is not None:

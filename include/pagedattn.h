@@ -101,7 +101,12 @@ int pa_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mappi
 
 /*
  * Paged decode: one query token per sequence attends to the first
- * context_lens[b] tokens of its sequence, fetched through block_tables:
+ * context_lens[b] tokens of its sequence, fetched through block_tables
+ * (PagedAttention over per-request block tables: psmarter/mini-infer summary,
+ * "How It Works"; the unified [B, 1] paged decode of the mini-infer docs,
+ * "Core Capabilities at a Glance" table, row "Batched Paged Decode"; the
+ * split-KV pieces below: zingnex.cn mini-infer thread, feature list item 7,
+ * and the MiniInfer README's "Attention Backend" table):
  *   out[b, h] = softmax_t(scale * q[b, h] . K_b[t, g]) V_b[t, g],  g = kv head of h,
  * with K_b[t] = k_cache[block_tables[b, t / block_size], t % block_size].
  * context_lens counts every cached token, including one appended this step.
