@@ -79,6 +79,10 @@ def parse_args(argv=None):
                    help="comma list of extra workloads measured into 'workloads' ('' = none)")
     p.add_argument("--kernel-loop", type=int, default=0,
                    help="profiling mode: launch only the split kernel this many times and exit")
+    p.add_argument("--graph", action="store_true",
+                   help="with --kernel-loop: capture the launches in one HIP graph and replay it, "
+                        "so they run back to back as in the timed region (a tracer's per-launch "
+                        "host work then no longer spaces them out)")
     p.add_argument("--sweep-splits", default="",
                    help="tuning mode: comma list of split counts; prints us/step per workload")
     p.add_argument("--ingest-trace", nargs=3, metavar=("DIR", "NAME", "COMMAND"),
@@ -1418,8 +1422,19 @@ def main(argv=None):
         return
     if args.kernel_loop:
         wl = DecodeWorkload(W.CONFIGS[args.workload], args.rotate_gib, args.splits)
-        for i in range(args.kernel_loop):
-            wl.kernel(i % wl.R)
+        if args.graph:
+            for i in range(3):
+                wl.kernel(i % wl.R)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(args.kernel_loop):
+                    wl.kernel(i % wl.R)
+            torch.cuda.synchronize()
+            g.replay()
+        else:
+            for i in range(args.kernel_loop):
+                wl.kernel(i % wl.R)
         torch.cuda.synchronize()
         print(json.dumps({"workload": args.workload, "kernel_launches": args.kernel_loop,
                           "splits": wl.S, "decode_bytes_per_launch": wl.decode_bytes}))
