@@ -36,6 +36,9 @@ Method
     fused decode step and the mixed prefill + decode step).
   * split_kv_gain: the ctx-4096 batches at the automatic split count against
     one piece per (sequence, kv head).
+  * equal_share_bound: the random-length batches' tokens laid out as equal
+    lengths, one workgroup per (compute unit, kv head): the fastest any split
+    into equal token shares could run, beside the drawn lengths' kernel.
 
 Prints ONE JSON line.
 """
@@ -1170,6 +1173,55 @@ def measure_split_gain(args, steps, warmup):
     return res
 
 
+def equal_share_lens(total: int, n: int):
+    """n lengths summing to total, differing by at most one token."""
+    base, extra = divmod(total, n)
+    return tuple([base + 1] * extra + [base] * (n - extra))
+
+
+def measure_equal_share(args, others, steps, warmup):
+    """The best any split of a random-length batch into equal token shares
+    can do: the same number of context tokens and the same heads, laid out
+    as one sequence per (compute unit, kv head) with equal lengths, decoded
+    at one piece per (sequence, kv head) so that every compute unit gets
+    one workgroup with the same work and no merge runs.  Reported beside the
+    drawn batch's own kernel and step times."""
+    import torch
+    import workloads as W
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {}
+    for name in ("c3", "c5d", "c4"):
+        if name not in others:
+            continue
+        spec = W.CONFIGS[name]
+        total = int(W.draw_context_lens(spec).sum())
+        n = max(spec.num_seqs, cus // spec.num_kv_heads)
+        eq = spec.with_(num_seqs=n, context_lens=equal_share_lens(total, n), len_range=None,
+                        num_blocks=max(spec.num_blocks, n * spec.max_blocks_per_seq))
+        wl = DecodeWorkload(eq, args.rotate_gib, 1)
+        ms_step, _ = time_steps_graph(wl, steps, warmup)
+        ms_k = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
+        drawn = others[name]
+        drawn_k = min(drawn["kernel_avg_us"], drawn.get("longest_first_kernel_us", 1e30))
+        row = {"workload": spec.name, "context_tokens": total, "equal_share_seqs": n,
+               "equal_share_len": int(wl.lens_np.max()),
+               "equal_share_kernel_us": round(ms_k * 1e3, 3),
+               "equal_share_step_us": round(ms_step * 1e3, 3),
+               "equal_share_kernel_frac": round(wl.decode_bytes / (ms_k * 1e-3) / 1e9
+                                                / HBM_PEAK_GBS, 4),
+               "drawn_kernel_us": round(drawn_k, 3),
+               "drawn_kernel_frac": round(drawn["decode_bytes"] / (drawn_k * 1e-6) / 1e9
+                                          / HBM_PEAK_GBS, 4)}
+        res[name] = row
+        print(f"[bench] equal-share bound {name}: kernel {row['equal_share_kernel_us']:.2f} us "
+              f"(frac {row['equal_share_kernel_frac']:.3f}) against {row['drawn_kernel_us']:.2f} "
+              f"us (frac {row['drawn_kernel_frac']:.3f}) for the drawn lengths", file=sys.stderr,
+              flush=True)
+        del wl
+        torch.cuda.empty_cache()
+    return res
+
+
 def longest_first_order(wl):
     """Device permutation of a workload's sequences, longest first, as the
     library's block manager gives it (pa_bm_order_longest_first)."""
@@ -1517,6 +1569,7 @@ def main(argv=None):
         print(f"[bench] {name}: {msg}", file=sys.stderr, flush=True)
 
     split_gain = measure_split_gain(args, min(args.steps, 100), min(args.warmup, 10))
+    equal_share = measure_equal_share(args, others, min(args.steps, 100), min(args.warmup, 10))
     multilayer = measure_multilayer(args)
     bm_rec = measure_block_manager()
     print(f"[bench] block manager: decode step {bm_rec['decode_step_us_256_seqs']:.1f} us, "
@@ -1572,6 +1625,7 @@ def main(argv=None):
                      "frac_of_measured_read_32MiB": round(achieved / ceiling["read_32MiB_gbps"], 4)},
         "measured_read_ceiling": ceiling,
         "split_kv_gain": split_gain,
+        "equal_share_bound": equal_share,
         "multilayer_graph": multilayer,
         "workloads": others,
     }
