@@ -36,6 +36,9 @@ Method
     fused decode step and the mixed prefill + decode step).
   * split_kv_gain: the ctx-4096 batches at the automatic split count against
     one piece per (sequence, kv head).
+  * device_pass: from the committed step trace (profiles/decode_<workload>_
+    step_trace), the split and merge kernels' medians and p90s and their sum
+    per step, when the trace matches the current kernels.
   * equal_share_bound: the random-length batches' tokens laid out as equal
     lengths, one workgroup per (compute unit, kv head): the fastest any split
     into equal token shares could run, beside the drawn lengths' kernel.
@@ -82,6 +85,9 @@ def parse_args(argv=None):
                    help="comma list of extra workloads measured into 'workloads' ('' = none)")
     p.add_argument("--kernel-loop", type=int, default=0,
                    help="profiling mode: launch only the split kernel this many times and exit")
+    p.add_argument("--step-loop", type=int, default=0,
+                   help="profiling mode: capture this many whole fused steps (append + split "
+                        "pass + merge) in one HIP graph, replay it once and exit")
     p.add_argument("--graph", action="store_true",
                    help="with --kernel-loop: capture the launches in one HIP graph and replay it, "
                         "so they run back to back as in the timed region (a tracer's per-launch "
@@ -671,6 +677,31 @@ def ingest_trace(directory: str, out_name: str, command: str):
                      f"{float(r['Percentage']):.1f} |")
         rec["kernels"][k] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
                              "median_us": statistics.median(d), "p90_us": p90}
+    # a decode step's device time: each merge dispatch paired with the split
+    # dispatch before it (trace order), as the sum of the two durations and as
+    # the span from the split's start to the merge's end
+    trace = sorted(_read_csv(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    sums, spans, last = [], [], None
+    for r in trace:
+        k = _short_kernel(r["Kernel_Name"])
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        if k.startswith("decode_split"):
+            last = (t0, t1)
+        elif k.startswith("decode_combine") and last is not None:
+            sums.append(((last[1] - last[0]) + (t1 - t0)) / 1e3)
+            spans.append((t1 - last[0]) / 1e3)
+            last = None
+    if sums:
+        sums.sort()
+        spans.sort()
+        pick = lambda d, q: d[min(len(d) - 1, int(q * len(d)))]
+        lines += ["", f"Per step ({len(sums)} split + merge pairs): split + merge durations median "
+                      f"{statistics.median(sums):.2f} us, p90 {pick(sums, 0.9):.2f} us; from the "
+                      f"split's start to the merge's end median {statistics.median(spans):.2f} us, "
+                      f"p90 {pick(spans, 0.9):.2f} us."]
+        rec["step"] = {"pairs": len(sums), "sum_median_us": statistics.median(sums),
+                       "sum_p90_us": pick(sums, 0.9), "span_median_us": statistics.median(spans),
+                       "span_p90_us": pick(spans, 0.9)}
     lines += ["", f"Kernel sources ({', '.join(os.path.basename(x) for x in srcs)}) "
                   f"sha256[:16], comments excluded: {src_hash}"]
     path = os.path.join(PROFILES, out_name + ".md")
@@ -679,6 +710,28 @@ def ingest_trace(directory: str, out_name: str, command: str):
     with open(os.path.join(PROFILES, out_name + ".json"), "w") as f:
         json.dump(rec, f, indent=1)
     print(path)
+
+
+def load_step_trace(out_name: str):
+    """The per-step device pass of a committed step trace summary (split and
+    merge kernels of graph-replayed fused steps), if its kernel sources match
+    the current ones; else None."""
+    path = os.path.join(PROFILES, out_name + ".json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or "step" not in rec:
+        return None
+    res = {"summary": f"profiles/{out_name}.md"}
+    for k, v in rec["kernels"].items():
+        tag = "split" if k.startswith("decode_split") else (
+            "merge" if k.startswith("decode_combine") else None)
+        if tag:
+            res[f"{tag}_median_us"] = round(v["median_us"], 3)
+            res[f"{tag}_p90_us"] = round(v["p90_us"], 3)
+    res.update({k: round(v, 3) if isinstance(v, float) else v for k, v in rec["step"].items()})
+    return res
 
 
 def load_trace(out_name: str, kernel_prefix: str):
@@ -1472,6 +1525,21 @@ def main(argv=None):
         print(json.dumps({"workload": args.workload, "calls": args.kernel_loop,
                           "splits": wl.S, "decode_bytes_per_call": wl.decode_bytes}))
         return
+    if args.step_loop:
+        wl = DecodeWorkload(W.CONFIGS[args.workload], args.rotate_gib, args.splits)
+        for i in range(3):
+            wl.step(i % wl.R)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.step_loop):
+                wl.step(i % wl.R)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": args.workload, "steps": args.step_loop, "splits": wl.S,
+                          "decode_bytes_per_step": wl.decode_bytes}))
+        return
     if args.kernel_loop:
         wl = DecodeWorkload(W.CONFIGS[args.workload], args.rotate_gib, args.splits)
         if args.graph:
@@ -1637,6 +1705,9 @@ def main(argv=None):
             "frac_from_avg": round(main_rec["decode_bytes"] / (avg_us * 1e-6) / 1e9
                                    / HBM_PEAK_GBS, 4),
             "events_over_trace_avg": round(main_rec["kernel_avg_us"] / avg_us, 4)}
+    device_pass = load_step_trace(f"decode_{args.workload}_step_trace")
+    if device_pass is not None:
+        line["device_pass"] = device_pass
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
