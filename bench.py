@@ -1112,7 +1112,7 @@ def oracle_job(name: str, pairs, seconds: float):
 
 def cpu_baseline(spec, seconds: float):
     """The oracle timed on the host's cores: one worker process per core (at
-    most 16, the CPU share of a one-GPU machine), each with one BLAS thread,
+    most 16), each with one BLAS thread,
     sharing the workload's (sequence, kv head) sub-calls; value = their
     algorithmic bytes over the slowest worker's time.  The same oracle on the
     whole call in one thread is nested as `single_thread`."""
