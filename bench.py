@@ -18,8 +18,9 @@ Method
     --rotate-gib GiB of K/V between two uses of the same block), so no call
     finds its K/V in the 256 MB last-level cache.
   * The K timed steps are captured once into a HIP graph and replayed
-    between two events, with torch.cuda.synchronize() on both sides, so host
-    launch overhead never starves the GPU.
+    between two events, with torch.cuda.synchronize() on both sides, the
+    queue primed by a device-side sleep so that the graph launch's host time
+    is spent while the GPU sleeps: the events bracket the K steps' GPU work.
   * The dominant kernel (the split-KV pass) is timed with HIP events around
     back-to-back launches on the current stream, the queue primed by a
     device-side sleep so the events bracket GPU work and not host gaps.
@@ -427,12 +428,7 @@ def time_graph(fn, R: int, steps: int, warmup: int) -> float:
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    g.replay()
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / steps
+    return primed_events(g.replay) / steps
 
 
 def measure_prefill(args, steps, warmup, with_decode: bool, kv_fp8: bool = False):
@@ -474,6 +470,29 @@ def sleep_cycles_for(ms: float) -> int:
     return int(ms / per)
 
 
+_SLEEP_CYCLES = None
+
+
+def primed_events(issue) -> float:
+    """Milliseconds between two HIP events around the GPU work `issue()`
+    enqueues on the current stream, the queue primed by a device-side sleep
+    so that the host's enqueue time (a graph launch, or the first eager
+    calls) is spent while the GPU sleeps and the events bracket GPU work
+    only.  Synchronised on both sides."""
+    import torch
+    global _SLEEP_CYCLES
+    if _SLEEP_CYCLES is None:
+        _SLEEP_CYCLES = sleep_cycles_for(20.0)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(_SLEEP_CYCLES)
+    s.record()
+    issue()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e)
+
+
 def time_kernel_events(fn, n: int, rotations: int):
     """HIP events around n back-to-back launches of `fn(i)` on the current
     stream, the queue primed by a device-side sleep so that the launches run
@@ -497,7 +516,8 @@ def time_steps_eager(wl, steps: int, warmup: int) -> float:
     """The fused append + decode step launched from the host every time (no
     graph), through the raw C function with prebuilt ctypes arguments so the
     binding's Python checks are not timed.  Returns milliseconds per step
-    (HIP events around the loop) and the host's issue time per call."""
+    (HIP events around the loop, the queue primed by a device-side sleep as
+    for the graph) and the host's issue time per call."""
     import ctypes
     import torch
     f = wl.pa.lib().pa_append_decode
@@ -512,15 +532,16 @@ def time_steps_eager(wl, steps: int, warmup: int) -> float:
     for i in range(warmup):
         assert f(*args[i % wl.R]) == 0
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        f(*args[i % wl.R])
-    host = time.perf_counter() - t0
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / steps, host * 1e3 / steps
+    host = [0.0]
+
+    def issue():
+        t0 = time.perf_counter()
+        for i in range(steps):
+            f(*args[i % wl.R])
+        host[0] = time.perf_counter() - t0
+
+    ms = primed_events(issue)
+    return ms / steps, host[0] * 1e3 / steps
 
 
 def measure_multilayer(args, layers: int = 28, steps: int = 20, warmup: int = 3):
@@ -617,15 +638,10 @@ def time_steps_graph(wl, steps: int, warmup: int, fused: bool = True):
     torch.cuda.synchronize()
     g.replay()          # first replay uploads the graph
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    s.record()
-    g.replay()
-    e.record()
-    torch.cuda.synchronize()
+    ms = primed_events(g.replay)
     wall = time.perf_counter() - t0
-    return s.elapsed_time(e) / steps, wall
+    return ms / steps, wall
 
 
 def _short_kernel(name: str) -> str:
