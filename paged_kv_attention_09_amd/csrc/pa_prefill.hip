@@ -88,15 +88,36 @@ __device__ __forceinline__ int k_pos8(int c, int r) {
   return c ^ ((r >> (D == 128 ? 1 : 2)) & (D / 16 - 1));
 }
 
+// fp8 pools: stored 16-byte position of chunk c of V row r.  One transposing
+// V read of a 16-lane group covers rows 4 q + e and 16 + 4 q + e (e < 4) of
+// a 32-key step at one chunk; the eight rows get distinct positions (D = 128:
+// eight positions per row; D = 64: four positions per 64-byte row, rows of
+// either parity sharing a 128-byte bank line), so the read is conflict-free.
+template <int D>
+__device__ __forceinline__ int v_pos8(int c, int r) {
+  return D == 128 ? c ^ ((r & 3) | ((r >> 2) & 4)) : c ^ (((r >> 1) & 1) | ((r >> 3) & 2));
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b8: within each group of 16 lanes, lane c receives as its
+// byte k (k < 8) byte c % 8 of the 8 bytes addressed by lane 2 k + c / 8 of
+// its group: the 8 rows addressed by lane pairs, column c.
+__device__ __forceinline__ uint2 read_tr8(const char *p) {
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2 *)(__attribute__((address_space(3))) void *)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
 // KV8: the pools hold fp8 codes, head-major [NB, Hkv, bs, D].  Tiles of
-// codes stream into LDS; K fragments widen to bf16 in registers, and each
-// tile's V is widened once, by all waves, into a bf16 tile laid out as the
-// bf16 path's V tile, which the unchanged transposed reads consume.  k_scale
+// codes stream into LDS and widen to bf16 in registers: K fragments after an
+// 8-byte read, V^T fragments after one 8-bit transposing read that gathers a
+// lane's eight keys (in the P^T key order) of its head_dim column.  k_scale
 // is folded into the score scale, v_scale into the output.
 template <int D, int G, bool KV8>
 __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   using Lay = PrefillLayout<D>;
-  constexpr int ROWB = Lay::ROWB, TILEB = Lay::TILEB, KS = Lay::KSTEPS;
+  constexpr int ROWB = Lay::ROWB, KS = Lay::KSTEPS;
   constexpr int DB = Lay::DBLK;
   // rows as stored and staged (one byte per element for fp8)
   constexpr int RB = KV8 ? D : ROWB;
@@ -113,13 +134,11 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   // as many stages (up to four) as kTileLds holds, fewer where the DMA
   // count of the tiles in flight behind the one waited for would overflow
   // the vmcnt field
-  constexpr int STL = (kTileLds - (KV8 ? TILEB : 0)) / (2 * TILEK);
+  constexpr int STL = kTileLds / (2 * TILEK);
   constexpr int NSTL = STL < 4 ? STL : 4;
   constexpr int NST = (NSTL - 2) * NPW <= 63 ? NSTL : 3;
   static_assert(NST >= 2 && (NST - 2) * NPW <= 63, "stages and vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[NST][2][TILEK];  // [stage][K, V]
-  // fp8 pools: this tile's V as bf16 (one byte when unused)
-  __shared__ __attribute__((aligned(1024))) char vconv[KV8 ? TILEB : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // q head within the group
@@ -183,8 +202,7 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
     const int jj = is_v ? j - NDMA : j;
     const int row_in = jj * RPD + lane / NCH;
     const int p = lane % NCH;
-    // fp8 V tiles stay unswizzled: they are only read by the widening pass
-    const int c = KV8 ? (is_v ? p : k_pos8<D>(p, row_in))
+    const int c = KV8 ? (is_v ? v_pos8<D>(p, row_in) : k_pos8<D>(p, row_in))
                       : (is_v ? v_pos<D>(p, row_in) : k_pos<D>(p, row_in));
     dma_voff[jw] = (uint32_t)(row_in & 15) * RS + (uint32_t)c * 16;
   }
@@ -245,17 +263,22 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   // db, key step kk): source row 4 q4 + c16 / 4 (+ 32 kk, + 16 for the upper
   // half), columns 16 db + 4 (c16 % 4) in the 32-byte pair db ^ (row & 7).
   // fp8 pools: K fragment (mb, ks) is 8 bytes of row 16 mb + c16 at chunk
-  // 2 ks + q4 / 2, half q4 % 2.
+  // 2 ks + q4 / 2, half q4 % 2.  V^T fragment (db, kk): lane c16 addresses
+  // half c16 % 2 of chunk db of key row kr = 4 q4 + k (k = c16 / 2 < 4) or
+  // 16 + 4 q4 + k - 4 (k >= 4), + 32 kk; the transposing read hands it
+  // column 16 db + c16 of its group's eight rows, k-th byte from row k.
   int k_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     k_off[ks] = KV8 ? c16 * RB + k_pos8<D>(2 * ks + (q4 >> 1), c16) * 16 + (q4 & 1) * 8
                     : c16 * ROWB + k_pos<D>(ks * 4 + q4, c16) * 16;
   const int tr_row = 4 * q4 + (c16 >> 2);
+  const int kr = (c16 >> 1) < 4 ? 4 * q4 + (c16 >> 1) : 12 + 4 * q4 + (c16 >> 1);
   int v_off[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
-    v_off[db] = tr_row * ROWB + v_pos<D>(2 * db + ((c16 & 3) >> 1), tr_row) * 16 + (c16 & 1) * 8;
+    v_off[db] = KV8 ? kr * RB + v_pos8<D>(db, kr) * 16 + (c16 & 1) * 8
+                    : tr_row * ROWB + v_pos<D>(2 * db + ((c16 & 3) >> 1), tr_row) * 16 + (c16 & 1) * 8;
 
   for (int it = 0; it < ntiles; ++it) {
     // this wave's DMAs of tile it are done when at most those of the tiles
@@ -270,19 +293,7 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
       if (it + NST < ntiles) tile_blocks(kt0 + NST * kKeys, blk);   // consumed next iteration
     }
     const char *Kt = smem[it % NST][0];
-    const char *Vt = KV8 ? vconv : smem[it % NST][1];
-    if constexpr (KV8) {
-      // widen this tile's V to bf16, every thread a few 16-code chunks:
-      // chunk c of row r becomes bf16 chunks 2c, 2c+1, one swizzled pair
-      const char *v8 = smem[it % NST][1];
-      for (int idx = threadIdx.x; idx < kKeys * NCH; idx += 64 * G) {
-        const int r = idx / NCH, c = idx % NCH;
-        const uint4 raw = *(const uint4 *)(v8 + r * RB + c * 16);
-        char *dst = vconv + r * ROWB + v_pos<D>(2 * c, r) * 16;
-        *(uint4 *)dst = fp8x8_to_bf16(uint2{raw.x, raw.y});
-        *(uint4 *)(dst + 16) = fp8x8_to_bf16(uint2{raw.z, raw.w});
-      }
-    }
+    const char *Vt = smem[it % NST][1];
 
     // ---- S^T = K Q^T: KG key blocks x 2 row blocks, 2 KG independent chains ----
     f32x4 s[KG][2];
@@ -385,17 +396,20 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // fp8 pools: every wave's widened V is in place
-    if constexpr (KV8) __syncthreads();
     // ---- O^T += V^T P^T, and the row sums l += ones P^T on the same unit ----
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char *vp = Vt + v_off[db] + kk * 32 * ROWB;
-        const uint2 lo = read_tr(vp);
-        const uint2 hi = read_tr(vp + 16 * ROWB);
-        const uint4 vf = uint4{lo.x, lo.y, hi.x, hi.y};
+        uint4 vf;
+        if constexpr (KV8) {
+          vf = fp8x8_to_bf16(read_tr8(Vt + v_off[db] + kk * 32 * RB));
+        } else {
+          const char *vp = Vt + v_off[db] + kk * 32 * ROWB;
+          const uint2 lo = read_tr(vp);
+          const uint2 hi = read_tr(vp + 16 * ROWB);
+          vf = uint4{lo.x, lo.y, hi.x, hi.y};
+        }
         o[db][0] = mfma_k32(vf, pf[0][kk], o[db][0]);
         o[db][1] = mfma_k32(vf, pf[1][kk], o[db][1]);
       }
