@@ -43,10 +43,10 @@
 //    rows, one or two tiles, with query token j masking keys past
 //    L - q_len + j; every staged chunk serves all of them.
 //  * fp8 pools (e4m3 codes, head-major [NB, Hkv, bs, D]): the chunks stage
-//    one byte per element; K fragments widen to bf16 in registers, each
-//    chunk's V widens into a per-wave bf16 buffer read by the same
-//    transposed reads; k_scale is folded into the score scale and v_scale
-//    into the output.
+//    one byte per element; K fragments widen to bf16 in registers, and V^T
+//    fragments come from the code chunk by an 8-bit transposing read and
+//    widen in registers too; k_scale is folded into the score scale and
+//    v_scale into the output.
 //  * The 4 waves' (m, l, O) are merged through LDS; the workgroup writes
 //    either the final bf16 rows (one piece) or fp32 partials plus their
 //    base-2 log-sum-exp for the combine kernel.
@@ -155,7 +155,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   constexpr int CHK = kChunk * RB;                 // bytes of one staged chunk of K (or V)
   constexpr int NDMA = CHK / 1024;                 // DMA instructions per tensor per chunk
   constexpr int STB = 2 * CHK;                     // one stage: K chunk then V chunk
-  constexpr int CVB = KV8 ? CHB : 0;               // bf16 V conversion buffer
+  // fp8 pools, several query tokens: room for the 16-row four-wave merge,
+  // which needs more than the stages
+  constexpr int CVB = KV8 && MULTI ? CHB : 0;
   constexpr int RC = MULTI ? 16 : G;   // rows per merge pass
   constexpr int WAVE_LDS =
       KV8 ? NSTAGE * STB + CVB + (MULTI ? 0 : (G * ROWB + 1023) / 1024 * 1024)
@@ -207,8 +209,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 
   constexpr int QB = MULTI ? 0 : (G * ROWB + 1023) / 1024 * 1024;
   char *my = smem + wave * WAVE_LDS;
-  char *cvb = my + NSTAGE * STB;  // fp8 pools: this chunk's V as bf16
-  char *qlds = cvb + CVB;
+  char *qlds = my + NSTAGE * STB + CVB;
   char *plds = qlds + QB;  // vector path only
   const uint32_t my_off = lds_offset(my);
   const uint32_t q_off = lds_offset(qlds);
@@ -344,7 +345,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
       // at head_dim 16 db + 4 (hh % 4).
       // fp8 pools: K fragment kk is 8 bytes of the stored row hh, at position
       // 2 kk + qd / 2, half qd % 2 (row_swizzle8 keeps these reads
-      // conflict-free); the V^T offsets then address the bf16 buffer.
+      // conflict-free).  V^T fragment db comes from one 8-bit transposing
+      // read: lane hh addresses half hh % 2 of position db of code row
+      // 4 qd + (hh / 2) % 4 (lane pairs 4..7 repeat rows 0..3), and receives
+      // head_dim 16 db + hh of rows 4 qd .. 4 qd + 3 as its bytes 0..3.
       uint32_t k_off[KS], v_off[DB];
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
@@ -354,18 +358,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
         else
           k_off[kk] = (uint32_t)(hh * ROWB + (((4 * kk + qd) ^ row_swizzle<D, MF>(hh)) * 16));
       }
-      {
+      if constexpr (KV8) {
+        const int vr = 4 * qd + ((hh >> 1) & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          v_off[db] = (uint32_t)(CHK + vr * RB + ((db ^ row_swizzle8<D>(vr)) * 16) + (hh & 1) * 8);
+      } else {
         const int vr = 4 * qd + (hh >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          v_off[db] = (uint32_t)((KV8 ? 0 : CHB) + vr * ROWB +
+          v_off[db] = (uint32_t)(CHB + vr * ROWB +
                                  (((2 * db + ((hh & 3) >> 1)) ^ row_swizzle<D, MF>(vr)) * 16) +
                                  (hh & 1) * 8);
       }
-      // fp8 pools, V conversion: lane converts BPL bytes of stored row lane / 4
-      constexpr int BPL = CHK / 64;
-      const int cv_row = lane >> 2;
-      const int cv_pos = (lane & 3) * (BPL / 16);
       // Per tile: is this lane's column a query row, and the last key its
       // query token may see (query token j sits at position L - q_len + j).
       bool colv[NT];
@@ -407,21 +412,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) sc[t] = mfma_k32(kf, qf[t][kk], sc[t]);
         }
-        if constexpr (KV8) {
-          // this chunk's V rows, fp8 -> bf16, into the wave's buffer (the
-          // previous chunk's V^T reads were issued before these writes)
-          const char *src = st + CHK + cv_row * RB;
-          char *dst = cvb + cv_row * ROWB;
-#pragma unroll
-          for (int j = 0; j < BPL / 16; ++j) {
-            const int p = cv_pos + j;
-            const uint4 raw = *(const uint4 *)(src + ((p ^ row_swizzle8<D>(cv_row)) * 16));
-            const uint4 lo = fp8x8_to_bf16(uint2{raw.x, raw.y});
-            const uint4 hi = fp8x8_to_bf16(uint2{raw.z, raw.w});
-            *(uint4 *)(dst + (((2 * p) ^ row_swizzle<D, MF>(cv_row)) * 16)) = lo;
-            *(uint4 *)(dst + (((2 * p + 1) ^ row_swizzle<D, MF>(cv_row)) * 16)) = hi;
-          }
-        }
 
         // ---- online softmax, lazily rescaled (see the file comment) ----
         const int tok = tc + 4 * qd;
@@ -462,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
         // ---- O^T += V^T P^T: lane holds query row 16 t + hh, head_dim 16 db + 4 qd + i ----
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint2 vf = read_tr((KV8 ? cvb : st) + v_off[db]);
+          const uint2 vf = KV8 ? fp8x4_to_bf16(read_tr8(st + v_off[db]).x) : read_tr(st + v_off[db]);
 #pragma unroll
           for (int t = 0; t < NT; ++t) o[t][db] = mfma_k16(vf, pb[t], o[t][db]);
         }

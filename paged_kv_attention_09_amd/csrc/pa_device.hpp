@@ -81,9 +81,25 @@ __device__ __forceinline__ uint2 read_tr(const char *p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b8: within each group of 16 lanes, lane c receives as its
+// byte k (k < 8) byte c % 8 of the 8 bytes addressed by lane 2 k + c / 8 of
+// its group: the 8 rows addressed by lane pairs, column c.
+__device__ __forceinline__ uint2 read_tr8(const char *p) {
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2 *)(__attribute__((address_space(3))) void *)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
 // ---- fp8 (OCP e4m3) codes ----
-// 8 codes -> 8 bf16 values (exact: every e4m3 value is a bf16 value), element
+// 4 codes -> 4 bf16 values (exact: every e4m3 value is a bf16 value), element
 // order kept.
+__device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t v) {
+  return uint2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.f, true))};
+}
+// 8 codes -> 8 bf16 values, element order kept.
 __device__ __forceinline__ uint4 fp8x8_to_bf16(uint2 v) {
   return uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, false)),
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.f, true)),

@@ -98,17 +98,6 @@ __device__ __forceinline__ int v_pos8(int c, int r) {
   return D == 128 ? c ^ ((r & 3) | ((r >> 2) & 4)) : c ^ (((r >> 1) & 1) | ((r >> 3) & 2));
 }
 
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-
-// ds_read_b64_tr_b8: within each group of 16 lanes, lane c receives as its
-// byte k (k < 8) byte c % 8 of the 8 bytes addressed by lane 2 k + c / 8 of
-// its group: the 8 rows addressed by lane pairs, column c.
-__device__ __forceinline__ uint2 read_tr8(const char *p) {
-  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-      (__attribute__((address_space(3))) i32x2 *)(__attribute__((address_space(3))) void *)p);
-  return __builtin_bit_cast(uint2, v);
-}
-
 // KV8: the pools hold fp8 codes, head-major [NB, Hkv, bs, D].  Tiles of
 // codes stream into LDS and widen to bf16 in registers: K fragments after an
 // 8-byte read, V^T fragments after one 8-bit transposing read that gathers a
