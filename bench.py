@@ -695,8 +695,13 @@ def ingest_trace(directory: str, out_name: str, command: str):
                              "median_us": statistics.median(d), "p90_us": p90}
     # a decode step's device time: each merge dispatch paired with the split
     # dispatch before it (trace order), as the sum of the two durations and as
-    # the span from the split's start to the merge's end
+    # the span from the split's start to the merge's end; only for a trace of
+    # one split-kernel variant (one workload)
     trace = sorted(_read_csv(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    splits = {_short_kernel(r["Kernel_Name"]) for r in trace
+              if _short_kernel(r["Kernel_Name"]).startswith("decode_split")}
+    if len(splits) != 1:
+        trace = []
     sums, spans, last = [], [], None
     for r in trace:
         k = _short_kernel(r["Kernel_Name"])
