@@ -89,10 +89,11 @@ __device__ __forceinline__ int k_pos8(int c, int r) {
 }
 
 // fp8 pools: stored 16-byte position of chunk c of V row r.  One transposing
-// V read of a 16-lane group covers rows 4 q + e and 16 + 4 q + e (e < 4) of
-// a 32-key step at one chunk; the eight rows get distinct positions (D = 128:
-// eight positions per row; D = 64: four positions per 64-byte row, rows of
-// either parity sharing a 128-byte bank line), so the read is conflict-free.
+// V read of a 16-lane group covers rows 4 q + e and 16 + 4 q + e (e < 4) of a
+// 32-key step at one chunk.  D = 128: the eight rows get eight distinct
+// positions.  D = 64 (four positions per row): rows e and 16 + e get distinct
+// positions, and so do rows of equal parity, so no two of the eight rows meet
+// in a bank whether a bank line is 128 or 256 bytes.
 template <int D>
 __device__ __forceinline__ int v_pos8(int c, int r) {
   return D == 128 ? c ^ ((r & 3) | ((r >> 2) & 4)) : c ^ (((r >> 1) & 1) | ((r >> 3) & 2));
