@@ -1316,15 +1316,21 @@ def longest_first_order(wl):
 def measure_longest_first(wl, steps, warmup):
     """The same batch launched longest sequence first, in the order the
     library's block manager gives (pa_bm_order_longest_first): the sequences'
-    rows of tables and lengths permuted, the work unchanged."""
+    rows of tables and lengths permuted, the work unchanged; the split count
+    from the host's lengths in that order (pa_decode_auto_splits_lengths)."""
     perm = longest_first_order(wl)
-    saved = wl.tables, wl.lens
+    saved = wl.tables, wl.lens, wl.S
     wl.tables = [t[perm].contiguous() for t in saved[0]]
     wl.lens = saved[1][perm].contiguous()
+    spec = wl.spec
+    S_lf = wl.pa.auto_splits_lengths(wl.lens_np[perm.cpu().numpy()], spec.num_kv_heads,
+                                     spec.max_blocks_per_seq, spec.block_size, wl.dev)
+    wl.set_splits(S_lf)
     ms_step, _ = time_steps_graph(wl, steps, warmup)
     avg = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
-    wl.tables, wl.lens = saved
-    return {"longest_first_us_per_call": ms_step * 1e3,
+    wl.tables, wl.lens = saved[:2]
+    wl.set_splits(saved[2])
+    return {"longest_first_splits": S_lf, "longest_first_us_per_call": ms_step * 1e3,
             "longest_first_gbps": (wl.decode_bytes + wl.append_bytes) / (ms_step * 1e-3) / 1e9,
             "longest_first_kernel_us": avg * 1e3,
             "longest_first_kernel_gbps": wl.decode_bytes / (avg * 1e-3) / 1e9}

@@ -344,6 +344,31 @@ int pa_decode_plan_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq
 int pa_decode_auto_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
                           int block_size, int device);
 
+/* Split count for a batch whose context lengths the host knows, in launch
+ * order (context_lens: host int32 [num_seqs], e.g. from the block manager,
+ * ordered longest first by pa_bm_order_longest_first).  The split pass
+ * balances the work of a compute unit, not of a sequence (split-KV
+ * partitioning, zingnex.cn mini-infer thread, feature list item 7; the
+ * variable-length batches of continuous batching, MiniInfer README,
+ * architecture figure, Scheduler box).  Returns pa_decode_plan_splits' choice except where the
+ * (sequence, kv head) units fill more than half and at most all of the
+ * num_cus compute units; there it compares one piece per unit with two
+ * pieces, whose second pieces pa_decode dispatches in mirrored unit order
+ * (unit u's second piece goes out as the (num_seqs * num_kv_heads - 1 - u)-th
+ * second-piece workgroup, so a compute unit's second workgroup belongs to the
+ * unit mirrored from its first), by the largest number of tokens one compute
+ * unit reads, counting the merge launch two pieces add as 256 tokens, and
+ * returns 1 or 2.  Lengths beyond the table capacity count as the capacity.
+ * Pure host arithmetic; returns PA_ERR_NULL without lengths, or a negative
+ * status for the shapes pa_decode_plan_splits refuses. */
+int pa_decode_plan_splits_lengths(const int32_t *context_lens, int num_seqs, int num_kv_heads,
+                                  int max_blocks_per_seq, int block_size, int num_cus);
+
+/* pa_decode_plan_splits_lengths with the compute-unit count of HIP device
+ * `device`. */
+int pa_decode_auto_splits_lengths(const int32_t *context_lens, int num_seqs, int num_kv_heads,
+                                  int max_blocks_per_seq, int block_size, int device);
+
 /*
  * Chunked prefill over the paged cache: sequence b contributes the
  * n_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b] query rows

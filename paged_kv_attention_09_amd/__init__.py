@@ -28,6 +28,9 @@ Calls (argument order as in the C ABI):
   decode_multi_workspace_size(num_seqs, q_len, num_q_heads, head_dim, num_splits)
   plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus)
   auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, device=None)
+  plan_splits_lengths(context_lens, num_kv_heads, max_blocks_per_seq, block_size, num_cus),
+  auto_splits_lengths(context_lens, num_kv_heads, max_blocks_per_seq, block_size, device=None):
+      the same from the host's context lengths in launch order (host int32 array)
   BlockManager(num_blocks, block_size, max_blocks_per_seq, prefix_cache): the host-side
       pool manager (admit / append / truncate / release / preempt / block_tables / stats)
   check_tables(block_tables, context_lens, num_blocks, block_size, fused_append=False),
@@ -73,6 +76,8 @@ SIGNATURES = {
     "pa_decode_multi_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "pa_decode_plan_splits": (_I, [_I, _I, _I, _I, _I]),
     "pa_decode_auto_splits": (_I, [_I, _I, _I, _I, _I]),
+    "pa_decode_plan_splits_lengths": (_I, [_VP, _I, _I, _I, _I, _I]),
+    "pa_decode_auto_splits_lengths": (_I, [_VP, _I, _I, _I, _I, _I]),
     "pa_decode_partials": (_I, [_VP, _VP, _VP, _VP, _VP, _F, _I, _I, _I, _I, _I, _I, _I64, _I, _VP,
                                 _SZ, _VP]),
     "pa_decode_merge": (_I, [_VP, _SZ, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP]),
@@ -223,16 +228,47 @@ def plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus)
     return r
 
 
-def auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, device=None) -> int:
+def _device_index(device) -> int:
     if isinstance(device, str):
         device = torch.device(device)
     if device is None:
-        device = torch.cuda.current_device()
-    elif isinstance(device, torch.device):
-        device = device.index if device.index is not None else torch.cuda.current_device()
+        return torch.cuda.current_device()
+    if isinstance(device, torch.device):
+        return device.index if device.index is not None else torch.cuda.current_device()
+    return int(device)
+
+
+def auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, device=None) -> int:
     r = int(lib().pa_decode_auto_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
-                                        int(device)))
+                                        _device_index(device)))
     _check("pa_decode_auto_splits", min(r, 0))
+    return r
+
+
+def _host_lens(context_lens):
+    a = np.ascontiguousarray(np.asarray(context_lens), dtype=np.int32)
+    if a.ndim != 1:
+        raise ValueError("context_lens must be one-dimensional")
+    return a
+
+
+def plan_splits_lengths(context_lens, num_kv_heads, max_blocks_per_seq, block_size,
+                        num_cus) -> int:
+    a = _host_lens(context_lens)
+    r = int(lib().pa_decode_plan_splits_lengths(a.ctypes.data_as(ctypes.c_void_p), len(a),
+                                                num_kv_heads, max_blocks_per_seq, block_size,
+                                                num_cus))
+    _check("pa_decode_plan_splits_lengths", min(r, 0))
+    return r
+
+
+def auto_splits_lengths(context_lens, num_kv_heads, max_blocks_per_seq, block_size,
+                        device=None) -> int:
+    a = _host_lens(context_lens)
+    r = int(lib().pa_decode_auto_splits_lengths(a.ctypes.data_as(ctypes.c_void_p), len(a),
+                                                num_kv_heads, max_blocks_per_seq, block_size,
+                                                _device_index(device)))
+    _check("pa_decode_auto_splits_lengths", min(r, 0))
     return r
 
 
@@ -643,7 +679,7 @@ def check_prefill(cu_seqlens_q, context_lens, max_q_len: int) -> None:
 
 __all__ = ["reshape_and_cache", "decode", "append_decode", "decode_partials", "decode_merge", "prefill",
            "prefill_workspace_size", "prefill_auto_splits", "decode_workspace_size", "plan_splits",
-           "auto_splits", "decode_multi", "decode_multi_workspace_size", "reshape_and_cache_fp8",
+           "auto_splits", "plan_splits_lengths", "auto_splits_lengths", "decode_multi", "decode_multi_workspace_size", "reshape_and_cache_fp8",
            "decode_fp8", "append_decode_fp8", "decode_multi_fp8", "prefill_fp8", "BlockManager", "lib", "LIB_PATH", "SIGNATURES", "PagedAttnError",
            "PA_MAX_SPLITS", "PA_MAX_QUERY_TOKENS", "PA_MAX_SEQS", "PA_MAX_HEADS",
            "check_tables", "check_slots", "check_prefill", "PreconditionError", "PA_CHECK_KINDS"]

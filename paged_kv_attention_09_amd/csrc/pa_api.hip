@@ -4,6 +4,7 @@
 // caller's stream, in the order the calls are made.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 
@@ -203,6 +204,53 @@ int pa_decode_auto_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq
   return pa_decode_plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, cus);
 }
 
+// The merge launch and its read of the partials cost about what a compute
+// unit takes to read this many tokens of one kv head at the decode's rate
+// (measured: ≈ 4 µs against ≈ 60 tokens per µs per compute unit).
+constexpr int64_t kMergeTokens = 256;
+
+int pa_decode_plan_splits_lengths(const int32_t *context_lens, int num_seqs, int num_kv_heads,
+                                  int max_blocks_per_seq, int block_size, int num_cus) {
+  const int base =
+      pa_decode_plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus);
+  if (base < 0) return base;
+  if (!context_lens) return PA_ERR_NULL;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  // the one-or-two-pieces regime: the first pieces fill more than half and at
+  // most all of the compute units
+  if (units > num_cus || 2 * units <= num_cus) return base;
+  const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
+  const int h = split_len_for(max_tokens, 2);
+  if (num_pieces(max_tokens, h) != 2) return base;
+  auto len = [&](int64_t u) {
+    const int64_t L = context_lens[u / num_kv_heads];
+    return L < 0 ? (int64_t)0 : (L > max_tokens ? max_tokens : L);
+  };
+  // S = 1: one workgroup per unit, each on its own compute unit.
+  int64_t m1 = 0;
+  for (int64_t u = 0; u < units; u += num_kv_heads) m1 = std::max(m1, len(u));
+  // S = 2: workgroup ids 0 .. units - 1 are the first pieces of units
+  // 0 .. units - 1, ids units + x the second piece of unit units - 1 - x
+  // (mirrored); ids i and i + num_cus share a compute unit (each round of
+  // dispatch gives every compute unit one workgroup, in id order).
+  auto tokens = [&](int64_t id) -> int64_t {
+    if (id < units) return std::min(len(id), (int64_t)h);
+    if (id < 2 * units) return std::max(len(2 * units - 1 - id) - h, (int64_t)0);
+    return 0;
+  };
+  int64_t m2 = 0;
+  for (int64_t c = 0; c < num_cus; ++c) m2 = std::max(m2, tokens(c) + tokens(c + num_cus));
+  return m2 + kMergeTokens < m1 ? 2 : 1;
+}
+
+int pa_decode_auto_splits_lengths(const int32_t *context_lens, int num_seqs, int num_kv_heads,
+                                  int max_blocks_per_seq, int block_size, int device) {
+  const int cus = cu_count(device);
+  if (cus <= 0) return PA_ERR_HIP;
+  return pa_decode_plan_splits_lengths(context_lens, num_seqs, num_kv_heads, max_blocks_per_seq,
+                                       block_size, cus);
+}
+
 namespace {
 
 // Shared argument resolution of the decode entry points.  Fills `a` except the
@@ -246,6 +294,7 @@ int resolve_decode(const void *q, const void *k_cache, const void *v_cache,
   a->bs_shift = log2_exact(block_size);
   a->split_len = split_len;
   a->num_splits = num_pieces(max_tokens, split_len);
+  a->mirror_second = 0;   // set at launch (split_launch)
   a->q_len = 1;
   a->kv_fp8 = 0;
   a->v_scale = 1.0f;
@@ -265,9 +314,25 @@ int attach_workspace(pa::DecodeArgs *a, int num_seqs, int head_dim, const void *
   return PA_OK;
 }
 
+// The split pass, after every argument check: with two pieces whose first
+// pieces take at most one compute unit each, the second pieces go out in
+// mirrored unit order (see decode_split_kernel).
+int split_launch(pa::DecodeArgs a, int head_dim, int group, int num_seqs, hipStream_t s) {
+  if (a.num_splits == 2) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+    const int cus = cu_count(dev);
+    if (cus <= 0) return PA_ERR_HIP;
+    a.mirror_second = (int64_t)num_seqs * a.num_kv_heads <= cus ? 1 : 0;
+  }
+  return pa::launch_decode_split(a, head_dim, group, num_seqs, s) == hipSuccess ? PA_OK
+                                                                                : PA_ERR_HIP;
+}
+
 int launch_split_and_merge(const pa::DecodeArgs &a, int head_dim, int group, int num_seqs,
                            hipStream_t s) {
-  if (pa::launch_decode_split(a, head_dim, group, num_seqs, s) != hipSuccess) return PA_ERR_HIP;
+  const int st = split_launch(a, head_dim, group, num_seqs, s);
+  if (st != PA_OK) return st;
   if (a.num_splits > 1 && pa::launch_decode_combine(a, head_dim, num_seqs, s) != hipSuccess)
     return PA_ERR_HIP;
   return PA_OK;
@@ -462,9 +527,7 @@ int pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
   st = attach_workspace(&a, num_seqs, head_dim, workspace, workspace_bytes);
   if (st != PA_OK) return st;
   const int group = num_q_heads / num_kv_heads;
-  return pa::launch_decode_split(a, head_dim, group, num_seqs, (hipStream_t)stream) == hipSuccess
-             ? PA_OK
-             : PA_ERR_HIP;
+  return split_launch(a, head_dim, group, num_seqs, (hipStream_t)stream);
 }
 
 int pa_decode_merge(const void *workspace, size_t workspace_bytes, const int32_t *context_lens,

@@ -170,9 +170,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   // Grid: x = (sequence, kv head), y = piece.  Workgroups dispatch in id
   // order and round-robin over the 8 XCDs, so every sequence's first piece
   // (never empty) goes out first and pieces of one index spread over all
-  // XCDs instead of piling one piece index onto one XCD.
-  const int g = blockIdx.x % a.num_kv_heads, b = blockIdx.x / a.num_kv_heads;
+  // XCDs instead of piling one piece index onto one XCD.  With two pieces
+  // and no more (sequence, kv head) units than compute units (mirror_second),
+  // the second pieces take the units in reverse order: the second-slot
+  // workgroup a compute unit receives then belongs to the mirrored unit, so
+  // in a batch ordered longest first a long sequence's first half shares a
+  // compute unit with a short sequence's tail instead of its own.
   const int split = blockIdx.y;
+  const int ux = (a.mirror_second && split == 1) ? (int)gridDim.x - 1 - (int)blockIdx.x
+                                                 : (int)blockIdx.x;
+  const int g = ux % a.num_kv_heads, b = ux / a.num_kv_heads;
   const int Hq = a.num_q_heads;
   const int QL = MULTI ? a.q_len : 1;
   const int R = G * QL;                                   // query rows of this workgroup

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import paged_kv_attention_09_amd as pa
@@ -25,7 +26,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(HEADERS) == 2 and len(names) == 35, names
+    assert len(HEADERS) == 2 and len(names) == 37, names
     L = pa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -216,6 +217,50 @@ def test_plan_splits():
         assert s == -(-max_tokens // ((c + 63) // 64 * 64))
     assert plan(0, 2, 256, 16, 256) == SHAPE and plan(1, 2, 256, 16, 0) == SHAPE
     assert plan(1, 2, 256, 32, 256) == UNSUP
+
+
+def test_plan_splits_lengths():
+    """The length-aware planner: outside the regime where the (sequence, kv
+    head) units fill more than half and at most all of the compute units it
+    returns pa_decode_plan_splits' choice; inside it, one piece per unit
+    against two pieces with mirrored second pieces, compared by the largest
+    per-compute-unit token count (cases worked by hand below: 8 compute
+    units, block size 256, 16 blocks per table, so two pieces of 2048)."""
+    plan = pa.lib().pa_decode_plan_splits
+    L = lambda *v: np.array(v, np.int32)                                      # noqa: E731
+
+    def lp(lens, hkv, cus, w=16, bs=256):
+        return pa.plan_splits_lengths(lens, hkv, w, bs, cus)
+
+    # 8 units on 8 compute units.  Two long, six short: one piece each puts
+    # 4096 tokens on a compute unit; two pieces put the long heads (2048) on
+    # compute units 0, 1 and the long tails (2048, mirrored to the last
+    # second-piece slots) beside the short heads (512) of units 6, 7: 2560.
+    assert lp(L(4096, 4096, 512, 512, 512, 512, 512, 512), 1, 8) == 2
+    # the same with two kv heads per sequence: units 0, 1 are sequence 0
+    assert lp(L(4096, 512, 512, 512), 2, 8) == 2
+    # four long, four half-length: the long tails land beside half-length
+    # heads (2048 + 2048), no better than a whole long sequence
+    assert lp(L(4096, 4096, 4096, 4096, 2048, 2048, 2048, 2048), 1, 8) == 1
+    # a saving smaller than the merge's 256 tokens: 8 units of 2200 tokens
+    # and the longest 2300 -> heads 2048 beside tails of at most 252
+    assert lp(L(2300, 2200, 2200, 2200, 2200, 2200, 2200, 2200), 1, 8) == 1
+    # 6 units on 8 compute units: the shape-only plan takes two pieces, but
+    # with equal lengths two pieces still put 2048 + 2048 on four compute
+    # units, so one piece each (no merge) is chosen
+    assert plan(6, 1, 16, 256, 8) == 2
+    assert lp(L(*[4096] * 6), 1, 8) == 1
+    # ... and two pieces when the lengths are uneven
+    assert lp(L(4096, 4096, 300, 300, 300, 300), 1, 8) == 2
+    # outside the regime: the shape-only plan, whatever the lengths
+    assert lp(L(*[4096] + [16] * 15), 1, 8) == plan(16, 1, 16, 256, 8) == 1
+    assert lp(L(4096, 16, 16, 16), 1, 8) == plan(4, 1, 16, 256, 8) == 2
+    # lengths beyond the table capacity count as the capacity
+    assert lp(L(9999, 9999, 512, 512, 512, 512, 512, 512), 1, 8) == 2
+    # errors: no lengths, and the shapes pa_decode_plan_splits refuses
+    f = pa.lib().pa_decode_plan_splits_lengths
+    assert f(None, 8, 1, 16, 256, 8) == NULL
+    assert f(P, 0, 1, 16, 256, 8) == SHAPE and f(P, 8, 1, 16, 32, 8) == UNSUP
 
 
 def test_binding_constants_match_header():

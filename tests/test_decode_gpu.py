@@ -301,8 +301,8 @@ def test_binding_workspace_lives_on_the_call_stream(monkeypatch):
     del junk
 
 
-@pytest.mark.parametrize("name,S", [("c3", 0), ("c3", 1), ("c5d", 0), ("c2b8", 7), ("c2b8", 0),
-                                    ("c2b1", 0), ("empty", 4)])
+@pytest.mark.parametrize("name,S", [("c3", 0), ("c3", 1), ("c5d", 0), ("c5d", 2), ("c2b8", 7),
+                                    ("c2b8", 0), ("c2b1", 0), ("empty", 4)])
 def test_fused_append_decode(name, S):
     """append_decode == reshape_and_cache at each sequence's last token followed
     by decode: pools bit-exact against the oracle append, output within
@@ -328,6 +328,27 @@ def test_fused_append_decode(name, S):
     assert np.array_equal(to_bits(case.k_cache), want_k)
     assert np.array_equal(to_bits(case.v_cache), want_v)
     assert_close(to_f64(case.out), case.ref, what=f"fused {name} S={S}")
+
+
+@pytest.mark.parametrize("B", [48, 64])
+@pytest.mark.parametrize("order", ["drawn", "longest first"])
+def test_two_pieces_mirrored_second_pieces(B, order):
+    """Two pieces with no more (sequence, kv head) units than compute units
+    (B x 4 kv heads <= 256): the second pieces go out in mirrored unit order.
+    Random lengths up to the table capacity, so the second pieces of long
+    sequences hold tokens and short sequences have empty ones; the batch as
+    drawn and ordered longest first; S = 2, the automatic count and the
+    length-aware plan."""
+    spec = W.DecodeSpec(f"mirror{B}", B, 28, 4, 128, 16, B * 64 + 16, 64, len_range=(1, 1024),
+                        seed=7100 + B)
+    if order != "drawn":
+        lens = sorted((int(x) for x in W.draw_context_lens(spec)), reverse=True)
+        spec = spec.with_(context_lens=tuple(lens), len_range=None)
+    inp = W.make_decode_inputs(spec)
+    case = DecodeCase(inp)
+    planned = pa.auto_splits_lengths(inp.context_lens, 4, 64, 16, DEV)
+    for S in sorted({2, 0, planned}):
+        assert_close(_run(case, S), case.ref, what=f"B={B} {order} S={S}")
 
 
 def test_workspace_reused_across_calls():

@@ -82,7 +82,7 @@ def case(request):
 
 def test_parity(case):
     name, c = case
-    for S in (1, 3, 0, 64):
+    for S in (1, 2, 3, 0, 64):     # S = 2: second pieces in mirrored unit order
         maxe, rms = assert_close(c.run(S), c.ref, what=f"{name} S={S}")
     print(f"{name}: max abs err {maxe:.3e} rms {rms:.3e}")
 

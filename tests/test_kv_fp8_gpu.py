@@ -156,7 +156,7 @@ def test_decode_fp8_shapes(D, Hq, Hkv, bs):
     k8, v8 = W.fp8_codes_like(inp)
     ks, vs = 0.21, 0.47
     ref = _oracle_fp8(inp, k8, v8, ks, vs)
-    for S in (1, 4, 0):
+    for S in (1, 2, 4, 0):     # S = 2: second pieces in mirrored unit order
         got = to_f64(_run_fp8(inp, k8, v8, ks, vs, S))
         assert_close(got, ref, what=f"D={D} Hq={Hq} Hkv={Hkv} bs={bs} S={S}")
 
