@@ -63,9 +63,11 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["paged_kv_attention_09_amd/csrc/pa_decode.hip",
-                  "paged_kv_attention_09_amd/csrc/pa_device.hpp"]
+                  "paged_kv_attention_09_amd/csrc/pa_device.hpp",
+                  "paged_kv_attention_09_amd/csrc/pa_kernels.hpp"]
 PREFILL_SOURCES = ["paged_kv_attention_09_amd/csrc/pa_prefill.hip",
-                   "paged_kv_attention_09_amd/csrc/pa_device.hpp"]
+                   "paged_kv_attention_09_amd/csrc/pa_device.hpp",
+                   "paged_kv_attention_09_amd/csrc/pa_kernels.hpp"]
 
 
 def parse_args(argv=None):
