@@ -380,6 +380,23 @@ class PrefillWorkload:
             self.append_chunk(r)
         torch.cuda.synchronize()
 
+    def order_decode(self, order, splits: int):
+        """Launch the decode sequences in `order` (host indices) with `splits`
+        pieces: their rows of q, new K/V, tables and lengths permuted, the
+        work unchanged."""
+        import numpy as np
+        import torch
+        pa = self.pa
+        perm = torch.from_numpy(np.asarray(order, np.int64)).to(self.dev)
+        self.dq, self.dk, self.dv = (t[perm].contiguous() for t in (self.dq, self.dk, self.dv))
+        self.dtables = [t[perm].contiguous() for t in self.dtables]
+        self.dlens = self.dlens[np.asarray(order)]
+        self.dlens_t = torch.from_numpy(self.dlens).to(self.dev)
+        self.dS = splits
+        B, Hq, D = (int(x) for x in self.dq.shape)
+        self.dws = torch.zeros(max(pa.decode_workspace_size(B, Hq, D, splits), 256),
+                               dtype=torch.uint8, device=self.dev)
+
     def append_chunk(self, r):
         if self.kv_fp8:
             self.pa.reshape_and_cache_fp8(self.ck, self.cv, self.cslots[r], self.k_cache,
@@ -434,6 +451,7 @@ def time_graph(fn, R: int, steps: int, warmup: int) -> float:
 
 
 def measure_prefill(args, steps, warmup, with_decode: bool, kv_fp8: bool = False):
+    import numpy as np
     import workloads as W
     wl = PrefillWorkload(W.PREFILL_CONFIGS["c5p"], W.CONFIGS["c5d"] if with_decode else None,
                          args.rotate_gib, kv_fp8=kv_fp8)
@@ -453,6 +471,19 @@ def measure_prefill(args, steps, warmup, with_decode: bool, kv_fp8: bool = False
                     "step": ("quantising append of the 512-token chunk, MFMA prefill over fp8 "
                              "pools, fused quantising append + fp8 decode of 64") if kv_fp8 else
                             "append 512-token chunk, MFMA prefill, fused append + decode of 64"})
+        # the same step with the decode batch launched longest first (the block
+        # manager's order: lengths descending, ties in order) and its split
+        # count from the host's lengths in that order
+        dspec = W.CONFIGS["c5d"]
+        order = np.argsort(-wl.dlens.astype(np.int64), kind="stable")
+        S_lf = wl.pa.auto_splits_lengths(wl.dlens[order], dspec.num_kv_heads,
+                                         dspec.max_blocks_per_seq, dspec.block_size, wl.dev)
+        wl.order_decode(order, S_lf)
+        ms_step_lf = time_graph(wl.step, wl.R, steps, warmup)
+        ms_dec_lf = time_graph(wl.decode, wl.R, steps, warmup)
+        rec.update({"longest_first_decode_splits": S_lf,
+                    "longest_first_us_per_step": ms_step_lf * 1e3,
+                    "longest_first_decode_us": ms_dec_lf * 1e3})
     if kv_fp8:
         rec["kv"] = "fp8 e4m3, per-tensor scales"
     return wl, rec
@@ -1650,7 +1681,10 @@ def main(argv=None):
                 msg = "fp8 pools: " + msg
             if name.startswith("c5mix"):
                 msg += (f"; mixed step {rec['us_per_step']:.2f} us (append {rec['append_us']:.2f}, "
-                        f"decode {rec['decode_us']:.2f})")
+                        f"decode {rec['decode_us']:.2f}); decode batch longest first "
+                        f"(S={rec['longest_first_decode_splits']}): step "
+                        f"{rec['longest_first_us_per_step']:.2f} us, decode "
+                        f"{rec['longest_first_decode_us']:.2f} us")
         else:
             wl, rec = measure(name, args, min(args.steps, 100), min(args.warmup, 10))
             msg = (f"{rec['us_per_call']:.2f} us/step, {rec['gbps']:.1f} GB/s; "

@@ -152,6 +152,19 @@ class MixedStep:
         self.pout.fill_(float("nan"))
         self.dout.fill_(float("nan"))
 
+    def order_decode(self, order, splits: int):
+        """Launch the decode sequences in `order` (host indices) with `splits`
+        pieces; the expected decode rows follow the order."""
+        perm = torch.from_numpy(np.asarray(order, np.int64)).to(DEV)
+        self.dq, self.dk, self.dv, self.dtables, self.dlens = (
+            t[perm].contiguous() for t in (self.dq, self.dk, self.dv, self.dtables, self.dlens))
+        self.ref_decode = self.ref_decode[np.asarray(order)]
+        self.dS = splits
+        s = self.m.decode.spec
+        self.dws = torch.empty(max(pa.decode_workspace_size(s.num_seqs, s.num_q_heads,
+                                                            s.head_dim, splits), 256),
+                               dtype=torch.uint8, device=DEV)
+
     def check(self, what: str):
         torch.cuda.synchronize()
         assert _same_bytes(self.k_cache, self.k_want), f"{what}: K pool differs from the oracle"
@@ -198,3 +211,31 @@ def test_mixed_step_graph_replays(mixed):
         got = mixed.check(f"replay {i}")
         assert np.array_equal(got[0], eager[0]) and np.array_equal(got[1], eager[1]), i
     del g
+
+
+def test_mixed_step_decode_longest_first(mixed):
+    """The same step with the decode batch launched longest first (the block
+    manager's order) and its split count from the host's lengths in that
+    order: two pieces with mirrored second pieces for this batch of 64
+    sequences x 4 kv heads on 256 compute units.  Pools bit for bit, rows
+    within tolerance; then back to the drawn order."""
+    d = mixed.m.decode
+    s = d.spec
+    bm = pa.BlockManager(s.num_blocks, s.block_size, s.max_blocks_per_seq, prefix_cache=False)
+    for b, L in enumerate(d.context_lens):
+        bm.admit(b, 0, np.zeros(int(L), np.int32))
+    order = bm.order_longest_first(np.arange(s.num_seqs))
+    del bm
+    assert np.all(np.diff(d.context_lens[order]) <= 0)
+    S = pa.auto_splits_lengths(d.context_lens[order], s.num_kv_heads, s.max_blocks_per_seq,
+                               s.block_size, DEV)
+    saved = (mixed.dq, mixed.dk, mixed.dv, mixed.dtables, mixed.dlens, mixed.ref_decode,
+             mixed.dS, mixed.dws)
+    try:
+        mixed.order_decode(order, S)
+        mixed.reset()
+        mixed.step()
+        mixed.check(f"decode longest first, S={S}")
+    finally:
+        (mixed.dq, mixed.dk, mixed.dv, mixed.dtables, mixed.dlens, mixed.ref_decode, mixed.dS,
+         mixed.dws) = saved
