@@ -1639,6 +1639,8 @@ def main(argv=None):
                 del wl
                 torch.cuda.empty_cache()
                 continue
+            if name not in W.CONFIGS or name in res:
+                continue    # the sweep covers the decode workloads and the prefill chunk
             wl = DecodeWorkload(W.CONFIGS[name], args.rotate_gib, args.splits)
             auto = wl.S
             res[name] = {"auto": auto}
