@@ -350,17 +350,18 @@ int pa_decode_auto_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq
  * balances the work of a compute unit, not of a sequence (split-KV
  * partitioning, zingnex.cn mini-infer thread, feature list item 7; the
  * variable-length batches of continuous batching, MiniInfer README,
- * architecture figure, Scheduler box).  Returns pa_decode_plan_splits' choice except where the
- * (sequence, kv head) units fill more than half and at most all of the
- * num_cus compute units; there it compares one piece per unit with two
- * pieces, whose second pieces pa_decode dispatches in mirrored unit order
- * (unit u's second piece goes out as the (num_seqs * num_kv_heads - 1 - u)-th
- * second-piece workgroup, so a compute unit's second workgroup belongs to the
- * unit mirrored from its first), by the largest number of tokens one compute
- * unit reads, counting the merge launch two pieces add as 256 tokens, and
- * returns 1 or 2.  Lengths beyond the table capacity count as the capacity.
- * Pure host arithmetic; returns PA_ERR_NULL without lengths, or a negative
- * status for the shapes pa_decode_plan_splits refuses. */
+ * architecture figure, Scheduler box).  Returns pa_decode_plan_splits'
+ * choice S0 when its workgroups (num_seqs * num_kv_heads * S0) exceed two per
+ * compute unit.  Otherwise, for every piece count whose workgroups fit two
+ * per compute unit, it predicts the largest number of tokens of one kv head
+ * a compute unit reads -- workgroup s * units + x (piece s of unit x) takes
+ * compute unit (s * units + x) mod num_cus, and when the workgroups exceed
+ * num_cus pa_decode hands the upper half of the pieces (2 s >= S) out in
+ * mirrored unit order (piece s of unit units - 1 - x) -- adds 256 tokens for
+ * the merge launch of any split, and returns the cheapest piece count, S0 on
+ * ties.  Lengths beyond the table capacity count as the capacity.  Pure host
+ * arithmetic; returns PA_ERR_NULL without lengths, or a negative status for
+ * the shapes pa_decode_plan_splits refuses. */
 int pa_decode_plan_splits_lengths(const int32_t *context_lens, int num_seqs, int num_kv_heads,
                                   int max_blocks_per_seq, int block_size, int num_cus);
 

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <vector>
 
 #include "pa_kernels.hpp"
 #include "pagedattn.h"
@@ -53,6 +54,15 @@ int split_len_for(int64_t max_tokens, int num_splits) {
 
 int num_pieces(int64_t max_tokens, int split_len) {
   return (int)((max_tokens + split_len - 1) / split_len);
+}
+
+// Whether a launch of `units` (sequence, kv head) units in `pieces` pieces
+// hands the upper half of its pieces out in mirrored unit order: exactly when
+// its workgroups are more than the compute units and at most two per compute
+// unit, so that the second round of slots exists and is filled in one go.
+int mirrored_launch(int64_t units, int pieces, int num_cus) {
+  const int64_t wgs = units * pieces;
+  return pieces >= 2 && wgs > num_cus && wgs <= 2 * (int64_t)num_cus ? 1 : 0;
 }
 
 constexpr int kMaxDevices = 64;
@@ -216,31 +226,50 @@ int pa_decode_plan_splits_lengths(const int32_t *context_lens, int num_seqs, int
   if (base < 0) return base;
   if (!context_lens) return PA_ERR_NULL;
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  // the one-or-two-pieces regime: the first pieces fill more than half and at
-  // most all of the compute units
-  if (units > num_cus || 2 * units <= num_cus) return base;
+  // several generations of workgroups: the shape-only plan
+  if (units * base > 2 * (int64_t)num_cus) return base;
   const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
-  const int h = split_len_for(max_tokens, 2);
-  if (num_pieces(max_tokens, h) != 2) return base;
   auto len = [&](int64_t u) {
     const int64_t L = context_lens[u / num_kv_heads];
     return L < 0 ? (int64_t)0 : (L > max_tokens ? max_tokens : L);
   };
-  // S = 1: one workgroup per unit, each on its own compute unit.
-  int64_t m1 = 0;
-  for (int64_t u = 0; u < units; u += num_kv_heads) m1 = std::max(m1, len(u));
-  // S = 2: workgroup ids 0 .. units - 1 are the first pieces of units
-  // 0 .. units - 1, ids units + x the second piece of unit units - 1 - x
-  // (mirrored); ids i and i + num_cus share a compute unit (each round of
-  // dispatch gives every compute unit one workgroup, in id order).
-  auto tokens = [&](int64_t id) -> int64_t {
-    if (id < units) return std::min(len(id), (int64_t)h);
-    if (id < 2 * units) return std::max(len(2 * units - 1 - id) - h, (int64_t)0);
-    return 0;
+  // Predicted cost of n pieces: the most tokens of one kv head a compute unit
+  // reads, plus the merge launch when there are pieces.  Workgroup id
+  // s * units + x (piece s of unit x, or of the mirrored unit units - 1 - x
+  // in the upper half of a mirrored launch) takes the compute unit
+  // id mod num_cus: each round of dispatch gives every compute unit one
+  // workgroup, in id order.
+  std::vector<int64_t> load(num_cus);
+  auto cost = [&](int n) {
+    const int h = split_len_for(max_tokens, n);
+    const int mirror = mirrored_launch(units, n, num_cus);
+    std::fill(load.begin(), load.end(), 0);
+    for (int sp = 0; sp < n; ++sp)
+      for (int64_t x = 0; x < units; ++x) {
+        const int64_t u = (mirror && 2 * sp >= n) ? units - 1 - x : x;
+        const int64_t t = std::min(std::max(len(u) - (int64_t)sp * h, (int64_t)0), (int64_t)h);
+        load[(sp * units + x) % num_cus] += t;
+      }
+    return *std::max_element(load.begin(), load.end()) + (n > 1 ? kMergeTokens : 0);
   };
-  int64_t m2 = 0;
-  for (int64_t c = 0; c < num_cus; ++c) m2 = std::max(m2, tokens(c) + tokens(c + num_cus));
-  return m2 + kMergeTokens < m1 ? 2 : 1;
+  // every piece count whose workgroups fit one generation of two per compute
+  // unit; the shape-only plan unless another is predicted cheaper
+  int best = base;
+  int64_t best_cost = cost(base);
+  int last = 0;
+  for (int S = 1; S <= PA_MAX_SPLITS; ++S) {
+    const int n = num_pieces(max_tokens, split_len_for(max_tokens, S));   // non-decreasing in S
+    if (n == last) continue;
+    last = n;
+    if (units * n > 2 * (int64_t)num_cus) break;
+    if (n == base) continue;
+    const int64_t c = cost(n);
+    if (c < best_cost) {
+      best = n;
+      best_cost = c;
+    }
+  }
+  return best;
 }
 
 int pa_decode_auto_splits_lengths(const int32_t *context_lens, int num_seqs, int num_kv_heads,
@@ -314,16 +343,17 @@ int attach_workspace(pa::DecodeArgs *a, int num_seqs, int head_dim, const void *
   return PA_OK;
 }
 
-// The split pass, after every argument check: with two pieces whose first
-// pieces take at most one compute unit each, the second pieces go out in
-// mirrored unit order (see decode_split_kernel).
+// The split pass, after every argument check.  When the workgroups are more
+// than the compute units but fit two to a compute unit (one generation with
+// a second round of slots), the upper half of the pieces goes out in mirrored
+// unit order (see decode_split_kernel).
 int split_launch(pa::DecodeArgs a, int head_dim, int group, int num_seqs, hipStream_t s) {
-  if (a.num_splits == 2) {
+  if (a.num_splits >= 2) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
     const int cus = cu_count(dev);
     if (cus <= 0) return PA_ERR_HIP;
-    a.mirror_second = (int64_t)num_seqs * a.num_kv_heads <= cus ? 1 : 0;
+    a.mirror_second = mirrored_launch((int64_t)num_seqs * a.num_kv_heads, a.num_splits, cus);
   }
   return pa::launch_decode_split(a, head_dim, group, num_seqs, s) == hipSuccess ? PA_OK
                                                                                 : PA_ERR_HIP;

@@ -170,15 +170,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   // Grid: x = (sequence, kv head), y = piece.  Workgroups dispatch in id
   // order and round-robin over the 8 XCDs, so every sequence's first piece
   // (never empty) goes out first and pieces of one index spread over all
-  // XCDs instead of piling one piece index onto one XCD.  With two pieces
-  // and no more (sequence, kv head) units than compute units (mirror_second),
-  // the second pieces take the units in reverse order: the second-slot
-  // workgroup a compute unit receives then belongs to the mirrored unit, so
-  // in a batch ordered longest first a long sequence's first half shares a
-  // compute unit with a short sequence's tail instead of its own.
+  // XCDs instead of piling one piece index onto one XCD.  When the
+  // workgroups are more than the compute units but at most two per compute
+  // unit (mirror_second), the upper half of the pieces takes the units in
+  // reverse order: the second-slot workgroup a compute unit receives then
+  // belongs to the mirrored unit, so in a batch ordered longest first a long
+  // sequence's early pieces share compute units with a short sequence's late
+  // (mostly empty) ones instead of its own.
   const int split = blockIdx.y;
-  const int ux = (a.mirror_second && split == 1) ? (int)gridDim.x - 1 - (int)blockIdx.x
-                                                 : (int)blockIdx.x;
+  const int ux = (a.mirror_second && 2 * split >= a.num_splits)
+                     ? (int)gridDim.x - 1 - (int)blockIdx.x
+                     : (int)blockIdx.x;
   const int g = ux % a.num_kv_heads, b = ux / a.num_kv_heads;
   const int Hq = a.num_q_heads;
   const int QL = MULTI ? a.q_len : 1;

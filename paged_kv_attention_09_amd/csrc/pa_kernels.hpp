@@ -35,7 +35,7 @@ struct DecodeArgs {
   int bs_shift;               // log2(block_size)
   int split_len;              // tokens per split, multiple of 64
   int num_splits;
-  int mirror_second;          // two pieces, units <= compute units: piece 1 takes units in mirrored order
+  int mirror_second;          // upper half of the pieces takes the units in mirrored order
   int q_len;                  // query tokens per sequence (1 = single-token decode)
   int kv_fp8;                 // pools hold fp8 codes, head-major [NB, Hkv, bs, D]
   float v_scale;              // fp8 pools: value of V = code value * v_scale

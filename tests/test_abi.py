@@ -220,41 +220,43 @@ def test_plan_splits():
 
 
 def test_plan_splits_lengths():
-    """The length-aware planner: outside the regime where the (sequence, kv
-    head) units fill more than half and at most all of the compute units it
-    returns pa_decode_plan_splits' choice; inside it, one piece per unit
-    against two pieces with mirrored second pieces, compared by the largest
-    per-compute-unit token count (cases worked by hand below: 8 compute
-    units, block size 256, 16 blocks per table, so two pieces of 2048)."""
+    """The length-aware planner on hand-worked cases: 8 compute units, block
+    size 256, 16 blocks per table (pieces of 4096 / n tokens rounded up to 64).
+    Workgroup s * units + x sits on compute unit (s * units + x) mod 8; with
+    more workgroups than compute units the upper half of the pieces belongs
+    to the mirrored units; a split adds 256 tokens for its merge."""
     plan = pa.lib().pa_decode_plan_splits
     L = lambda *v: np.array(v, np.int32)                                      # noqa: E731
 
     def lp(lens, hkv, cus, w=16, bs=256):
         return pa.plan_splits_lengths(lens, hkv, w, bs, cus)
 
-    # 8 units on 8 compute units.  Two long, six short: one piece each puts
-    # 4096 tokens on a compute unit; two pieces put the long heads (2048) on
-    # compute units 0, 1 and the long tails (2048, mirrored to the last
-    # second-piece slots) beside the short heads (512) of units 6, 7: 2560.
+    # 8 units: 1 piece reads 4096 on one compute unit; 2 pieces (mirrored)
+    # put the long tails (2048) beside the short heads (512) of units 6 and 7:
+    # 2560 + 256
+    assert plan(8, 1, 16, 256, 8) == 1
     assert lp(L(4096, 4096, 512, 512, 512, 512, 512, 512), 1, 8) == 2
-    # the same with two kv heads per sequence: units 0, 1 are sequence 0
-    assert lp(L(4096, 512, 512, 512), 2, 8) == 2
-    # four long, four half-length: the long tails land beside half-length
-    # heads (2048 + 2048), no better than a whole long sequence
+    assert lp(L(4096, 512, 512, 512), 2, 8) == 2          # two kv heads per sequence
+    # the long tails land beside half-length heads: 2048 + 2048 + 256 > 4096
     assert lp(L(4096, 4096, 4096, 4096, 2048, 2048, 2048, 2048), 1, 8) == 1
-    # a saving smaller than the merge's 256 tokens: 8 units of 2200 tokens
-    # and the longest 2300 -> heads 2048 beside tails of at most 252
+    # a saving below the merge's 256 tokens: heads 2048 beside tails <= 252
     assert lp(L(2300, 2200, 2200, 2200, 2200, 2200, 2200, 2200), 1, 8) == 1
-    # 6 units on 8 compute units: the shape-only plan takes two pieces, but
-    # with equal lengths two pieces still put 2048 + 2048 on four compute
-    # units, so one piece each (no merge) is chosen
+    # 6 units, equal lengths: the shape-only plan takes 2 pieces, but they put
+    # 2048 + 2048 on four compute units (+ 256), more than one piece each
     assert plan(6, 1, 16, 256, 8) == 2
     assert lp(L(*[4096] * 6), 1, 8) == 1
-    # ... and two pieces when the lengths are uneven
+    # ... and 2 pieces when the lengths are uneven: 300 + 2048 + 256
     assert lp(L(4096, 4096, 300, 300, 300, 300), 1, 8) == 2
-    # outside the regime: the shape-only plan, whatever the lengths
-    assert lp(L(*[4096] + [16] * 15), 1, 8) == plan(16, 1, 16, 256, 8) == 1
-    assert lp(L(4096, 16, 16, 16), 1, 8) == plan(4, 1, 16, 256, 8) == 2
+    # 4 units, one long: 4 pieces of 1024 (16 workgroups, pieces 2 and 3
+    # mirrored) put at most 16 + 1024 on a compute unit, + 256 = 1296; 3
+    # pieces of 1408 give 1408 + 256, 2 pieces 2048 + 256, 1 piece 4096
+    assert plan(4, 1, 16, 256, 8) == 2
+    assert lp(L(4096, 16, 16, 16), 1, 8) == 4
+    # the same lengths without the long one: every plan reads at most 16
+    # tokens on a compute unit, so no split and no merge
+    assert lp(L(16, 16, 16, 16), 1, 8) == 1
+    # workgroups of the shape-only plan beyond two per compute unit: that plan
+    assert lp(L(*[4096] + [16] * 23), 1, 8) == plan(24, 1, 16, 256, 8) == 1
     # lengths beyond the table capacity count as the capacity
     assert lp(L(9999, 9999, 512, 512, 512, 512, 512, 512), 1, 8) == 2
     # errors: no lengths, and the shapes pa_decode_plan_splits refuses
