@@ -330,15 +330,16 @@ def test_fused_append_decode(name, S):
     assert_close(to_f64(case.out), case.ref, what=f"fused {name} S={S}")
 
 
-@pytest.mark.parametrize("B", [48, 64])
+@pytest.mark.parametrize("B,splits", [(24, (3, 4)), (48, (2,)), (64, (2,))])
 @pytest.mark.parametrize("order", ["drawn", "longest first"])
-def test_two_pieces_mirrored_second_pieces(B, order):
-    """Two pieces with no more (sequence, kv head) units than compute units
-    (B x 4 kv heads <= 256): the second pieces go out in mirrored unit order.
-    Random lengths up to the table capacity, so the second pieces of long
-    sequences hold tokens and short sequences have empty ones; the batch as
-    drawn and ordered longest first; S = 2, the automatic count and the
-    length-aware plan."""
+def test_mirrored_upper_pieces(B, splits, order):
+    """Launches whose workgroups exceed the 256 compute units but fit two to
+    a compute unit hand the upper half of their pieces (2 s >= S) out in
+    mirrored unit order: B sequences x 4 kv heads at S pieces (24 x 4 at S = 3
+    and 4, pieces 2 and 3 mirrored; 48 and 64 x 4 at S = 2).  Random lengths
+    up to the table capacity, so late pieces of long sequences hold tokens
+    and those of short ones are empty; the batch as drawn and ordered longest
+    first; also the automatic count and the length-aware plan."""
     spec = W.DecodeSpec(f"mirror{B}", B, 28, 4, 128, 16, B * 64 + 16, 64, len_range=(1, 1024),
                         seed=7100 + B)
     if order != "drawn":
@@ -347,7 +348,7 @@ def test_two_pieces_mirrored_second_pieces(B, order):
     inp = W.make_decode_inputs(spec)
     case = DecodeCase(inp)
     planned = pa.auto_splits_lengths(inp.context_lens, 4, 64, 16, DEV)
-    for S in sorted({2, 0, planned}):
+    for S in sorted(set(splits) | {0, planned}):
         assert_close(_run(case, S), case.ref, what=f"B={B} {order} S={S}")
 
 
