@@ -1183,11 +1183,18 @@ def cpu_baseline(spec, seconds: float):
         procs.append(subprocess.Popen([sys.executable, "-c", code], cwd=ROOT, env=env,
                                       stdout=subprocess.PIPE, text=True))
     res = []
-    for p in procs:
-        out, _ = p.communicate()
-        if p.returncode != 0:
-            raise RuntimeError(f"oracle worker failed with status {p.returncode}")
-        res.append(json.loads(out.strip().splitlines()[-1]))
+    try:
+        for p in procs:
+            out, _ = p.communicate()
+            if p.returncode != 0:
+                raise RuntimeError(f"oracle worker failed with status {p.returncode}")
+            res.append(json.loads(out.strip().splitlines()[-1]))
+    finally:
+        # no worker outlives the call, also when one of them failed
+        for p in procs:
+            if p.poll() is None:
+                p.kill()
+                p.wait()
     total = sum(r["bytes"] for r in res)
     wall = max(r["seconds"] for r in res)
     rec = {"value": round(total / wall / 1e9, 4), "unit": "GB/s", "cores": workers,
