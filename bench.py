@@ -1235,6 +1235,7 @@ def measure(name, args, steps, warmup, with_kernel=True):
         rec["kernel_avg_us"] = avg * 1e3
         rec["kernel_gbps"] = wl.decode_bytes / (avg * 1e-3) / 1e9
     if spec.len_range is not None:
+        rec.update(measure_drawn_order_planned(wl, steps, warmup))
         rec.update(measure_longest_first(wl, steps, warmup))
     return wl, rec
 
@@ -1353,6 +1354,27 @@ def longest_first_order(wl):
     order = bm.order_longest_first(np.arange(B))
     del bm
     return torch.from_numpy(order).to(wl.dev)
+
+
+def measure_drawn_order_planned(wl, steps, warmup):
+    """The batch in its drawn order at the split count planned from the
+    host's lengths (pa_decode_auto_splits_lengths) instead of the shape-only
+    automatic count; timed only where the two counts differ."""
+    spec = wl.spec
+    S_d = wl.pa.auto_splits_lengths(wl.lens_np, spec.num_kv_heads, spec.max_blocks_per_seq,
+                                    spec.block_size, wl.dev)
+    rec = {"lengths_planned_splits": S_d}
+    if S_d == wl.S:
+        return rec
+    S0 = wl.S
+    wl.set_splits(S_d)
+    ms_step, _ = time_steps_graph(wl, steps, warmup)
+    avg = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
+    wl.set_splits(S0)
+    rec.update({"lengths_planned_us_per_call": ms_step * 1e3,
+                "lengths_planned_kernel_us": avg * 1e3,
+                "lengths_planned_kernel_gbps": wl.decode_bytes / (avg * 1e-3) / 1e9})
+    return rec
 
 
 def measure_longest_first(wl, steps, warmup):
@@ -1702,6 +1724,10 @@ def main(argv=None):
                    f"kernel {rec['kernel_avg_us']:.2f} us ({rec['kernel_gbps']:.0f} GB/s); "
                    f"eager {rec['eager_us_per_step']:.2f} us (graph saves "
                    f"{100 * rec['graph_saving']:.0f}%)")
+            if "lengths_planned_us_per_call" in rec:
+                msg += (f"; drawn order at S = {rec['lengths_planned_splits']} from the lengths "
+                        f"{rec['lengths_planned_us_per_call']:.2f} us/step, kernel "
+                        f"{rec['lengths_planned_kernel_us']:.2f} us")
             if "longest_first_us_per_call" in rec:
                 msg += (f"; longest first {rec['longest_first_us_per_call']:.2f} us/step, kernel "
                         f"{rec['longest_first_kernel_us']:.2f} us "

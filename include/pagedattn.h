@@ -360,8 +360,9 @@ int pa_decode_auto_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq
  * mirrored unit order (piece s of unit units - 1 - x) -- adds 256 tokens for
  * the merge launch of any split, and returns the cheapest piece count, S0 on
  * ties.  Lengths beyond the table capacity count as the capacity.  Pure host
- * arithmetic; returns PA_ERR_NULL without lengths, or a negative status for
- * the shapes pa_decode_plan_splits refuses. */
+ * arithmetic; returns PA_ERR_NULL without lengths, PA_ERR_SHAPE for
+ * num_cus > 65536, or a negative status for the shapes pa_decode_plan_splits
+ * refuses. */
 int pa_decode_plan_splits_lengths(const int32_t *context_lens, int num_seqs, int num_kv_heads,
                                   int max_blocks_per_seq, int block_size, int num_cus);
 

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <new>
 #include <vector>
 
 #include "pa_kernels.hpp"
@@ -218,6 +219,9 @@ int pa_decode_auto_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq
 // unit takes to read this many tokens of one kv head at the decode's rate
 // (measured: ≈ 4 µs against ≈ 60 tokens per µs per compute unit).
 constexpr int64_t kMergeTokens = 256;
+// Largest compute-unit count the length-aware planner models (its per-unit
+// table is one int64 per compute unit).
+constexpr int kMaxPlanCus = 1 << 16;
 
 int pa_decode_plan_splits_lengths(const int32_t *context_lens, int num_seqs, int num_kv_heads,
                                   int max_blocks_per_seq, int block_size, int num_cus) {
@@ -225,6 +229,7 @@ int pa_decode_plan_splits_lengths(const int32_t *context_lens, int num_seqs, int
       pa_decode_plan_splits(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, num_cus);
   if (base < 0) return base;
   if (!context_lens) return PA_ERR_NULL;
+  if (num_cus > kMaxPlanCus) return PA_ERR_SHAPE;
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
   // several generations of workgroups: the shape-only plan
   if (units * base > 2 * (int64_t)num_cus) return base;
@@ -239,7 +244,14 @@ int pa_decode_plan_splits_lengths(const int32_t *context_lens, int num_seqs, int
   // in the upper half of a mirrored launch) takes the compute unit
   // id mod num_cus: each round of dispatch gives every compute unit one
   // workgroup, in id order.
-  std::vector<int64_t> load(num_cus);
+  // no exception crosses the C ABI: without memory for the table, the
+  // shape-only plan
+  std::vector<int64_t> load;
+  try {
+    load.resize(num_cus);
+  } catch (const std::bad_alloc &) {
+    return base;
+  }
   auto cost = [&](int n) {
     const int h = split_len_for(max_tokens, n);
     const int mirror = mirrored_launch(units, n, num_cus);

@@ -263,6 +263,10 @@ def test_plan_splits_lengths():
     f = pa.lib().pa_decode_plan_splits_lengths
     assert f(None, 8, 1, 16, 256, 8) == NULL
     assert f(P, 0, 1, 16, 256, 8) == SHAPE and f(P, 8, 1, 16, 32, 8) == UNSUP
+    # a compute-unit count beyond what the planner models
+    lens = L(4096, 512)
+    ptr = lens.ctypes.data_as(ctypes.c_void_p)
+    assert f(ptr, 2, 1, 16, 256, 1 << 16) >= 1 and f(ptr, 2, 1, 16, 256, (1 << 16) + 1) == SHAPE
 
 
 def test_binding_constants_match_header():
