@@ -11,9 +11,11 @@
 //    tile staged in LDS serves all G heads.  Long key ranges are cut into
 //    pieces handled by separate workgroups (the same split-KV scheme as
 //    decode) and merged by log-sum-exp afterwards.
-//  * Key tiles of 64 rows stream into LDS by global_load_lds_dwordx4, four
-//    stages deep (three tiles in flight while one is computed; three stages
-//    for the one shape whose DMA count would overflow the wait counter).  K rows are
+//  * Key tiles of 64 rows stream into LDS by global_load_lds_dwordx4 in
+//    pairs, four tile buffers: while one pair is computed the next is in
+//    flight, and one barrier per pair publishes it and frees the buffers of
+//    the pair before (where two tiles' DMAs would overflow the wait counter:
+//    three buffers, two tiles in flight, one barrier per tile).  K rows are
 //    stored with their 16-byte chunks XOR swizzled by row, V rows with their
 //    32-byte column pairs swizzled, so the reads below hit distinct banks.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K fragments (keys x head_dim)
@@ -116,9 +118,9 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   constexpr int NDMA = TILEK / 1024;              // DMA instructions per tensor per tile
   constexpr int RPD = 1024 / RB;                  // rows per DMA instruction
   static_assert(RPD <= 16, "a DMA instruction stays inside one 16-row group");
-  // NST tile buffers: NST - 1 tiles in flight while one is computed.  The
-  // DMAs of a tile are issued by NI waves (a power of two), NPW instructions
-  // each, so every issuing wave waits on a fixed count per tile.
+  // NST tile buffers.  The DMAs of a tile are issued by NI waves (a power of
+  // two), NPW instructions each, so every issuing wave waits on a fixed count
+  // per tile.
   constexpr int NI = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
   constexpr int NPW = 2 * NDMA / NI;
   // as many stages (up to four) as kTileLds holds, fewer where the DMA
@@ -128,6 +130,10 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   constexpr int NSTL = STL < 4 ? STL : 4;
   constexpr int NST = (NSTL - 2) * NPW <= 63 ? NSTL : 3;
   static_assert(NST >= 2 && (NST - 2) * NPW <= 63, "stages and vmcnt range");
+  // Four buffers: tiles go in pairs, one barrier per pair (the pair in
+  // flight, 2 NPW DMAs per wave, fits the wait counter).  Otherwise one
+  // barrier per tile with NST - 1 tiles in flight.
+  constexpr bool PAIRS = NST == 4;
   __shared__ __attribute__((aligned(1024))) char smem[NST][2][TILEK];  // [stage][K, V]
 
   const int lane = threadIdx.x & 63;
@@ -230,15 +236,28 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
   };
 
   const int ntiles = (kend - kbeg + kKeys - 1) / kKeys;
-  int blk[KG];
+  // blk: block ids of the next tile to issue; blk2 (pairs): of the one after
+  int blk[KG], blk2[KG];
+  if constexpr (PAIRS) {
 #pragma unroll
-  for (int t = 0; t < NST - 1; ++t) {
-    if (t < ntiles) {
-      tile_blocks(kbeg + t * kKeys, blk);
-      issue_tile(kbeg + t * kKeys, t, blk);
+    for (int t = 0; t < 2; ++t) {
+      if (t < ntiles) {
+        tile_blocks(kbeg + t * kKeys, blk);
+        issue_tile(kbeg + t * kKeys, t, blk);
+      }
     }
+    if (ntiles > 2) tile_blocks(kbeg + 2 * kKeys, blk);     // the second pair
+    if (ntiles > 3) tile_blocks(kbeg + 3 * kKeys, blk2);
+  } else {
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t) {
+      if (t < ntiles) {
+        tile_blocks(kbeg + t * kKeys, blk);
+        issue_tile(kbeg + t * kKeys, t, blk);
+      }
+    }
+    if (ntiles > NST - 1) tile_blocks(kbeg + (NST - 1) * kKeys, blk);   // for tile NST - 1
   }
-  if (ntiles > NST - 1) tile_blocks(kbeg + (NST - 1) * kKeys, blk);   // for tile NST - 1
 
   float m[2] = {-INFINITY, -INFINITY};
   f32x4 o[DB][2];
@@ -271,16 +290,30 @@ __global__ __launch_bounds__(64 * G) void prefill_kernel(PrefillArgs a) {
                     : tr_row * ROWB + v_pos<D>(2 * db + ((c16 & 3) >> 1), tr_row) * 16 + (c16 & 1) * 8;
 
   for (int it = 0; it < ntiles; ++it) {
-    // this wave's DMAs of tile it are done when at most those of the tiles
-    // issued after it (up to NST - 2) are outstanding; the barrier then
-    // publishes everyone's tile it and retires all reads of the stage that
-    // tile it + NST - 1 is about to overwrite (it held tile it - 1).
-    wait_vmcnt_steps<NPW, NST - 2>(min(NST - 2, ntiles - 1 - it));
-    __syncthreads();
     const int kt0 = kbeg + it * kKeys;
-    if (it + NST - 1 < ntiles) {
-      issue_tile(kt0 + (NST - 1) * kKeys, (it + NST - 1) % NST, blk);
-      if (it + NST < ntiles) tile_blocks(kt0 + NST * kKeys, blk);   // consumed next iteration
+    if constexpr (PAIRS) {
+      if ((it & 1) == 0) {
+        // the pair (it, it + 1) is the only one in flight: once this wave's
+        // DMAs are done, the barrier publishes everyone's and retires all
+        // reads of the pair before, whose buffers the next pair takes
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (it + 2 < ntiles) issue_tile(kt0 + 2 * kKeys, (it + 2) & 3, blk);
+        if (it + 3 < ntiles) issue_tile(kt0 + 3 * kKeys, (it + 3) & 3, blk2);
+        if (it + 4 < ntiles) tile_blocks(kt0 + 4 * kKeys, blk);    // consumed at the next pair
+        if (it + 5 < ntiles) tile_blocks(kt0 + 5 * kKeys, blk2);
+      }
+    } else {
+      // this wave's DMAs of tile it are done when at most those of the tiles
+      // issued after it (up to NST - 2) are outstanding; the barrier then
+      // publishes everyone's tile it and retires all reads of the stage that
+      // tile it + NST - 1 is about to overwrite (it held tile it - 1).
+      wait_vmcnt_steps<NPW, NST - 2>(min(NST - 2, ntiles - 1 - it));
+      __syncthreads();
+      if (it + NST - 1 < ntiles) {
+        issue_tile(kt0 + (NST - 1) * kKeys, (it + NST - 1) % NST, blk);
+        if (it + NST < ntiles) tile_blocks(kt0 + NST * kKeys, blk);   // consumed next iteration
+      }
     }
     const char *Kt = smem[it % NST][0];
     const char *Vt = smem[it % NST][1];
