@@ -68,6 +68,9 @@ KERNEL_SOURCES = ["paged_kv_attention_09_amd/csrc/pa_decode.hip",
 PREFILL_SOURCES = ["paged_kv_attention_09_amd/csrc/pa_prefill.hip",
                    "paged_kv_attention_09_amd/csrc/pa_device.hpp",
                    "paged_kv_attention_09_amd/csrc/pa_kernels.hpp"]
+# a mixed step runs the append, prefill and decode kernels
+MIXED_SOURCES = KERNEL_SOURCES + ["paged_kv_attention_09_amd/csrc/pa_prefill.hip",
+                                  "paged_kv_attention_09_amd/csrc/pa_append.hip"]
 
 
 def parse_args(argv=None):
@@ -707,7 +710,8 @@ def ingest_trace(directory: str, out_name: str, command: str):
     for r in _read_csv(directory, "kernel_trace.csv"):
         k = _short_kernel(r["Kernel_Name"])
         durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    srcs = PREFILL_SOURCES if "prefill" in out_name else KERNEL_SOURCES
+    srcs = (MIXED_SOURCES if "mixed" in out_name else
+            PREFILL_SOURCES if "prefill" in out_name else KERNEL_SOURCES)
     src_hash = kernel_source_hash(srcs)
     lines = [f"# Kernel durations: {out_name}", "", "Command (run from /tmp with TMPDIR=/tmp):", "",
              "```", command, "```", "",
