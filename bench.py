@@ -6,7 +6,7 @@ K/V row at its last token's slot and run the paged split-KV decode over the
 whole context (pa_append_decode: the append fused into the split pass, then
 the log-sum-exp merge).  The same step as separate calls
 (pa_reshape_and_cache, then pa_decode) is timed too and reported as
-config.unfused_us_per_step.
+config.unfused_graph_us_per_step.
 
 Default workload: 12 q / 2 kv heads (Qwen2.5-1.5B attention shape), head_dim
 128, block_size 16, batch 8, every context 4096 tokens, bf16, automatic split
@@ -16,11 +16,18 @@ seed; block tables are random permutations of a shuffled pool.
 Method
   * Cold HBM: steps rotate over R disjoint sets of blocks (at least
     --rotate-gib GiB of K/V between two uses of the same block), so no call
-    finds its K/V in the 256 MB last-level cache.
-  * The K timed steps are captured once into a HIP graph and replayed
-    between two events, with torch.cuda.synchronize() on both sides, the
-    queue primed by a device-side sleep so that the graph launch's host time
-    is spent while the GPU sleeps: the events bracket the K steps' GPU work.
+    finds its K/V in the 256 MB last-level cache; the timed steps continue
+    the rotation where the warm-up stopped.  Building the inputs ends with
+    one read of every rotation, so timed steps meet warm address
+    translations, as in a running engine, and not first touches.
+  * The K timed steps are issued from the host through the C ABI
+    (pa_append_decode with prebuilt arguments) between two events, with
+    torch.cuda.synchronize() on both sides, the queue primed by a device-side
+    sleep so that the host's enqueue time is spent while the GPU sleeps: the
+    events bracket the K steps' GPU work (the host issues a step in less time
+    than the GPU runs it).  The same K steps captured into one HIP graph and
+    replayed are reported beside (config.graph_us_per_step); a replay adds a
+    fixed cost of several microseconds, which few steps do not amortise.
   * The dominant kernel (the split-KV pass) is timed with HIP events around
     back-to-back launches on the current stream, the queue primed by a
     device-side sleep so the events bracket GPU work and not host gaps.
@@ -61,6 +68,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# steps timed, and warm-up steps, per extra workload (every workload but the
+# headline one), whatever --steps and --warmup are: a replayed graph's fixed
+# cost spread over this many steps is small
+EXTRA_STEPS = 100
+EXTRA_WARMUP = 20
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["paged_kv_attention_09_amd/csrc/pa_decode.hip",
                   "paged_kv_attention_09_amd/csrc/pa_device.hpp",
@@ -210,6 +222,22 @@ class DecodeWorkload:
             self.decode_bytes -= int(self.lens_np.sum()) * Hkv * D * 2
         self.append_bytes = B * Hkv * D * 2 * 2 * 2 + B * 8
         self.decode_flop = 4 * D * Hq * int(self.lens_np.sum())
+        self.read_every_rotation()
+
+    def read_every_rotation(self):
+        """Part of making the inputs resident: one read of every rotation's
+        blocks through its tables (a decode of the workload's kind without
+        the append, which writes only the output and the workspace), so that
+        timed steps meet the address translations a running engine has
+        rather than first touches."""
+        import torch
+        if self.q_len > 1:
+            read = self.step_multi_fp8 if self.kv_fp8 else self.step_multi
+        else:
+            read = self.step_fp8 if self.kv_fp8 else self.kernel
+        for r in range(self.R):
+            read(r)
+        torch.cuda.synchronize()
 
     def set_splits(self, S: int):
         import torch
@@ -378,9 +406,15 @@ class PrefillWorkload:
             if kv_fp8:
                 self.decode_bytes -= int(self.dlens.sum()) * Hkv * D * 2
         self.B = B
-        # the chunk's K/V must be in the pool before any prefill-only timing
+        # the chunk's K/V must be in the pool before any prefill-only timing;
+        # then one read of every rotation (prefill, and the decode, whose
+        # fused append rewrites the same rows), as for the decode workloads
         for r in range(self.R):
             self.append_chunk(r)
+        for r in range(self.R):
+            self.prefill(r)
+            if self.B:
+                self.decode(r)
         torch.cuda.synchronize()
 
     def order_decode(self, order, splits: int):
@@ -437,8 +471,9 @@ class PrefillWorkload:
 
 
 def time_graph(fn, R: int, steps: int, warmup: int) -> float:
-    """Average milliseconds of fn(i % R) over `steps` calls captured in one
-    HIP graph (after `warmup` eager calls)."""
+    """Average milliseconds per call of `steps` calls fn(r) captured in one
+    HIP graph after `warmup` eager calls, r running over the R rotations
+    without restarting (the timed calls continue where the warm-up stopped)."""
     import torch
     for i in range(warmup):
         fn(i % R)
@@ -446,7 +481,7 @@ def time_graph(fn, R: int, steps: int, warmup: int) -> float:
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(steps):
-            fn(i % R)
+            fn((warmup + i) % R)      # the rotation continues after the warm-up
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
@@ -542,7 +577,7 @@ def time_kernel_events(fn, n: int, rotations: int):
     torch.cuda._sleep(cyc)
     s.record()
     for i in range(n):
-        fn(i % rotations)
+        fn((1 + i) % rotations)
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / n
@@ -573,7 +608,7 @@ def time_steps_eager(wl, steps: int, warmup: int) -> float:
     def issue():
         t0 = time.perf_counter()
         for i in range(steps):
-            f(*args[i % wl.R])
+            f(*args[(warmup + i) % wl.R])      # the rotation continues after the warm-up
         host[0] = time.perf_counter() - t0
 
     ms = primed_events(issue)
@@ -670,7 +705,7 @@ def time_steps_graph(wl, steps: int, warmup: int, fused: bool = True):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(steps):
-            step(i % wl.R)
+            step((warmup + i) % wl.R)      # the rotation continues after the warm-up
     torch.cuda.synchronize()
     g.replay()          # first replay uploads the graph
     torch.cuda.synchronize()
@@ -1221,15 +1256,20 @@ def measure(name, args, steps, warmup, with_kernel=True):
     import workloads as W
     spec = W.CONFIGS[name]
     wl = DecodeWorkload(spec, args.rotate_gib, args.splits)
-    ms_step, wall = time_steps_graph(wl, steps, warmup)
+    # the step issued through the C ABI from the host, exactly `steps` of them
+    # between two events (the queue primed so the host's enqueue time stays
+    # outside); the same steps replayed from one HIP graph are reported beside
+    ms_step, _ = time_steps_eager(wl, steps, warmup)
     bytes_step = wl.decode_bytes + wl.append_bytes
-    rec = {"workload": spec.name, "key": name, "ms_per_step": ms_step, "wall_s": wall,
+    rec = {"workload": spec.name, "key": name, "ms_per_step": ms_step,
            "gbps": bytes_step / (ms_step * 1e-3) / 1e9,
            "us_per_call": ms_step * 1e3, "splits": wl.S, "rotations": wl.R,
            "decode_bytes": wl.decode_bytes, "append_bytes": wl.append_bytes,
            "context_tokens": int(wl.lens_np.sum())}
+    ms_graph, _ = time_steps_graph(wl, steps, 2)
+    rec["graph_us_per_step"] = ms_graph * 1e3
     ms_unfused, _ = time_steps_graph(wl, steps, 2, fused=False)
-    rec["unfused_us_per_step"] = ms_unfused * 1e3
+    rec["unfused_graph_us_per_step"] = ms_unfused * 1e3
     # graph against eager issue: two adjacent (eager, graph) pairs, so that a
     # drift of the GPU's pace between legs timed apart does not enter the
     # comparison
@@ -1282,7 +1322,7 @@ def measure_split_gain(args, steps, warmup):
         row = {"workload": W.CONFIGS[name].name, "auto_splits": auto}
         for label, S in (("auto", auto), ("s1", 1)):
             wl.set_splits(S)
-            ms_step, _ = time_steps_graph(wl, steps, warmup)
+            ms_step, _ = time_steps_eager(wl, steps, warmup)
             ms_k = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
             row[f"{label}_step_us"] = round(ms_step * 1e3, 3)
             row[f"{label}_kernel_us"] = round(ms_k * 1e3, 3)
@@ -1327,7 +1367,7 @@ def measure_equal_share(args, others, steps, warmup):
         eq = spec.with_(num_seqs=n, context_lens=equal_share_lens(total, n), len_range=None,
                         num_blocks=max(spec.num_blocks, n * spec.max_blocks_per_seq))
         wl = DecodeWorkload(eq, args.rotate_gib, 1)
-        ms_step, _ = time_steps_graph(wl, steps, warmup)
+        ms_step, _ = time_steps_eager(wl, steps, warmup)
         ms_k = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
         drawn = others[name]
         # the library's best for the drawn lengths: the drawn order at the
@@ -1381,7 +1421,7 @@ def measure_drawn_order_planned(wl, steps, warmup):
         return rec
     S0 = wl.S
     wl.set_splits(S_d)
-    ms_step, _ = time_steps_graph(wl, steps, warmup)
+    ms_step, _ = time_steps_eager(wl, steps, warmup)
     avg = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
     wl.set_splits(S0)
     rec.update({"lengths_planned_us_per_call": ms_step * 1e3,
@@ -1403,7 +1443,7 @@ def measure_longest_first(wl, steps, warmup):
     S_lf = wl.pa.auto_splits_lengths(wl.lens_np[perm.cpu().numpy()], spec.num_kv_heads,
                                      spec.max_blocks_per_seq, spec.block_size, wl.dev)
     wl.set_splits(S_lf)
-    ms_step, _ = time_steps_graph(wl, steps, warmup)
+    ms_step, _ = time_steps_eager(wl, steps, warmup)
     avg = time_kernel_events(wl.kernel, min(200, max(50, steps)), wl.R)
     wl.tables, wl.lens = saved[:2]
     wl.set_splits(saved[2])
@@ -1688,7 +1728,7 @@ def main(argv=None):
             res[name] = {"auto": auto}
             for S in [int(x) for x in args.sweep_splits.split(",")]:
                 wl.set_splits(S)
-                ms, _ = time_steps_graph(wl, min(args.steps, 100), 3)
+                ms, _ = time_steps_eager(wl, min(args.steps, 100), 3)
                 res[name][S] = round(ms * 1e3, 2)
                 print(f"[sweep] {name} S={S}: {ms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
             del wl
@@ -1699,7 +1739,8 @@ def main(argv=None):
     print(f"[bench] {args.workload}: building inputs", file=sys.stderr, flush=True)
     wl, main_rec = measure(args.workload, args, args.steps, args.warmup)
     print(f"[bench] {args.workload}: {main_rec['us_per_call']:.2f} us/step, "
-          f"{main_rec['gbps']:.1f} GB/s; kernel {main_rec['kernel_avg_us']:.2f} us; eager "
+          f"{main_rec['gbps']:.1f} GB/s (graph replay {main_rec['graph_us_per_step']:.2f} us); "
+          f"kernel {main_rec['kernel_avg_us']:.2f} us; eager "
           f"{main_rec['eager_us_per_step']:.2f} us against graph "
           f"{main_rec['graph_us_per_step_paired']:.2f} us in adjacent pairs (graph saves "
           f"{100 * main_rec['graph_saving']:.1f}%, host issue "
@@ -1709,18 +1750,18 @@ def main(argv=None):
         del wl
         torch.cuda.empty_cache()
         if name in FP8_WORKLOADS:
-            wl, rec = measure_fp8(name, args, min(args.steps, 100), min(args.warmup, 10))
+            wl, rec = measure_fp8(name, args, EXTRA_STEPS, EXTRA_WARMUP)
             msg = (f"fp8 pools: {rec['us_per_call']:.2f} us/call, {rec['gbps']:.1f} GB/s; bf16 "
                    f"{rec['bf16_us_per_call']:.2f} us (x{rec['speedup_over_bf16']:.2f})")
             if "longest_first_us_per_call" in rec:
                 msg += f"; longest first {rec['longest_first_us_per_call']:.2f} us"
         elif name in MULTI_WORKLOADS:
-            wl, rec = measure_multi(name, args, min(args.steps, 100), min(args.warmup, 10))
+            wl, rec = measure_multi(name, args, EXTRA_STEPS, EXTRA_WARMUP)
             msg = (f"q_len {rec['q_len']}: {rec['us_per_call']:.2f} us/call, {rec['gbps']:.1f} GB/s;"
                    f" single-token {rec['single_token_us_per_call']:.2f} us "
                    f"(x{rec['ratio_to_single_token']:.2f})")
         elif name in ("c5p", "c5mix", "c5pf8", "c5mixf8"):
-            wl, rec = measure_prefill(args, min(args.steps, 50), min(args.warmup, 5),
+            wl, rec = measure_prefill(args, EXTRA_STEPS // 2, EXTRA_WARMUP,
                                       with_decode=name.startswith("c5mix"),
                                       kv_fp8=name.endswith("f8"))
             msg = f"prefill {rec['prefill_us']:.2f} us ({rec['prefill_tflops']:.0f} TFLOP/s)"
@@ -1733,7 +1774,7 @@ def main(argv=None):
                         f"{rec['longest_first_us_per_step']:.2f} us, decode "
                         f"{rec['longest_first_decode_us']:.2f} us")
         else:
-            wl, rec = measure(name, args, min(args.steps, 100), min(args.warmup, 10))
+            wl, rec = measure(name, args, EXTRA_STEPS, EXTRA_WARMUP)
             msg = (f"{rec['us_per_call']:.2f} us/step, {rec['gbps']:.1f} GB/s; "
                    f"kernel {rec['kernel_avg_us']:.2f} us ({rec['kernel_gbps']:.0f} GB/s); "
                    f"eager {rec['eager_us_per_step']:.2f} us against graph "
@@ -1751,8 +1792,8 @@ def main(argv=None):
                         if k not in ("wall_s",)}
         print(f"[bench] {name}: {msg}", file=sys.stderr, flush=True)
 
-    split_gain = measure_split_gain(args, min(args.steps, 100), min(args.warmup, 10))
-    equal_share = measure_equal_share(args, others, min(args.steps, 100), min(args.warmup, 10))
+    split_gain = measure_split_gain(args, EXTRA_STEPS, EXTRA_WARMUP)
+    equal_share = measure_equal_share(args, others, EXTRA_STEPS, EXTRA_WARMUP)
     multilayer = measure_multilayer(args)
     bm_rec = measure_block_manager()
     print(f"[bench] block manager: decode step {bm_rec['decode_step_us_256_seqs']:.1f} us, "
@@ -1794,12 +1835,15 @@ def main(argv=None):
                    "head_dim": spec.head_dim, "block_size": spec.block_size,
                    "context_tokens": main_rec["context_tokens"], "num_splits": main_rec["splits"],
                    "rotations": main_rec["rotations"], "step": "append fused into split-KV decode, then merge",
-                   "unfused_us_per_step": round(main_rec["unfused_us_per_step"], 3),
+                   "graph_us_per_step": round(main_rec["graph_us_per_step"], 3),
+                   "unfused_graph_us_per_step": round(main_rec["unfused_graph_us_per_step"], 3),
                    "eager_us_per_step": round(main_rec["eager_us_per_step"], 3),
                    "graph_us_per_step_paired": round(main_rec["graph_us_per_step_paired"], 3),
                    "host_issue_us_per_call": round(main_rec["host_issue_us_per_call"], 3),
-                   "timing": "HIP graph of the timed steps between HIP events; kernel: HIP "
-                             "events around back-to-back launches behind a primed queue"},
+                   "timing": "the timed steps issued through the C ABI between HIP events "
+                             "behind a primed queue (graph_us_per_step: the same steps "
+                             "replayed from one HIP graph); kernel: HIP events around "
+                             "back-to-back launches behind a primed queue"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
