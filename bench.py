@@ -23,9 +23,8 @@ Method
   * The K timed steps are issued from the host through the C ABI
     (pa_append_decode with prebuilt arguments) between two events, with
     torch.cuda.synchronize() on both sides, the queue primed by a device-side
-    sleep so that the host's enqueue time is spent while the GPU sleeps: the
-    events bracket the K steps' GPU work (the host issues a step in less time
-    than the GPU runs it).  The same K steps captured into one HIP graph and
+    sleep (20 ms, time for the host to enqueue all K steps) so that the
+    events bracket the K steps' GPU work.  The same K steps captured into one HIP graph and
     replayed are reported beside (config.graph_us_per_step); a replay adds a
     fixed cost of several microseconds, which few steps do not amortise.
   * The dominant kernel (the split-KV pass) is timed with HIP events around
