@@ -23,7 +23,8 @@ Method
   * The K timed steps are issued from the host through the C ABI
     (pa_append_decode with prebuilt arguments) between two events, with
     torch.cuda.synchronize() on both sides, the queue primed by a device-side
-    sleep (20 ms, time for the host to enqueue all K steps) so that the
+    sleep (20 ms, or 20 us per step for more than 1000, time for the host to
+    enqueue all K steps) so that the
     events bracket the K steps' GPU work.  The same K steps captured into one HIP graph and
     replayed are reported beside (config.graph_us_per_step); a replay adds a
     fixed cost of several microseconds, which few steps do not amortise.
@@ -543,19 +544,19 @@ def sleep_cycles_for(ms: float) -> int:
 _SLEEP_CYCLES = None
 
 
-def primed_events(issue) -> float:
+def primed_events(issue, sleep_ms: float = 20.0) -> float:
     """Milliseconds between two HIP events around the GPU work `issue()`
     enqueues on the current stream, the queue primed by a device-side sleep
-    so that the host's enqueue time (a graph launch, or the first eager
-    calls) is spent while the GPU sleeps and the events bracket GPU work
-    only.  Synchronised on both sides."""
+    of about `sleep_ms` so that the host's enqueue time (a graph launch, or
+    eager calls) is spent while the GPU sleeps and the events bracket GPU
+    work only.  Synchronised on both sides."""
     import torch
     global _SLEEP_CYCLES
     if _SLEEP_CYCLES is None:
         _SLEEP_CYCLES = sleep_cycles_for(20.0)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    torch.cuda._sleep(_SLEEP_CYCLES)
+    torch.cuda._sleep(int(_SLEEP_CYCLES * max(1.0, sleep_ms / 20.0)))
     s.record()
     issue()
     e.record()
@@ -610,7 +611,8 @@ def time_steps_eager(wl, steps: int, warmup: int) -> float:
             f(*args[(warmup + i) % wl.R])      # the rotation continues after the warm-up
         host[0] = time.perf_counter() - t0
 
-    ms = primed_events(issue)
+    # a head start in which the host enqueues all the steps (≈ 10 µs each)
+    ms = primed_events(issue, sleep_ms=max(20.0, 0.02 * steps))
     return ms / steps, host[0] * 1e3 / steps
 
 
