@@ -676,8 +676,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the pieces of one (sequence, query token, q head) row; one 256-thread
-// workgroup per row.  Thread t reads lse of piece t; the workgroup max and the weights
+// Merge the pieces of one (sequence, query token, q head) row when there are
+// more than 64 pieces; one 256-thread workgroup per row.  Thread t reads lse of
+// piece t; the workgroup max and the weights
 // 2^(lse_s - M) go through LDS.  For the weighted sum, thread t owns float4
 // column group t % (D/4) and pieces s = t / (D/4) (mod 256 / (D/4)).  Every
 // load of the first batch (pieces, lse and the context length) is issued at
@@ -769,6 +770,68 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
 }
 
+// The merge of at most 64 pieces, one 256-thread workgroup per row: every
+// wave holds all the pieces' base-2 log-sum-exps (one per lane), so the
+// maximum, the weights and their sum come from wave reductions; thread t owns
+// float4 column group t / SG and pieces t % SG + SG k, so one column's pieces
+// sit in SG consecutive lanes and sum by shuffles: no LDS and no barrier.  As
+// in the kernel above, every load is issued before the number of non-empty
+// pieces is known and pieces past it are dropped by a select.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine64_kernel(DecodeArgs a) {
+  constexpr int NV = D / 4;          // float4 columns per row
+  constexpr int SG = 256 / NV;       // lanes per column
+  constexpr int BATCH = 64 / SG;     // pieces per lane
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int S = a.num_splits;
+  const size_t row = (size_t)b * a.q_len * a.num_q_heads + h;
+  const int v = tid / SG, sg = tid % SG;
+  const float4 *op = (const float4 *)(a.o_part + row * (size_t)S * D) + v;
+  const int L = as_const(a.context_lens)[b];
+  float4 ov[BATCH];
+#pragma unroll
+  for (int k = 0; k < BATCH; ++k) {
+    const int s = sg + k * SG;
+    ov[k] = s < S ? op[(size_t)s * NV] : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float lse_raw = lane < S ? a.lse_part[row * S + lane] : -INFINITY;
+  uint16_t *out = a.out + row * D;
+  if (L <= 0) {
+    if (tid < D) out[tid] = 0;
+    return;
+  }
+  const int ns = min(S, (L + a.split_len - 1) / a.split_len);
+  const float lse = lane < ns ? lse_raw : -INFINITY;
+  const float M = wave_max(lse);
+  const float Mm = M == -INFINITY ? 0.f : M;
+  const float w = lane < ns ? exp2_fast(lse - Mm) : 0.f;
+  const float den = wave_sum(w);
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < BATCH; ++k) {
+    const int s = sg + k * SG;
+    const float wk = __shfl(w, s);
+    if (s < ns) {
+      acc.x += wk * ov[k].x; acc.y += wk * ov[k].y; acc.z += wk * ov[k].z; acc.w += wk * ov[k].w;
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < SG; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+  if (sg == 0) {
+    const float inv = den != 0.f ? 1.f / den : 0.f;
+    uint2 pk;
+    pk.x = pack_bf16(acc.x * inv, acc.y * inv);
+    pk.y = pack_bf16(acc.z * inv, acc.w * inv);
+    *(uint2 *)(out + 4 * v) = pk;
+  }
+}
+
 template <int D, int G, bool MF, int NT, bool MULTI, bool KV8 = false>
 hipError_t launch_split_variant(const DecodeArgs &a, int num_seqs, hipStream_t stream) {
   dim3 grid(num_seqs * a.num_kv_heads, a.num_splits);
@@ -832,12 +895,20 @@ hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, int group, int
 hipError_t launch_decode_combine(const DecodeArgs &a, int head_dim, int num_seqs,
                                  hipStream_t stream) {
   dim3 grid(a.num_q_heads * a.q_len, num_seqs);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(256), 0, stream, a);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(256), 0, stream, a);
-  else
+  const bool small = a.num_splits <= 64;
+  if (head_dim == 128) {
+    if (small)
+      hipLaunchKernelGGL(decode_combine64_kernel<128>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(256), 0, stream, a);
+  } else if (head_dim == 64) {
+    if (small)
+      hipLaunchKernelGGL(decode_combine64_kernel<64>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(256), 0, stream, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
