@@ -717,7 +717,8 @@ def time_steps_graph(wl, steps: int, warmup: int, fused: bool = True):
 
 
 def _short_kernel(name: str) -> str:
-    for k in ("decode_split_kernel", "decode_combine_kernel", "append_fp8_kernel", "append_kernel",
+    for k in ("decode_split_kernel", "decode_combine64_kernel", "decode_combine_kernel",
+              "append_fp8_kernel", "append_kernel",
               "prefill_kernel", "prefill_merge_kernel", "spin_kernel", "read_probe_kernel"):
         if k in name:
             tmpl = name[name.find(k):]
