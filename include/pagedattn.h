@@ -333,9 +333,10 @@ int pa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
  * num_cus compute units.  Pure host arithmetic on the shapes (context
  * lengths are device-resident and are not read): it aims for about one
  * (sequence, kv head, piece) work unit per compute unit, so S = 1 once the
- * (sequence, kv head) pairs alone reach num_cus; pieces never go below 64
- * tokens.  Returns a value in [1, PA_MAX_SPLITS], or a negative status for
- * invalid arguments. */
+ * (sequence, kv head) pairs alone reach num_cus; the planned pieces never
+ * go below 128 tokens (an explicit num_splits may ask for pieces of 64).
+ * Returns a value in [1, PA_MAX_SPLITS], or a negative status for invalid
+ * arguments. */
 int pa_decode_plan_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
                           int block_size, int num_cus);
 
@@ -353,7 +354,7 @@ int pa_decode_auto_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq
  * architecture figure, Scheduler box).  Returns pa_decode_plan_splits'
  * choice S0 when its workgroups (num_seqs * num_kv_heads * S0) exceed two per
  * compute unit.  Otherwise, for every piece count whose workgroups fit two
- * per compute unit, it predicts the largest number of tokens of one kv head
+ * per compute unit and whose pieces are at least 128 tokens, it predicts the largest number of tokens of one kv head
  * a compute unit reads -- workgroup s * units + x (piece s of unit x) takes
  * compute unit (s * units + x) mod num_cus, and when the workgroups exceed
  * num_cus pa_decode hands the upper half of the pieces (2 s >= S) out in

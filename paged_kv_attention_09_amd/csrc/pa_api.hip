@@ -57,6 +57,16 @@ int num_pieces(int64_t max_tokens, int split_len) {
   return (int)((max_tokens + split_len - 1) / split_len);
 }
 
+// The planners' pieces are at least 128 tokens: measured at ctx 4096 batch 1,
+// 32 pieces of 128 tokens make the step 2% faster than 64 pieces of 64 (the
+// split kernel is slower, the merge of half the pieces faster).  An explicit
+// piece count may still ask for 64-token pieces.
+constexpr int kMinPlanSplitLen = 128;
+int plan_split_len(int64_t max_tokens, int num_splits) {
+  const int c = split_len_for(max_tokens, num_splits);
+  return c < kMinPlanSplitLen ? kMinPlanSplitLen : c;
+}
+
 // Whether a launch of `units` (sequence, kv head) units in `pieces` pieces
 // hands the upper half of its pieces out in mirrored unit order: exactly when
 // its workgroups are more than the compute units and at most two per compute
@@ -201,7 +211,7 @@ int pa_decode_plan_splits(int num_seqs, int num_kv_heads, int max_blocks_per_seq
   int64_t s = 1;
   if (units < target) s = (target + units - 1) / units;
   if (s > PA_MAX_SPLITS) s = PA_MAX_SPLITS;
-  const int c = split_len_for(max_tokens, (int)s);
+  const int c = plan_split_len(max_tokens, (int)s);
   int n = num_pieces(max_tokens, c);
   if (n < 1) n = 1;
   if (n > PA_MAX_SPLITS) n = PA_MAX_SPLITS;
@@ -270,7 +280,7 @@ int pa_decode_plan_splits_lengths(const int32_t *context_lens, int num_seqs, int
   int64_t best_cost = cost(base);
   int last = 0;
   for (int S = 1; S <= PA_MAX_SPLITS; ++S) {
-    const int n = num_pieces(max_tokens, split_len_for(max_tokens, S));   // non-decreasing in S
+    const int n = num_pieces(max_tokens, plan_split_len(max_tokens, S));  // non-decreasing in S
     if (n == last) continue;
     last = n;
     if (units * n > 2 * (int64_t)num_cus) break;

@@ -208,13 +208,16 @@ def test_plan_splits():
     assert plan(8, 2, 256, 16, 256) == 16        # 16 units x 16 pieces of 256 tokens
     assert plan(8, 4, 16, 256, 256) == 8         # 32 units x 8 pieces of 512 tokens
     assert plan(64, 4, 16, 256, 256) == 1        # 256 units fill 256 compute units
-    assert plan(1, 2, 256, 16, 256) == 64        # pieces cannot go below 64 tokens
+    assert plan(1, 2, 256, 16, 256) == 32        # planned pieces are at least 128 tokens
+    assert plan(2, 2, 256, 16, 256) == 32        # 4 units: 64 pieces would be 64 tokens
+    assert plan(4, 2, 256, 16, 256) == 32        # 8 units x 32 pieces of 128 tokens
+    assert plan(1, 1, 1, 16, 256) == 1           # a 16-token table: one piece
     for args in [(4, 1, 16, 16, 256), (8, 4, 16, 256, 256), (64, 4, 16, 256, 256)]:
         s = plan(*args)
         assert 1 <= s <= 256
         max_tokens = args[2] * args[3]
         c = -(-max_tokens // s)
-        assert s == -(-max_tokens // ((c + 63) // 64 * 64))
+        assert s == -(-max_tokens // max(128, (c + 63) // 64 * 64))
     assert plan(0, 2, 256, 16, 256) == SHAPE and plan(1, 2, 256, 16, 0) == SHAPE
     assert plan(1, 2, 256, 32, 256) == UNSUP
 
