@@ -67,6 +67,26 @@ def test_long_context_decode(bs, Hq, Hkv, S):
     assert_close(_run(case, S), case.ref, what=f"long bs={bs} S={S}")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_merge_either_side_of_64_pieces(D):
+    """The merge runs one kernel for at most 64 pieces (weights by wave
+    reductions and shuffles) and another above (weights through LDS): a
+    64K-token table at 64 pieces of 1024 tokens and at 69 pieces of 960, two
+    sequences (one ending mid-block), both against the oracle and close to
+    each other."""
+    bs = 16
+    W_ = 65536 // bs
+    spec = W.DecodeSpec(f"merge64-{D}", 2, 6, 2, D, bs, 2 * W_ + 8, W_,
+                        context_lens=(65536, 40001), seed=7100 + D)
+    case = DecodeCase(W.make_decode_inputs(spec, fill="normal"))
+    outs = {}
+    for S in (64, 69):
+        assert pa.decode_workspace_size(2, 6, D, S) > 0
+        outs[S] = _run(case, S)
+        assert_close(outs[S], case.ref, what=f"D{D} S={S}")
+    assert (np.abs(outs[64] - outs[69]) <= 2 ** -7 * np.abs(outs[64]) + 1e-3).all()
+
+
 def test_mixed_batch_decode_part():
     """The 64 decode sequences of the mixed batch (lengths 512..4096, group 7)."""
     case = DecodeCase(W.make_decode_inputs(W.CONFIGS["c5d"]))
